@@ -1,0 +1,240 @@
+/*
+ * moert.h — C ABI of the routed-expert MoE step on one MI355X (gfx950).
+ *
+ * The step, per MoE layer, as the FreeToken pages describe it:
+ *   route top-k → one device-side control kernel (dedup the routed
+ *   (layer, expert) ids, classify them against the residency table, split the
+ *   misses by q, surface the K least-recently-used victim slots, rewrite ids
+ *   into slot ids or a CPU flag) → PCIe fills into victims ∥ host execution of
+ *   the remaining misses → grouped expert FFN over the slot pool → exact,
+ *   fixed-order merge of GPU and host partial sums.  Prefill streams whole
+ *   layers into two full-layer buffers carved out of the same pool; the pool
+ *   can be rebuilt under a new budget without reloading the host pool.
+ *
+ * Pages cited (by title and section):
+ *   [snackonai] "FreeToken, or why your laptop was never the bottleneck",
+ *               https://www.snackonai.com/p/freetoken-or-why-your-laptop-was-never-the-bottleneck
+ *   [satyajit]  "FreeToken: a 753B model on one GPU, and the two bandwidths that
+ *               decide everything", https://ai.thesatyajit.com/articles/freetoken
+ *   [son]       "FreeToken: treat the whole PC as one" (essay, no headings),
+ *               https://signalovernoise.tech/p/freetoken-treat-the-whole-pc-as-one
+ *   [devto]     "FreeToken runs frontier-scale MoE models by treating the whole PC
+ *               as the inference platform", dev.to/khasky
+ *
+ * Conventions for every call:
+ *   - Pointers marked (device) are device addresses (e.g. torch.cuda tensors);
+ *     (host) are host addresses.  The caller owns every buffer it passes; the
+ *     library keeps no pointer to it after the call returns, except the host
+ *     pool given to moe_create (kept until moe_destroy).
+ *   - Arguments are validated before anything is enqueued: a bad argument
+ *     returns MOE_EINVAL and enqueues nothing.  No C++ exception crosses the
+ *     ABI.  A HIP failure returns MOE_EHIP and is latched: every later call on
+ *     that context returns MOE_EHIP (moe_last_error() has the text).
+ *   - route / plan / ffn / merge / prefill enqueue work on `stream` and never
+ *     synchronise the host; plans stay on the device (the host never reads
+ *     them on this path) [snackonai, "The Architecture, Unpacked"].
+ *   - One context is driven by one host thread, and its decode calls for a
+ *     layer are issued in the order plan → ffn → merge on one stream; a call
+ *     out of that order returns MOE_EINVAL.
+ *   - Matrices are row-major.  Activations (x, y) use the context's act dtype
+ *     (f32 or bf16); router logits and weights are fp32.
+ */
+#ifndef MOERT_H
+#define MOERT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct moe_ctx moe_ctx;
+typedef void* moe_stream; /* a hipStream_t; NULL is the null stream */
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_EINVAL = -1,       /* bad argument or call order; nothing enqueued      */
+  MOE_ENOMEM = -2,       /* device or pinned host allocation failed           */
+  MOE_ENOSPC = -3,       /* two full-layer buffers do not fit (prefill)       */
+  MOE_EHIP = -4,         /* HIP runtime error (latched)                       */
+  MOE_EBUSY = -5,        /* work still in flight where a safe point is needed */
+  MOE_ETIMEDOUT = -6,    /* resize could not drain within timeout_ms          */
+  MOE_EUNSUPPORTED = -7  /* device lacks a needed feature                     */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_MXFP4 = 2 } moe_dtype;
+
+/* Miss handling [satyajit, "Four backends, and the one that has to be
+ * measured"]: HYBRID fills q = clamp(round_half_even(m*B_P/B_H), 1, m) misses
+ * and runs the rest on the host; OFFLOAD fills every miss; CPU fills none. */
+typedef enum { MOE_HYBRID = 0, MOE_OFFLOAD = 1, MOE_CPU = 2 } moe_mode;
+
+typedef struct {
+  int32_t n_layers;      /* L: MoE layers; flat expert id u = l*E + e        */
+  int32_t n_experts;     /* E (1..1024)                                       */
+  int32_t top_k;         /* k (1..min(E, 32))                                 */
+  int32_t hidden;        /* H (multiple of 256)                               */
+  int32_t inter;         /* I, expert intermediate (multiple of 256)          */
+  int32_t w_dtype;       /* moe_dtype of expert weights: F32, BF16 or MXFP4   */
+  int32_t act_dtype;     /* moe_dtype of x and y: F32 or BF16                 */
+  int32_t n_slots;       /* initial device slot budget (0..max_slots)         */
+  int32_t max_slots;     /* address-space reservation; resize may grow to it  */
+  int32_t max_tokens;    /* largest T of a decode layer call (1..256)          */
+  int64_t bw_pcie_mbps;  /* B_P, MB/s (> 0)                                   */
+  int64_t bw_host_mbps;  /* B_H, MB/s (>= B_P in HYBRID)                      */
+  int32_t max_fetch;     /* cap on PCIe fills per layer call; 0 = none        */
+  int32_t mode;          /* moe_mode                                          */
+  int32_t cpu_threads;   /* host worker threads; 0 = one per available core   */
+  int32_t max_prefill_tokens; /* largest prefill chunk; 0 disables prefill    */
+} moe_config;
+
+/* Bytes of one expert bank == one device slot stride (expert bytes rounded up
+ * to 256).  A slot is a complete expert, named by its flat id u = l*E + e in
+ * every bank [snackonai, "The Architecture, Unpacked", first decision].
+ * Bank layout (contraction axis contiguous in every matrix):
+ *   F32  : W_gate[I][H] | W_up[I][H] | W_down[H][I]           (float)
+ *   BF16 : the same, bfloat16
+ *   MXFP4: codes W_gate[I][H/2] | W_up[I][H/2] | W_down[H][I/2], then
+ *          scales W_gate[I][H/32] | W_up[I][H/32] | W_down[H][I/32];
+ *          OCP MX v1.0 E2M1 codes two per byte (low nibble = even element),
+ *          one E8M0 scale per 32 contraction elements.
+ * The expert is SwiGLU without biases: p = W_down (silu(W_gate x) * W_up x).
+ * Returns 0 for an invalid config. */
+size_t moe_expert_bytes(const moe_config* cfg);
+
+/* Pinned, device-mapped host memory for the host expert pool (the source of
+ * truth: [son]; [snackonai, "What It Actually Does"]).  The caller fills bank
+ * u at offset u * moe_expert_bytes() and then calls moe_create.  The pages pin
+ * after filling; this library allocates pinned memory first because
+ * registering existing pages is not available on the target platform.
+ * Returns MOE_ENOMEM on failure. */
+moe_status moe_host_pool_alloc(size_t bytes, void** out /* (host) */);
+moe_status moe_host_pool_free(void* p);
+
+/* Create a context on the current HIP device.  host_pool (host) must come
+ * from moe_host_pool_alloc and hold L*E banks (host_pool_bytes >=
+ * L*E*moe_expert_bytes); the library only reads it.  Reserves device address
+ * space for max_slots slots, maps n_slots of them, allocates the residency
+ * tables (all slots empty: no warmup [satyajit, "Elastic memory, because the
+ * machine is not yours"]), plan buffers sized by max_tokens, staging, side
+ * streams and the host worker pool. */
+moe_status moe_create(const moe_config* cfg, void* host_pool, size_t host_pool_bytes,
+                      moe_ctx** out);
+/* Waits for the context's work, then frees everything it owns. */
+moe_status moe_destroy(moe_ctx* ctx);
+
+/* Router top-k [snackonai, "The Promise" leaves router design out; a softmax
+ * router is assumed].  logits (device) fp32 [T][E]; ids (device) int32 [T][k]
+ * receives experts by descending logit, equal logits by ascending index (NaN
+ * ranks as -inf); w (device) fp32 [T][k] receives the softmax over the k
+ * selected logits.  1 <= T <= max(max_tokens, max_prefill_tokens). */
+moe_status moe_route_topk(moe_ctx* ctx, const float* logits, int32_t T, int32_t* ids,
+                          float* w, moe_stream stream);
+
+/* The control step of MoE layer `layer` [snackonai, "The Architecture,
+ * Unpacked", third decision; satyajit, "Residency that follows the router";
+ * snackonai, "The Code, Annotated"]: one kernel deduplicates {layer*E +
+ * ids[t][j]} (ascending), classifies them against id2slot, computes q (mode,
+ * then max_fetch, then the slots not holding a current hit), refreshes the
+ * hits' recency, surfaces the K = min(max_tokens*k, E, n_slots[, max_fetch])
+ * least-recently-used slots by (tick, slot) excluding current hits, admits the
+ * first q misses into the first q of them and writes slot_map[t][j] (slot id,
+ * or -1 = run on the host).  One LRU tick per call.  It then enqueues the
+ * host branch for the remaining misses (launched first, on a side stream) and
+ * the PCIe fill of the q admitted experts into their slots (on `stream`).
+ * ids (device) int32 [T][k]; x (device) [T][H] act dtype, read by the host
+ * branch.  1 <= T <= max_tokens. */
+moe_status moe_cache_plan(moe_ctx* ctx, int32_t layer, const int32_t* ids, int32_t T,
+                          const void* x, moe_stream stream);
+
+/* Grouped SwiGLU evaluation of every GPU-resident routed expert of the last
+ * plan (hits and fills; each slot's weights read once per call) into the
+ * context's fp32 partial rows P_gpu[T][k][H].  x (device) [T][H] act dtype;
+ * layer and T must equal the last moe_cache_plan's. */
+moe_status moe_expert_ffn(moe_ctx* ctx, int32_t layer, const void* x, int32_t T,
+                          moe_stream stream);
+
+/* Exact merge [snackonai, "What It Actually Does"; satyajit, "Decode: the one
+ * equation"]: waits for the host branch, then y[t] = sum over ascending j of
+ * w[t][j] * (slot_map[t][j] >= 0 ? P_gpu[t][j] : P_cpu[t][j]) in fp32, rounded
+ * once to the act dtype.  w (device) fp32 [T][k]; y (device) [T][H]. */
+moe_status moe_merge(moe_ctx* ctx, const float* w, int32_t T, void* y, moe_stream stream);
+
+/* Rebuild the slot pool under a new budget at a safe point [satyajit,
+ * "Elastic memory, because the machine is not yours"; snackonai, "Resizing
+ * the cache without a restart"].  Drains the context's streams (waiting up to
+ * timeout_ms, else MOE_ETIMEDOUT with nothing changed), evicts in LRU victim
+ * order until min(new_n_slots, occupied) experts remain, packs the survivors
+ * to slots 0.. in ascending old-slot order with device-to-device copies (each
+ * to a lower or equal index), keeps their recency, and maps or unmaps device
+ * memory beyond the new budget.  The host pool is never read or written.
+ * 0 <= new_n_slots <= max_slots.  Synchronous. */
+moe_status moe_cache_resize(moe_ctx* ctx, int32_t new_n_slots, int32_t timeout_ms);
+
+/* One prefill chunk of MoE layer `layer` [satyajit, "Prefill: hide the pool
+ * behind the wire"; son]: two full-layer buffers are slots [0,E) and [E,2E)
+ * of the shared pool; layer l runs out of buffer l%2 while a copy stream
+ * streams every expert of layer l+1 into the other buffer with one
+ * hipMemcpyAsync from the pinned host pool.  The residency tables record the
+ * buffer's experts as ordinary slots (one tick per layer), so what survives
+ * seeds decode.  Tokens are grouped by expert and evaluated with an MFMA
+ * grouped GEMM; y[t] = sum over ascending j of w[t][j] * FFN(x[t]).
+ * x (device) [T][H] act dtype; ids (device) int32 [T][k]; w (device) fp32
+ * [T][k]; y (device) [T][H].  1 <= T <= max_prefill_tokens.
+ * MOE_ENOSPC if n_slots < 2E (the pages fall back to on-demand loading
+ * instead of oversubscribing; that fallback is not provided). */
+moe_status moe_prefill_layer(moe_ctx* ctx, int32_t layer, const void* x, int32_t T,
+                             const int32_t* ids, const float* w, void* y, moe_stream stream);
+
+/* Device addresses of the last plan's fixed-shape outputs and of the
+ * residency tables (for inspection and tests; reading them requires the
+ * plan's stream to have completed).  Counts layout: see moe_plan_counts. */
+typedef struct {
+  int32_t n_uniq, n_hit, n_miss, q, n_cpu, n_gpu, K, tick_lo;
+} moe_plan_counts;
+
+typedef struct {
+  const moe_plan_counts* counts; /* (device) */
+  const int32_t* uniq;       /* [Umax] ascending flat ids                     */
+  const int32_t* hits;       /* [Umax] ascending                              */
+  const int32_t* misses;     /* [Umax] ascending                              */
+  const int32_t* victims;    /* [Kmax] LRU-first, -1 padded to K              */
+  const int32_t* fill_u;     /* [Kmax] first q misses                          */
+  const int32_t* fill_slot;  /* [Kmax]                                         */
+  const int32_t* fill_old;   /* [Kmax] evicted id or -1                        */
+  const int32_t* cpu_u;      /* [Umax] misses[q:]                              */
+  const int32_t* gpu_u;      /* [Umax] resident after the plan, ascending u    */
+  const int32_t* gpu_slot;   /* [Umax]                                         */
+  const int32_t* slot_map;   /* [max_tokens*k]                                 */
+  const int32_t* id2slot;    /* [L*E]                                          */
+  const int32_t* slot2id;    /* [max_slots]                                    */
+  const int64_t* slot_ts;    /* [max_slots], -1 = empty                        */
+  const int64_t* tick;       /* [1]                                            */
+  const float* p_gpu;        /* [max_tokens*k][H] fp32                         */
+  const float* p_cpu;        /* [max_tokens*k][H] fp32 (pinned host, mapped)   */
+  const void* slot_base;     /* slot s at slot_base + s * moe_expert_bytes()   */
+  int32_t n_slots, max_slots, umax, kmax;
+} moe_plan_view;
+
+moe_status moe_plan_view_get(moe_ctx* ctx, moe_plan_view* out);
+
+/* Pool table [snackonai, "Resizing the cache without a restart"]: occupancy
+ * and counters accumulated on the device since moe_create.  Synchronises the
+ * context's streams; not for the hot path. */
+typedef struct {
+  int32_t n_slots, occupied;
+  int64_t plans, hits, fills, cpu, evictions;
+  int64_t prefill_layers, resizes;
+} moe_stats;
+
+moe_status moe_ctx_stats(moe_ctx* ctx, moe_stats* out);
+
+const char* moe_strerror(moe_status s);
+/* Text of the last error on the calling thread ("" if none). */
+const char* moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOERT_H */

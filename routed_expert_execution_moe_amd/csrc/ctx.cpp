@@ -1,0 +1,692 @@
+// Context lifecycle, slot pool, entry points and resize of the routed-expert
+// MoE library.  Kernels live in the .hip files, the host branch in
+// cpu_branch.cpp.
+#include <unistd.h>
+
+#include <algorithm>
+#include <chrono>
+#include <cstdio>
+#include <cstdlib>
+#include <thread>
+
+#include "internal.h"
+
+using namespace moert;
+
+namespace moert {
+
+static thread_local std::string g_last_error;
+
+void set_last_error(const std::string& s) { g_last_error = s; }
+
+moe_status fail(moe_ctx* ctx, moe_status s, const std::string& msg) {
+  set_last_error(msg);
+  if (ctx && s == MOE_EHIP) {
+    ctx->err = MOE_EHIP;
+    ctx->err_msg = msg;
+  }
+  return s;
+}
+
+moe_status hip_fail(moe_ctx* ctx, hipError_t e, const char* what) {
+  std::string m = std::string(what) + ": " + hipGetErrorString(e);
+  if (e == hipErrorOutOfMemory) {
+    set_last_error(m);
+    return MOE_ENOMEM;
+  }
+  return fail(ctx, MOE_EHIP, m);
+}
+
+}  // namespace moert
+
+// ------------------------------------------------------------------ config
+static size_t expert_bytes_of(const moe_config* c) {
+  size_t H = (size_t)c->hidden, I = (size_t)c->inter;
+  switch (c->w_dtype) {
+    case MOE_F32: return 12 * H * I;
+    case MOE_BF16: return 6 * H * I;
+    case MOE_MXFP4: return 3 * H * I / 2 + 3 * H * I / 32;
+    default: return 0;
+  }
+}
+
+// Row chunk (elements per 16-byte weight load) of a weight dtype.
+static int chunk_elems(int w_dtype) { return w_dtype == MOE_F32 ? 4 : w_dtype == MOE_BF16 ? 8 : 32; }
+
+// The decode kernels split a row of K elements into NCH = K / chunk chunks
+// handled by G = (largest power of two dividing NCH, at most 64) lanes and
+// KS = NCH / G waves; G must be >= 16 and KS <= 4.
+static bool row_split_ok(int K, int w_dtype) {
+  int ch = chunk_elems(w_dtype);
+  if (K % ch) return false;
+  int nch = K / ch;
+  int g = 1;
+  while (g < 64 && nch % (2 * g) == 0) g *= 2;
+  return g >= 16 && nch / g <= 4;
+}
+
+static std::string validate(const moe_config* c) {
+  if (!c) return "config is NULL";
+  if (c->n_layers < 1) return "n_layers must be >= 1";
+  if (c->n_experts < 1 || c->n_experts > kMaxExperts) return "n_experts must be in 1..1024";
+  if (c->top_k < 1 || c->top_k > std::min(c->n_experts, kMaxTopK)) return "top_k must be in 1..min(E,32)";
+  if (c->w_dtype < MOE_F32 || c->w_dtype > MOE_MXFP4) return "w_dtype must be F32, BF16 or MXFP4";
+  if (c->act_dtype != MOE_F32 && c->act_dtype != MOE_BF16) return "act_dtype must be F32 or BF16";
+  if (c->hidden < 1 || c->inter < 1) return "hidden and inter must be positive";
+  if (c->hidden % 64 || c->inter % 64) return "hidden and inter must be multiples of 64";
+  if (!row_split_ok(c->hidden, c->w_dtype) || !row_split_ok(c->inter, c->w_dtype))
+    return "hidden/inter must split into at most 4 waves of 16..64-lane groups (e.g. bf16: 128..2048 in steps of 128 with an odd factor <= 3)";
+  if (c->max_slots < 0 || c->max_slots > kMaxSlots) return "max_slots must be in 0..32768";
+  if (c->n_slots < 0 || c->n_slots > c->max_slots) return "n_slots must be in 0..max_slots";
+  if (c->max_tokens < 1 || c->max_tokens > kMaxDecodeTokens) return "max_tokens must be in 1..256";
+  if ((int64_t)c->max_tokens * c->top_k > 4096) return "max_tokens*top_k must be <= 4096";
+  if (c->bw_pcie_mbps <= 0 || c->bw_host_mbps <= 0) return "bandwidths must be positive";
+  if (c->bw_pcie_mbps > (int64_t)1 << 40 || c->bw_host_mbps > (int64_t)1 << 40) return "bandwidth too large";
+  if (c->mode < MOE_HYBRID || c->mode > MOE_CPU) return "mode must be HYBRID, OFFLOAD or CPU";
+  if (c->max_fetch < 0) return "max_fetch must be >= 0";
+  if (c->cpu_threads < 0) return "cpu_threads must be >= 0";
+  if (c->max_prefill_tokens < 0 || c->max_prefill_tokens > 65536) return "max_prefill_tokens must be in 0..65536";
+  if ((int64_t)c->n_layers * c->n_experts > (int64_t)1 << 30) return "too many expert ids";
+  return "";
+}
+
+extern "C" size_t moe_expert_bytes(const moe_config* cfg) {
+  if (!validate(cfg).empty()) return 0;
+  return (expert_bytes_of(cfg) + 255) / 256 * 256;
+}
+
+extern "C" const char* moe_strerror(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_EINVAL: return "invalid argument or call order";
+    case MOE_ENOMEM: return "out of memory";
+    case MOE_ENOSPC: return "two full-layer buffers do not fit in the slot pool";
+    case MOE_EHIP: return "HIP runtime error";
+    case MOE_EBUSY: return "busy";
+    case MOE_ETIMEDOUT: return "timed out";
+    case MOE_EUNSUPPORTED: return "unsupported";
+  }
+  return "unknown status";
+}
+
+extern "C" const char* moe_last_error(void) { return g_last_error.c_str(); }
+
+// ------------------------------------------------------------------ host pool
+extern "C" moe_status moe_host_pool_alloc(size_t bytes, void** out) {
+  if (!out || bytes == 0) return fail(nullptr, MOE_EINVAL, "moe_host_pool_alloc: bad arguments");
+  void* p = nullptr;
+  hipError_t e = hipHostMalloc(&p, bytes, hipHostMallocMapped | hipHostMallocPortable);
+  if (e != hipSuccess) {
+    set_last_error(std::string("hipHostMalloc: ") + hipGetErrorString(e));
+    return MOE_ENOMEM;
+  }
+  *out = p;
+  return MOE_OK;
+}
+
+extern "C" moe_status moe_host_pool_free(void* p) {
+  if (!p) return MOE_OK;
+  hipError_t e = hipHostFree(p);
+  if (e != hipSuccess) return hip_fail(nullptr, e, "hipHostFree");
+  return MOE_OK;
+}
+
+// ------------------------------------------------------------------ slot pool
+static bool env_flag(const char* name) {
+  const char* v = getenv(name);
+  return v && v[0] && v[0] != '0';
+}
+
+static moe_status pool_map_to(moe_ctx* ctx, size_t need) {
+  SlotPool& P = ctx->pool;
+  if (!P.vmm) return need <= P.reserved ? MOE_OK : fail(ctx, MOE_ENOMEM, "slot pool exhausted");
+  hipMemAllocationProp prop = {};
+  prop.type = hipMemAllocationTypePinned;
+  prop.location.type = hipMemLocationTypeDevice;
+  prop.location.id = ctx->device;
+  while (P.mapped < need) {
+    PoolChunk c{};
+    c.offset = P.mapped;
+    c.bytes = P.gran;
+    MOE_HIP(ctx, hipMemCreate(&c.h, c.bytes, &prop, 0));
+    hipError_t e = hipMemMap(P.base + c.offset, c.bytes, 0, c.h, 0);
+    if (e != hipSuccess) {
+      (void)hipMemRelease(c.h);
+      return hip_fail(ctx, e, "hipMemMap");
+    }
+    hipMemAccessDesc acc = {};
+    acc.location = prop.location;
+    acc.flags = hipMemAccessFlagsProtReadWrite;
+    MOE_HIP(ctx, hipMemSetAccess(P.base + c.offset, c.bytes, &acc, 1));
+    P.chunks.push_back(c);
+    P.mapped += c.bytes;
+  }
+  return MOE_OK;
+}
+
+static moe_status pool_unmap_to(moe_ctx* ctx, size_t need) {
+  SlotPool& P = ctx->pool;
+  if (!P.vmm) return MOE_OK;
+  while (!P.chunks.empty() && P.chunks.back().offset >= need) {
+    PoolChunk c = P.chunks.back();
+    MOE_HIP(ctx, hipMemUnmap(P.base + c.offset, c.bytes));
+    MOE_HIP(ctx, hipMemRelease(c.h));
+    P.chunks.pop_back();
+    P.mapped = c.offset;
+  }
+  return MOE_OK;
+}
+
+static moe_status pool_create(moe_ctx* ctx) {
+  SlotPool& P = ctx->pool;
+  size_t want = (size_t)ctx->cfg.max_slots * ctx->stride;
+  int vmm = 0;
+  (void)hipDeviceGetAttribute(&vmm, hipDeviceAttributeVirtualMemoryManagementSupported, ctx->device);
+  P.vmm = vmm && !env_flag("MOERT_NO_VMM");
+  if (P.vmm) {
+    hipMemAllocationProp prop = {};
+    prop.type = hipMemAllocationTypePinned;
+    prop.location.type = hipMemLocationTypeDevice;
+    prop.location.id = ctx->device;
+    size_t g = 0;
+    if (hipMemGetAllocationGranularity(&g, &prop, hipMemAllocationGranularityMinimum) != hipSuccess ||
+        g == 0) {
+      P.vmm = false;
+    } else {
+      size_t chunk = (size_t)64 << 20;
+      P.gran = (chunk + g - 1) / g * g;
+      P.reserved = std::max<size_t>(P.gran, (want + P.gran - 1) / P.gran * P.gran);
+      void* base = nullptr;
+      if (hipMemAddressReserve(&base, P.reserved, 0, nullptr, 0) != hipSuccess) {
+        P.vmm = false;
+      } else {
+        P.base = (uint8_t*)base;
+      }
+    }
+  }
+  if (!P.vmm) {
+    P.reserved = std::max<size_t>(256, want);
+    void* b = nullptr;
+    MOE_HIP(ctx, hipMalloc(&b, P.reserved));
+    P.base = (uint8_t*)b;
+    P.mapped = P.reserved;
+    return MOE_OK;
+  }
+  return pool_map_to(ctx, (size_t)ctx->cfg.n_slots * ctx->stride);
+}
+
+static void pool_destroy(moe_ctx* ctx) {
+  SlotPool& P = ctx->pool;
+  if (!P.base) return;
+  if (P.vmm) {
+    pool_unmap_to(ctx, 0);
+    (void)hipMemAddressFree(P.base, P.reserved);
+  } else {
+    (void)hipFree(P.base);
+  }
+  P.base = nullptr;
+}
+
+// ------------------------------------------------------------------ create
+static int32_t victim_bound(const moe_config& c, int32_t n_slots) {
+  int64_t K = std::min<int64_t>((int64_t)c.max_tokens * c.top_k, c.n_experts);
+  K = std::min<int64_t>(K, n_slots);
+  if (c.max_fetch > 0) K = std::min<int64_t>(K, c.max_fetch);
+  return (int32_t)K;
+}
+
+static void CUDA_free_all(moe_ctx* ctx);
+
+extern "C" moe_status moe_create(const moe_config* cfg, void* host_pool, size_t host_pool_bytes,
+                                 moe_ctx** out) {
+  std::string why = validate(cfg);
+  if (!why.empty()) return fail(nullptr, MOE_EINVAL, "moe_create: " + why);
+  if (!out) return fail(nullptr, MOE_EINVAL, "moe_create: out is NULL");
+  size_t stride = moe_expert_bytes(cfg);
+  int64_t n_ids = (int64_t)cfg->n_layers * cfg->n_experts;
+  if (!host_pool || host_pool_bytes < (size_t)n_ids * stride)
+    return fail(nullptr, MOE_EINVAL, "moe_create: host pool smaller than L*E banks");
+
+  moe_ctx* ctx = new (std::nothrow) moe_ctx();
+  if (!ctx) return fail(nullptr, MOE_ENOMEM, "moe_create: out of host memory");
+  ctx->cfg = *cfg;
+  ctx->stride = stride;
+  ctx->expert_bytes = expert_bytes_of(cfg);
+  ctx->n_ids = n_ids;
+  ctx->n_slots = cfg->n_slots;
+  ctx->umax = std::min(cfg->max_tokens * cfg->top_k, cfg->n_experts);
+  ctx->kmax = std::max(1, victim_bound(*cfg, cfg->max_slots));
+  ctx->host_pool = (uint8_t*)host_pool;
+  ctx->host_pool_bytes = host_pool_bytes;
+  moe_status st = MOE_OK;
+  auto bail = [&](moe_status s) {
+    CUDA_free_all(ctx);
+    delete ctx;
+    return s;
+  };
+  (void)hipGetDevice(&ctx->device);
+
+  void* hp_dev = nullptr;
+  hipError_t e = hipHostGetDevicePointer(&hp_dev, host_pool, 0);
+  if (e != hipSuccess) {
+    set_last_error(std::string("host pool is not pinned, mapped memory (hipHostGetDevicePointer: ") +
+                   hipGetErrorString(e) + ")");
+    delete ctx;
+    return MOE_EUNSUPPORTED;
+  }
+  ctx->host_pool_dev = (const uint8_t*)hp_dev;
+
+  if ((st = pool_create(ctx)) != MOE_OK) return bail(st);
+
+  const int H = cfg->hidden, I = cfg->inter, k = cfg->top_k;
+  const int maxTk = cfg->max_tokens * k;
+#define ALLOC(ptr, bytes)                                                   \
+  do {                                                                      \
+    hipError_t _e = hipMalloc((void**)&(ptr), (bytes));                     \
+    if (_e != hipSuccess) return bail(hip_fail(ctx, _e, "hipMalloc " #ptr)); \
+  } while (0)
+  ALLOC(ctx->id2slot, sizeof(int32_t) * n_ids);
+  ALLOC(ctx->slot2id, sizeof(int32_t) * std::max(1, cfg->max_slots));
+  ALLOC(ctx->slot_ts, sizeof(int64_t) * std::max(1, cfg->max_slots));
+  ALLOC(ctx->dstate, sizeof(DevState));
+  ALLOC(ctx->p_gpu, sizeof(float) * maxTk * H);
+  ALLOC(ctx->h_mid, sizeof(float) * maxTk * I);
+
+  // plan buffers: one allocation, 256-byte aligned sub-arrays
+  {
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+      size_t o = off;
+      off += (bytes + 255) / 256 * 256;
+      return o;
+    };
+    size_t o_counts = take(sizeof(moe_plan_counts));
+    size_t o_uniq = take(4 * ctx->umax), o_hits = take(4 * ctx->umax), o_miss = take(4 * ctx->umax);
+    size_t o_vic = take(4 * ctx->kmax), o_fu = take(4 * ctx->kmax), o_fs = take(4 * ctx->kmax),
+           o_fo = take(4 * ctx->kmax);
+    size_t o_cpu = take(4 * ctx->umax), o_gu = take(4 * ctx->umax), o_gs = take(4 * ctx->umax);
+    size_t o_sm = take(4 * maxTk);
+    size_t hb = sizeof(HostBlockHeader) + 2 * 4 * (size_t)maxTk;
+    size_t o_hb = take(hb);
+    ALLOC(ctx->plan_alloc, off);
+    uint8_t* b = ctx->plan_alloc;
+    PlanBufs& p = ctx->plan;
+    p.counts = (moe_plan_counts*)(b + o_counts);
+    p.uniq = (int32_t*)(b + o_uniq);
+    p.hits = (int32_t*)(b + o_hits);
+    p.misses = (int32_t*)(b + o_miss);
+    p.victims = (int32_t*)(b + o_vic);
+    p.fill_u = (int32_t*)(b + o_fu);
+    p.fill_slot = (int32_t*)(b + o_fs);
+    p.fill_old = (int32_t*)(b + o_fo);
+    p.cpu_u = (int32_t*)(b + o_cpu);
+    p.gpu_u = (int32_t*)(b + o_gu);
+    p.gpu_slot = (int32_t*)(b + o_gs);
+    p.slot_map = (int32_t*)(b + o_sm);
+    p.hblock = b + o_hb;
+    p.hblock_bytes = hb;
+  }
+#undef ALLOC
+
+  // pinned staging: the host branch's inputs and its output rows
+  {
+    void* p = nullptr;
+    e = hipHostMalloc(&p, ctx->plan.hblock_bytes, hipHostMallocDefault);
+    if (e != hipSuccess) return bail(hip_fail(ctx, e, "hipHostMalloc hstage"));
+    ctx->hstage = (uint8_t*)p;
+    e = hipHostMalloc(&p, (size_t)cfg->max_tokens * H * dtype_bytes(cfg->act_dtype), hipHostMallocDefault);
+    if (e != hipSuccess) return bail(hip_fail(ctx, e, "hipHostMalloc xstage"));
+    ctx->xstage = (uint8_t*)p;
+    e = hipHostMalloc(&p, sizeof(float) * maxTk * H, hipHostMallocMapped | hipHostMallocCoherent);
+    if (e != hipSuccess) return bail(hip_fail(ctx, e, "hipHostMalloc p_cpu"));
+    ctx->p_cpu = (float*)p;
+    memset(p, 0, sizeof(float) * maxTk * H);
+    void* d = nullptr;
+    e = hipHostGetDevicePointer(&d, p, 0);
+    if (e != hipSuccess) return bail(hip_fail(ctx, e, "hipHostGetDevicePointer p_cpu"));
+    ctx->p_cpu_dev = (const float*)d;
+  }
+
+  e = hipStreamCreateWithFlags(&ctx->side, hipStreamNonBlocking);
+  if (e != hipSuccess) return bail(hip_fail(ctx, e, "hipStreamCreate side"));
+  e = hipStreamCreateWithFlags(&ctx->copy, hipStreamNonBlocking);
+  if (e != hipSuccess) return bail(hip_fail(ctx, e, "hipStreamCreate copy"));
+  e = hipEventCreateWithFlags(&ctx->ev_plan, hipEventDisableTiming);
+  if (e != hipSuccess) return bail(hip_fail(ctx, e, "hipEventCreate"));
+  e = hipEventCreateWithFlags(&ctx->ev_cpu, hipEventDisableTiming);
+  if (e != hipSuccess) return bail(hip_fail(ctx, e, "hipEventCreate"));
+
+  // empty tables, tick 0
+  e = launch_table_reset(ctx, ctx->copy);
+  if (e != hipSuccess) return bail(hip_fail(ctx, e, "table reset"));
+  e = hipStreamSynchronize(ctx->copy);
+  if (e != hipSuccess) return bail(hip_fail(ctx, e, "table reset sync"));
+
+  int threads = cfg->cpu_threads;
+  if (threads == 0) {
+    cpu_set_t cs;
+    int avail = (sched_getaffinity(0, sizeof cs, &cs) == 0) ? CPU_COUNT(&cs) : 1;
+    threads = std::max(1, avail - 1);
+  }
+  ctx->cpu_threads = threads;
+  ctx->cpu = cpu_pool_create(threads);
+  if (!ctx->cpu) return bail(fail(nullptr, MOE_ENOMEM, "host worker pool"));
+  ctx->job.ctx = ctx;
+  *out = ctx;
+  return MOE_OK;
+}
+
+static void CUDA_free_all(moe_ctx* ctx) {
+  if (ctx->cpu) cpu_pool_destroy(ctx->cpu);
+  ctx->cpu = nullptr;
+  if (ctx->side) (void)hipStreamSynchronize(ctx->side);
+  if (ctx->copy) (void)hipStreamSynchronize(ctx->copy);
+  auto F = [](void* p) {
+    if (p) (void)hipFree(p);
+  };
+  F(ctx->id2slot); F(ctx->slot2id); F(ctx->slot_ts); F(ctx->dstate);
+  F(ctx->p_gpu); F(ctx->h_mid); F(ctx->plan_alloc);
+  auto& pf = ctx->pf;
+  F(pf.counts); F(pf.offsets); F(pf.cursor); F(pf.perm); F(pf.hmid); F(pf.prow); F(pf.tiles);
+  for (int b = 0; b < 2; ++b)
+    if (pf.ev_copied[b]) (void)hipEventDestroy(pf.ev_copied[b]);
+  if (pf.ev_start) (void)hipEventDestroy(pf.ev_start);
+  if (ctx->hstage) (void)hipHostFree(ctx->hstage);
+  if (ctx->xstage) (void)hipHostFree(ctx->xstage);
+  if (ctx->p_cpu) (void)hipHostFree(ctx->p_cpu);
+  if (ctx->ev_plan) (void)hipEventDestroy(ctx->ev_plan);
+  if (ctx->ev_cpu) (void)hipEventDestroy(ctx->ev_cpu);
+  if (ctx->side) (void)hipStreamDestroy(ctx->side);
+  if (ctx->copy) (void)hipStreamDestroy(ctx->copy);
+  pool_destroy(ctx);
+}
+
+extern "C" moe_status moe_destroy(moe_ctx* ctx) {
+  if (!ctx) return MOE_OK;
+  (void)hipDeviceSynchronize();
+  CUDA_free_all(ctx);
+  delete ctx;
+  return MOE_OK;
+}
+
+// ------------------------------------------------------------------ calls
+#define CHECK_CTX(ctx)                                                        \
+  do {                                                                        \
+    if (!(ctx)) return fail(nullptr, MOE_EINVAL, "context is NULL");          \
+    if ((ctx)->err != MOE_OK) {                                               \
+      set_last_error((ctx)->err_msg);                                         \
+      return (ctx)->err;                                                      \
+    }                                                                         \
+  } while (0)
+
+extern "C" moe_status moe_route_topk(moe_ctx* ctx, const float* logits, int32_t T, int32_t* ids,
+                                     float* w, moe_stream stream) {
+  CHECK_CTX(ctx);
+  int tmax = std::max(ctx->cfg.max_tokens, ctx->cfg.max_prefill_tokens);
+  if (!logits || !ids || !w || T < 1 || T > tmax)
+    return fail(ctx, MOE_EINVAL, "moe_route_topk: bad arguments");
+  MOE_HIP(ctx, launch_route_topk(logits, T, ctx->cfg.n_experts, ctx->cfg.top_k, ids, w,
+                                 (hipStream_t)stream));
+  return MOE_OK;
+}
+
+static void host_branch_cb(void* user) {
+  moe_ctx* ctx = (moe_ctx*)user;
+  cpu_branch_run(ctx);
+}
+
+extern "C" moe_status moe_cache_plan(moe_ctx* ctx, int32_t layer, const int32_t* ids, int32_t T,
+                                     const void* x, moe_stream stream) {
+  CHECK_CTX(ctx);
+  if (!ids || !x || layer < 0 || layer >= ctx->cfg.n_layers || T < 1 || T > ctx->cfg.max_tokens)
+    return fail(ctx, MOE_EINVAL, "moe_cache_plan: bad arguments");
+  if (ctx->state != kIdle)
+    return fail(ctx, MOE_EINVAL, "moe_cache_plan: previous layer call was not merged");
+  hipStream_t s = (hipStream_t)stream;
+  moe_status pst = prefill_settle(ctx, s);
+  if (pst != MOE_OK) return pst;
+  MOE_HIP(ctx, launch_plan(ctx, layer, ids, T, s));
+  MOE_HIP(ctx, hipEventRecord(ctx->ev_plan, s));
+  // host branch first: plan + activations to the host, then the host experts
+  MOE_HIP(ctx, hipStreamWaitEvent(ctx->side, ctx->ev_plan, 0));
+  MOE_HIP(ctx, hipMemcpyAsync(ctx->hstage, ctx->plan.hblock, ctx->plan.hblock_bytes,
+                              hipMemcpyDeviceToHost, ctx->side));
+  MOE_HIP(ctx, hipMemcpyAsync(ctx->xstage, x,
+                              (size_t)T * ctx->cfg.hidden * dtype_bytes(ctx->cfg.act_dtype),
+                              hipMemcpyDeviceToHost, ctx->side));
+  MOE_HIP(ctx, hipLaunchHostFunc(ctx->side, host_branch_cb, ctx));
+  MOE_HIP(ctx, hipEventRecord(ctx->ev_cpu, ctx->side));
+  // GPU miss path: batched copy of the admitted experts into their slots
+  MOE_HIP(ctx, launch_fill(ctx, s));
+  ctx->state = kPlanned;
+  ctx->cur_layer = layer;
+  ctx->cur_T = T;
+  return MOE_OK;
+}
+
+extern "C" moe_status moe_expert_ffn(moe_ctx* ctx, int32_t layer, const void* x, int32_t T,
+                                     moe_stream stream) {
+  CHECK_CTX(ctx);
+  if (!x || ctx->state != kPlanned || layer != ctx->cur_layer || T != ctx->cur_T)
+    return fail(ctx, MOE_EINVAL, "moe_expert_ffn: must follow moe_cache_plan of the same layer and T");
+  MOE_HIP(ctx, launch_ffn(ctx, x, T, (hipStream_t)stream));
+  ctx->state = kEvaluated;
+  return MOE_OK;
+}
+
+extern "C" moe_status moe_merge(moe_ctx* ctx, const float* w, int32_t T, void* y,
+                                moe_stream stream) {
+  CHECK_CTX(ctx);
+  if (!w || !y || ctx->state != kEvaluated || T != ctx->cur_T)
+    return fail(ctx, MOE_EINVAL, "moe_merge: must follow moe_expert_ffn with the same T");
+  hipStream_t s = (hipStream_t)stream;
+  MOE_HIP(ctx, hipStreamWaitEvent(s, ctx->ev_cpu, 0));
+  MOE_HIP(ctx, launch_merge(ctx, w, T, y, s));
+  ctx->state = kIdle;
+  return MOE_OK;
+}
+
+extern "C" moe_status moe_plan_view_get(moe_ctx* ctx, moe_plan_view* v) {
+  if (!ctx || !v) return fail(nullptr, MOE_EINVAL, "moe_plan_view_get: NULL argument");
+  PlanBufs& p = ctx->plan;
+  v->counts = p.counts;
+  v->uniq = p.uniq; v->hits = p.hits; v->misses = p.misses; v->victims = p.victims;
+  v->fill_u = p.fill_u; v->fill_slot = p.fill_slot; v->fill_old = p.fill_old;
+  v->cpu_u = p.cpu_u; v->gpu_u = p.gpu_u; v->gpu_slot = p.gpu_slot; v->slot_map = p.slot_map;
+  v->id2slot = ctx->id2slot; v->slot2id = ctx->slot2id; v->slot_ts = ctx->slot_ts;
+  v->tick = &ctx->dstate->tick;
+  v->p_gpu = ctx->p_gpu; v->p_cpu = ctx->p_cpu;
+  v->slot_base = ctx->pool.base;
+  v->n_slots = ctx->n_slots; v->max_slots = ctx->cfg.max_slots;
+  v->umax = ctx->umax; v->kmax = ctx->kmax;
+  return MOE_OK;
+}
+
+extern "C" moe_status moe_ctx_stats(moe_ctx* ctx, moe_stats* out) {
+  CHECK_CTX(ctx);
+  if (!out) return fail(ctx, MOE_EINVAL, "moe_ctx_stats: out is NULL");
+  MOE_HIP(ctx, hipDeviceSynchronize());
+  DevState ds;
+  MOE_HIP(ctx, hipMemcpy(&ds, ctx->dstate, sizeof ds, hipMemcpyDeviceToHost));
+  std::vector<int32_t> s2i(std::max(1, ctx->n_slots));
+  if (ctx->n_slots)
+    MOE_HIP(ctx, hipMemcpy(s2i.data(), ctx->slot2id, 4 * (size_t)ctx->n_slots, hipMemcpyDeviceToHost));
+  out->n_slots = ctx->n_slots;
+  out->occupied = 0;
+  for (int s = 0; s < ctx->n_slots; ++s) out->occupied += s2i[s] >= 0;
+  out->plans = ds.plans; out->hits = ds.hits; out->fills = ds.fills; out->cpu = ds.cpu;
+  out->evictions = ds.evictions; out->prefill_layers = ds.prefill_layers;
+  out->resizes = 0;
+  return MOE_OK;
+}
+
+// ------------------------------------------------------------------ resize
+static moe_status drain(moe_ctx* ctx, int32_t timeout_ms) {
+  auto t0 = std::chrono::steady_clock::now();
+  hipEvent_t ev;
+  MOE_HIP(ctx, hipEventCreateWithFlags(&ev, hipEventDisableTiming));
+  // everything enqueued on the device so far, on any stream
+  hipError_t e = hipEventRecord(ev, nullptr);
+  if (e != hipSuccess) {
+    (void)hipEventDestroy(ev);
+    return hip_fail(ctx, e, "hipEventRecord");
+  }
+  for (;;) {
+    bool done = hipEventQuery(ev) == hipSuccess && hipStreamQuery(ctx->side) == hipSuccess &&
+                hipStreamQuery(ctx->copy) == hipSuccess;
+    if (done) break;
+    double ms = std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t0).count();
+    if (timeout_ms >= 0 && ms > timeout_ms) {
+      (void)hipEventDestroy(ev);
+      return fail(ctx, MOE_ETIMEDOUT, "moe_cache_resize: work still in flight");
+    }
+    std::this_thread::sleep_for(std::chrono::microseconds(50));
+  }
+  (void)hipEventDestroy(ev);
+  MOE_HIP(ctx, hipDeviceSynchronize());
+  return MOE_OK;
+}
+
+extern "C" moe_status moe_cache_resize(moe_ctx* ctx, int32_t new_n, int32_t timeout_ms) {
+  CHECK_CTX(ctx);
+  if (new_n < 0 || new_n > ctx->cfg.max_slots)
+    return fail(ctx, MOE_EINVAL, "moe_cache_resize: new_n_slots out of 0..max_slots");
+  if (ctx->state != kIdle) return fail(ctx, MOE_EINVAL, "moe_cache_resize: a layer call is open");
+  moe_status st = drain(ctx, timeout_ms);
+  if (st != MOE_OK) return st;
+  const int32_t n = ctx->n_slots;
+  std::vector<int32_t> s2i(std::max(1, n));
+  std::vector<int64_t> ts(std::max(1, n));
+  if (n) {
+    MOE_HIP(ctx, hipMemcpy(s2i.data(), ctx->slot2id, 4 * (size_t)n, hipMemcpyDeviceToHost));
+    MOE_HIP(ctx, hipMemcpy(ts.data(), ctx->slot_ts, 8 * (size_t)n, hipMemcpyDeviceToHost));
+  }
+  // evict in victim order, (tick, slot) ascending, until new_n remain
+  std::vector<int32_t> occ;
+  for (int s = 0; s < n; ++s)
+    if (s2i[s] >= 0) occ.push_back(s);
+  std::vector<int32_t> lru = occ;
+  std::stable_sort(lru.begin(), lru.end(), [&](int a, int b) {
+    return ts[a] != ts[b] ? ts[a] < ts[b] : a < b;
+  });
+  size_t n_keep = std::min<size_t>((size_t)new_n, occ.size());
+  std::vector<char> keep(std::max(1, n), 0);
+  for (size_t i = lru.size() - n_keep; i < lru.size(); ++i) keep[lru[i]] = 1;
+  // new tables
+  std::vector<int32_t> i2s((size_t)ctx->n_ids, -1);
+  std::vector<int32_t> ns2i(std::max(1, new_n), -1);
+  std::vector<int64_t> nts(std::max(1, new_n), -1);
+  std::vector<std::pair<int32_t, int32_t>> moves;
+  int32_t j = 0;
+  for (int s = 0; s < n; ++s) {
+    if (!keep[s]) continue;
+    ns2i[j] = s2i[s];
+    nts[j] = ts[s];
+    i2s[s2i[s]] = j;
+    if (s != j) moves.push_back({s, j});
+    ++j;
+  }
+  // grow the mapping first, copy survivors forward, then release the tail
+  size_t need = (size_t)std::max(new_n, n) * ctx->stride;
+  if ((st = pool_map_to(ctx, need)) != MOE_OK) return st;
+  for (auto& mv : moves)
+    MOE_HIP(ctx, hipMemcpyAsync(ctx->pool.base + (size_t)mv.second * ctx->stride,
+                                ctx->pool.base + (size_t)mv.first * ctx->stride, ctx->stride,
+                                hipMemcpyDeviceToDevice, ctx->copy));
+  MOE_HIP(ctx, hipMemcpyAsync(ctx->id2slot, i2s.data(), 4 * i2s.size(), hipMemcpyHostToDevice, ctx->copy));
+  if (new_n) {
+    MOE_HIP(ctx, hipMemcpyAsync(ctx->slot2id, ns2i.data(), 4 * (size_t)new_n, hipMemcpyHostToDevice, ctx->copy));
+    MOE_HIP(ctx, hipMemcpyAsync(ctx->slot_ts, nts.data(), 8 * (size_t)new_n, hipMemcpyHostToDevice, ctx->copy));
+  }
+  int32_t nn = new_n;
+  MOE_HIP(ctx, hipMemcpyAsync(&ctx->dstate->n_slots, &nn, 4, hipMemcpyHostToDevice, ctx->copy));
+  MOE_HIP(ctx, hipStreamSynchronize(ctx->copy));
+  if ((st = pool_unmap_to(ctx, (size_t)new_n * ctx->stride)) != MOE_OK) return st;
+  ctx->n_slots = new_n;
+  // resize drained the copy stream: an unconsumed prefetch is simply gone
+  // (its slots were emptied above unless admitted)
+  ctx->pf.buf_layer[0] = ctx->pf.buf_layer[1] = -1;
+  return MOE_OK;
+}
+
+// ------------------------------------------------------------------ prefill
+static moe_status prefill_setup(moe_ctx* ctx) {
+  auto& pf = ctx->pf;
+  if (pf.ready) return MOE_OK;
+  const moe_config& c = ctx->cfg;
+  const size_t Tk = (size_t)c.max_prefill_tokens * c.top_k;
+  MOE_HIP(ctx, hipMalloc((void**)&pf.counts, 4 * (size_t)c.n_experts));
+  MOE_HIP(ctx, hipMalloc((void**)&pf.offsets, 4 * (size_t)(c.n_experts + 1)));
+  MOE_HIP(ctx, hipMalloc((void**)&pf.cursor, 4 * (size_t)c.n_experts));
+  MOE_HIP(ctx, hipMalloc((void**)&pf.perm, 4 * Tk));
+  MOE_HIP(ctx, hipMalloc((void**)&pf.hmid, 2 * Tk * c.inter));
+  MOE_HIP(ctx, hipMalloc((void**)&pf.prow, 4 * Tk * c.hidden));
+  for (int b = 0; b < 2; ++b)
+    MOE_HIP(ctx, hipEventCreateWithFlags(&pf.ev_copied[b], hipEventDisableTiming));
+  MOE_HIP(ctx, hipEventCreateWithFlags(&pf.ev_start, hipEventDisableTiming));
+  pf.ready = true;
+  return MOE_OK;
+}
+
+// Issue the slab copy of `layer` into buffer layer % 2 on the copy stream.
+// It waits for everything enqueued on the caller's stream before this call
+// (ev_start): earlier readers of that buffer, decode work on those slots.
+static moe_status prefill_issue(moe_ctx* ctx, int32_t layer) {
+  auto& pf = ctx->pf;
+  int b = layer % 2;
+  const int E = ctx->cfg.n_experts;
+  MOE_HIP(ctx, hipStreamWaitEvent(ctx->copy, pf.ev_start, 0));
+  MOE_HIP(ctx, hipMemcpyAsync(ctx->pool.base + (size_t)b * E * ctx->stride,
+                              ctx->host_pool + (size_t)layer * E * ctx->stride, (size_t)E * ctx->stride,
+                              hipMemcpyHostToDevice, ctx->copy));
+  MOE_HIP(ctx, hipEventRecord(pf.ev_copied[b], ctx->copy));
+  pf.buf_layer[b] = layer;
+  pf.admitted[b] = false;
+  return MOE_OK;
+}
+
+// A prefetched slab that no prefill call consumed is admitted before decode
+// touches the pool, so the tables describe what the slots hold.
+moe_status moert::prefill_settle(moe_ctx* ctx, hipStream_t s) {
+  auto& pf = ctx->pf;
+  if (!pf.ready) return MOE_OK;
+  for (int b = 0; b < 2; ++b) {
+    if (pf.buf_layer[b] >= 0 && !pf.admitted[b]) {
+      MOE_HIP(ctx, hipStreamWaitEvent(s, pf.ev_copied[b], 0));
+      MOE_HIP(ctx, launch_prefill_admit(ctx, pf.buf_layer[b], s));
+      pf.admitted[b] = true;
+    }
+    pf.buf_layer[b] = -1;  // decode fills may overwrite the buffer from here on
+  }
+  return MOE_OK;
+}
+
+extern "C" moe_status moe_prefill_layer(moe_ctx* ctx, int32_t layer, const void* x, int32_t T,
+                                        const int32_t* ids, const float* w, void* y,
+                                        moe_stream stream) {
+  CHECK_CTX(ctx);
+  const moe_config& c = ctx->cfg;
+  if (!x || !ids || !w || !y || layer < 0 || layer >= c.n_layers || T < 1 || T > c.max_prefill_tokens)
+    return fail(ctx, MOE_EINVAL, "moe_prefill_layer: bad arguments");
+  if (ctx->state != kIdle) return fail(ctx, MOE_EINVAL, "moe_prefill_layer: a decode layer call is open");
+  if (ctx->n_slots < 2 * c.n_experts)
+    return fail(ctx, MOE_ENOSPC, "moe_prefill_layer: two full-layer buffers do not fit in the slot pool");
+  moe_status st = prefill_setup(ctx);
+  if (st != MOE_OK) return st;
+  auto& pf = ctx->pf;
+  hipStream_t s = (hipStream_t)stream;
+  const int b = layer % 2;
+  MOE_HIP(ctx, hipEventRecord(pf.ev_start, s));
+  if (pf.buf_layer[b] != layer && (st = prefill_issue(ctx, layer)) != MOE_OK) return st;
+  // stream the next layer into the other buffer while this one computes
+  if (layer + 1 < c.n_layers && pf.buf_layer[1 - b] != layer + 1 &&
+      (st = prefill_issue(ctx, layer + 1)) != MOE_OK)
+    return st;
+  MOE_HIP(ctx, hipStreamWaitEvent(s, pf.ev_copied[b], 0));
+  if (!pf.admitted[b]) {
+    MOE_HIP(ctx, launch_prefill_admit(ctx, layer, s));
+    pf.admitted[b] = true;
+  }
+  MOE_HIP(ctx, launch_prefill_compute(ctx, layer, x, T, ids, w, y, s));
+  return MOE_OK;
+}

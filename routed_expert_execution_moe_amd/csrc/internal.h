@@ -1,0 +1,181 @@
+// Internal declarations of the routed-expert MoE library (gfx950, HIP).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdint>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/moert.h"
+
+namespace moert {
+
+constexpr int kMaxExperts = 1024;
+constexpr int kMaxTopK = 32;
+constexpr int kMaxSlots = 32768;
+constexpr int kMaxDecodeTokens = 256;
+constexpr int kPlanThreads = 1024;
+
+// Device-resident scalars the control kernel owns: the LRU tick and the
+// running counters of the pool table.
+struct DevState {
+  int64_t tick;
+  int64_t plans, hits, fills, cpu, evictions;
+  int64_t prefill_layers;
+  int32_t n_slots;   // current budget, read by the control kernel
+  int32_t pad;
+};
+
+// Everything the host branch needs from one plan, packed so a single
+// device-to-host copy moves it.  Written by the control kernel.
+struct HostBlockHeader {
+  moe_plan_counts c;
+  int32_t layer, T;
+};
+
+// Fixed-shape plan outputs in device memory (one allocation).
+struct PlanBufs {
+  moe_plan_counts* counts;
+  int32_t *uniq, *hits, *misses, *victims, *fill_u, *fill_slot, *fill_old;
+  int32_t *cpu_u, *gpu_u, *gpu_slot, *slot_map;
+  // host block mirror: header | ids[maxTk] | slot_map[maxTk]
+  uint8_t* hblock;
+  size_t hblock_bytes;
+};
+
+// One physical chunk of the slot pool mapped into the reserved range.
+struct PoolChunk {
+  hipMemGenericAllocationHandle_t h;
+  size_t offset, bytes;
+};
+
+struct SlotPool {
+  uint8_t* base = nullptr;     // start of the reserved (or allocated) range
+  size_t reserved = 0;         // bytes of address space
+  size_t mapped = 0;           // bytes currently backed
+  size_t gran = 0;             // chunk size (multiple of the VMM granularity)
+  bool vmm = false;            // false: one plain allocation of `reserved`
+  std::vector<PoolChunk> chunks;
+};
+
+struct CpuPool;  // host worker pool (cpu_branch.cpp)
+
+// Work description handed to the host branch callback.
+struct CpuJob {
+  moe_ctx* ctx;
+};
+
+enum CallState { kIdle = 0, kPlanned = 1, kEvaluated = 2 };
+
+}  // namespace moert
+
+struct moe_ctx {
+  moe_config cfg;
+  int device = 0;
+  size_t stride = 0;          // slot / bank stride
+  size_t expert_bytes = 0;
+  int64_t n_ids = 0;
+  int32_t n_slots = 0;
+  int32_t umax = 0;           // plan list bound: min(max_tokens*k, E)
+  int32_t kmax = 0;           // victim list bound for the largest budget
+  int32_t cpu_threads = 0;
+
+  // host expert pool (caller-owned, pinned + mapped)
+  uint8_t* host_pool = nullptr;
+  const uint8_t* host_pool_dev = nullptr;
+  size_t host_pool_bytes = 0;
+
+  moert::SlotPool pool;
+
+  // residency tables (device)
+  int32_t* id2slot = nullptr;
+  int32_t* slot2id = nullptr;
+  int64_t* slot_ts = nullptr;
+  moert::DevState* dstate = nullptr;
+
+  moert::PlanBufs plan{};
+  uint8_t* plan_alloc = nullptr;
+
+  // partial rows and decode intermediate
+  float* p_gpu = nullptr;      // device [max_tokens*k][H]
+  float* p_cpu = nullptr;      // pinned host, mapped [max_tokens*k][H]
+  const float* p_cpu_dev = nullptr;
+  float* h_mid = nullptr;      // device [max_tokens*k][I]
+
+  // host staging for the host branch (pinned)
+  uint8_t* hstage = nullptr;   // plan host block copy
+  uint8_t* xstage = nullptr;   // x copy [max_tokens][H] act dtype
+
+  // streams and events owned by the context
+  hipStream_t side = nullptr;  // host branch
+  hipStream_t copy = nullptr;  // prefill transfers
+  hipEvent_t ev_plan = nullptr, ev_cpu = nullptr;
+
+  moert::CpuPool* cpu = nullptr;
+  moert::CpuJob job{};
+
+  // decode call order
+  int state = moert::kIdle;
+  int32_t cur_layer = -1, cur_T = 0;
+
+  // prefill (allocated lazily on the first prefill call)
+  struct Prefill {
+    bool ready = false;
+    int32_t buf_layer[2] = {-1, -1};      // layer whose slab was issued into buffer b
+    bool admitted[2] = {false, false};     // tables already describe buffer b
+    hipEvent_t ev_copied[2] = {nullptr, nullptr};
+    hipEvent_t ev_start = nullptr;
+    int32_t* counts = nullptr;             // [E]
+    int32_t* offsets = nullptr;            // [E+1]
+    int32_t* cursor = nullptr;             // [E]
+    int32_t* perm = nullptr;               // [Tmax*k] pair index, grouped by expert
+    uint16_t* xg = nullptr;                // unused placeholder
+    uint16_t* hmid = nullptr;              // [Tmax*k][I] bf16 intermediate
+    float* prow = nullptr;                 // [Tmax*k][H] fp32 partial rows
+    int32_t* tiles = nullptr;              // GEMM tile schedule
+    int32_t max_tiles = 0;
+  } pf;
+
+  moe_status err = MOE_OK;     // latched HIP error
+  std::string err_msg;
+};
+
+namespace moert {
+
+// error helpers --------------------------------------------------------------
+void set_last_error(const std::string& s);
+moe_status fail(moe_ctx* ctx, moe_status s, const std::string& msg);
+moe_status hip_fail(moe_ctx* ctx, hipError_t e, const char* what);
+
+#define MOE_HIP(ctx, expr)                                   \
+  do {                                                       \
+    hipError_t _e = (expr);                                  \
+    if (_e != hipSuccess) return ::moert::hip_fail((ctx), _e, #expr); \
+  } while (0)
+
+inline int dtype_bytes(int d) { return d == MOE_F32 ? 4 : 2; }
+
+// kernel launchers (defined in the .hip files) -------------------------------
+hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w,
+                             hipStream_t s);
+hipError_t launch_plan(moe_ctx* ctx, int layer, const int32_t* ids, int T, hipStream_t s);
+hipError_t launch_fill(moe_ctx* ctx, hipStream_t s);
+hipError_t launch_ffn(moe_ctx* ctx, const void* x, int T, hipStream_t s);
+hipError_t launch_merge(moe_ctx* ctx, const float* w, int T, void* y, hipStream_t s);
+hipError_t launch_prefill_admit(moe_ctx* ctx, int layer, hipStream_t s);
+hipError_t launch_prefill_compute(moe_ctx* ctx, int layer, const void* x, int T,
+                                  const int32_t* ids, const float* w, void* y, hipStream_t s);
+hipError_t launch_table_reset(moe_ctx* ctx, hipStream_t s);
+moe_status prefill_settle(moe_ctx* ctx, hipStream_t s);
+
+// host branch -----------------------------------------------------------------
+CpuPool* cpu_pool_create(int threads);
+void cpu_pool_destroy(CpuPool* p);
+// Runs on the HIP host-function thread: evaluates the CPU-assigned experts of
+// the staged plan into ctx->p_cpu.
+void cpu_branch_run(moe_ctx* ctx);
+
+}  // namespace moert

@@ -1,0 +1,421 @@
+// The per-layer control kernel and prefill buffer admission.
+//
+// One kernel per MoE-layer call does all routing-dependent control on the
+// device (snackonai, "The Architecture, Unpacked", third decision; satyajit,
+// "Residency that follows the router"):
+//   1. dedup   the flat ids u = layer*E + ids[t][j] via an E-bit mask in LDS;
+//              ascending order falls out of wave ballots over the mask bits;
+//   2. classify each u against id2slot (hit: resident);
+//   3. q       = clamp(round_half_even(m*B_P/B_H), 1, m) in HYBRID, m in
+//              OFFLOAD, 0 in CPU; then the fetch cap and the free capacity
+//              (snackonai, "The split policy itself");
+//   4. victims the K least recently used slots by (tick, slot), current hits
+//              excluded, in one pass over the slot table: one radix select of
+//              the K-th smallest tick over register-resident keys, then a
+//              rank sort of the K survivors;
+//   5. rewrite the first q misses take the first q victims; slot_map[t][j]
+//              gets the slot, or -1 for the host.
+// Recency is one tick per call; hits and fills take that tick.
+#include "internal.h"
+
+namespace moert {
+
+constexpr int kWaves = kPlanThreads / 64;
+constexpr uint32_t kSentinel = 0xFFFFFFFFu;
+
+struct PlanArgs {
+  const int32_t* ids;
+  int32_t T, k, layer, E, K, n, mode, max_fetch;
+  int64_t bwp, bwh;
+  int32_t* id2slot;
+  int32_t* slot2id;
+  int64_t* slot_ts;
+  DevState* st;
+  PlanBufs pb;
+};
+
+__device__ inline int64_t rne_div(int64_t a, int64_t b) {
+  int64_t q = a / b, r = a - q * b;
+  if (2 * r > b || (2 * r == b && (q & 1))) ++q;
+  return q;
+}
+
+// Exclusive prefix of per-wave totals; returns this wave's offset and the sum.
+__device__ inline int wave_offset(const int* cnt, int wave, int* total) {
+  int off = 0, sum = 0;
+  for (int w = 0; w < kWaves; ++w) {
+    if (w < wave) off += cnt[w];
+    sum += cnt[w];
+  }
+  *total = sum;
+  return off;
+}
+
+__device__ inline int lane_rank(uint64_t m, int lane) {
+  return __builtin_popcountll(m & ((1ull << lane) - 1ull));
+}
+
+template <int SPT>
+__global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
+  __shared__ uint32_t s_mask[kMaxExperts / 32];
+  __shared__ int32_t s_eslot[kMaxExperts];
+  __shared__ int32_t s_miss[kMaxExperts];
+  __shared__ int32_t s_vic[kMaxExperts];
+  __shared__ uint32_t s_hitbits[kMaxSlots / 32];
+  __shared__ uint32_t s_hist[2048];
+  __shared__ int32_t s_cnt[3][kWaves];
+  __shared__ int32_t s_scan[kPlanThreads];
+  __shared__ int32_t s_scan2[kPlanThreads];
+  __shared__ uint64_t s_sel[kMaxExperts];
+  __shared__ int64_t s_tick;
+  __shared__ int32_t s_nuniq, s_nhit, s_m, s_q, s_keff, s_evict, s_ngpu;
+  __shared__ uint32_t s_prefix, s_pmask, s_kk;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int E = a.E, Tk = a.T * a.k, n = a.n;
+  const PlanBufs& pb = a.pb;
+
+  // -------------------------------------------------------------- init
+  if (tid < kMaxExperts / 32) s_mask[tid] = 0;
+  for (int i = tid; i < (n + 31) / 32; i += kPlanThreads) s_hitbits[i] = 0;
+  if (tid < E) s_eslot[tid] = -1;
+  if (tid == 0) {
+    s_tick = a.st->tick + 1;
+    s_evict = 0;
+  }
+  __syncthreads();
+  const int64_t tick = s_tick;
+
+  // -------------------------------------------------------------- 1. dedup
+  for (int i = tid; i < Tk; i += kPlanThreads) {
+    int e = a.ids[i];
+    if (e >= 0 && e < E) atomicOr(&s_mask[e >> 5], 1u << (e & 31));
+  }
+  __syncthreads();
+
+  // -------------------------------------------------------------- 2. classify
+  const int e = tid;
+  const bool present = e < E && ((s_mask[e >> 5] >> (e & 31)) & 1u);
+  const int u = a.layer * E + e;
+  int slot = -1;
+  if (present) slot = a.id2slot[u];
+  const bool hit = present && slot >= 0;
+  const bool miss = present && slot < 0;
+  const uint64_t b_pres = __ballot(present), b_hit = __ballot(hit), b_miss = __ballot(miss);
+  if (lane == 0) {
+    s_cnt[0][wave] = __builtin_popcountll(b_pres);
+    s_cnt[1][wave] = __builtin_popcountll(b_hit);
+    s_cnt[2][wave] = __builtin_popcountll(b_miss);
+  }
+  __syncthreads();
+  int n_uniq, n_hit, m;
+  const int o_pres = wave_offset(s_cnt[0], wave, &n_uniq);
+  const int o_hit = wave_offset(s_cnt[1], wave, &n_hit);
+  const int o_miss = wave_offset(s_cnt[2], wave, &m);
+  if (present) pb.uniq[o_pres + lane_rank(b_pres, lane)] = u;
+  if (hit) {
+    pb.hits[o_hit + lane_rank(b_hit, lane)] = u;
+    atomicOr(&s_hitbits[slot >> 5], 1u << (slot & 31));
+    s_eslot[e] = slot;
+    a.slot_ts[slot] = tick;  // a hit refreshes recency
+  }
+  if (miss) {
+    int p = o_miss + lane_rank(b_miss, lane);
+    s_miss[p] = u;
+    pb.misses[p] = u;
+  }
+
+  // -------------------------------------------------------------- 3. q
+  if (tid == 0) {
+    int q;
+    if (m == 0 || a.mode == MOE_CPU) q = 0;
+    else if (a.mode == MOE_OFFLOAD) q = m;
+    else {
+      int64_t r = rne_div((int64_t)m * a.bwp, a.bwh);
+      q = (int)min<int64_t>(max<int64_t>(1, r), m);
+    }
+    if (a.max_fetch > 0) q = min(q, a.max_fetch);
+    q = min(q, n - n_hit);
+    s_nuniq = n_uniq;
+    s_nhit = n_hit;
+    s_m = m;
+    s_q = q;
+    s_keff = min(a.K, n - n_hit);
+  }
+  __syncthreads();
+  const int keff = s_keff;
+
+  // -------------------------------------------------------------- 4. victims
+  if (keff > 0) {
+    // keys of this thread's contiguous slots: tick + 1 (empty = 0), hits and
+    // slots past n excluded
+    uint32_t key[SPT];
+    const int s0 = tid * SPT;
+    int ncand = 0;
+#pragma unroll
+    for (int i = 0; i < SPT; ++i) {
+      int s = s0 + i;
+      uint32_t kv = kSentinel;
+      if (s < n && !((s_hitbits[s >> 5] >> (s & 31)) & 1u)) kv = (uint32_t)(a.slot_ts[s] + 1);
+      key[i] = kv;
+    }
+    const int n_cand = n - s_nhit;
+    uint32_t tau = kSentinel;  // keys < tau are all taken
+    if (keff < n_cand) {
+      // radix select of the keff-th smallest key: 11 + 11 + 10 bits
+      if (tid == 0) {
+        s_prefix = 0;
+        s_pmask = 0;
+        s_kk = (uint32_t)keff;
+      }
+      const int shifts[3] = {21, 10, 0};
+      const uint32_t dmask[3] = {0x7FFu, 0x7FFu, 0x3FFu};
+#pragma unroll
+      for (int pass = 0; pass < 3; ++pass) {
+        for (int i = tid; i < 2048; i += kPlanThreads) s_hist[i] = 0;
+        __syncthreads();
+        const uint32_t prefix = s_prefix, pmask = s_pmask;
+#pragma unroll
+        for (int i = 0; i < SPT; ++i)
+          if (key[i] != kSentinel && (key[i] & pmask) == prefix)
+            atomicAdd(&s_hist[(key[i] >> shifts[pass]) & dmask[pass]], 1u);
+        __syncthreads();
+        // block scan over 2048 bins, two per thread
+        int c0 = s_hist[2 * tid], c1 = s_hist[2 * tid + 1];
+        int v = c0 + c1;
+        // inclusive scan of v across the block
+        int x = v;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          int y = __shfl_up(x, off);
+          if (lane >= off) x += y;
+        }
+        if (lane == 63) s_scan[wave] = x;
+        __syncthreads();
+        int wbase = 0;
+        for (int w = 0; w < wave; ++w) wbase += s_scan[w];
+        const int incl = wbase + x, excl = incl - v;
+        const uint32_t kk = s_kk;
+        __syncthreads();
+        if ((uint32_t)excl < kk && kk <= (uint32_t)incl) {
+          int bin;
+          uint32_t before;
+          if (kk <= (uint32_t)(excl + c0)) {
+            bin = 2 * tid;
+            before = excl;
+          } else {
+            bin = 2 * tid + 1;
+            before = excl + c0;
+          }
+          s_prefix = prefix | ((uint32_t)bin << shifts[pass]);
+          s_pmask = pmask | (dmask[pass] << shifts[pass]);
+          s_kk = kk - before;
+        }
+        __syncthreads();
+      }
+      tau = s_prefix;  // the keff-th smallest key
+    }
+    // take every key < tau, then the lowest slots with key == tau
+    int lt = 0, eq = 0;
+#pragma unroll
+    for (int i = 0; i < SPT; ++i) {
+      lt += key[i] < tau;
+      eq += key[i] == tau && key[i] != kSentinel;
+    }
+    // block exclusive scans of lt and eq in thread (= slot) order
+    int xl = lt, xe = eq;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      int yl = __shfl_up(xl, off), ye = __shfl_up(xe, off);
+      if (lane >= off) {
+        xl += yl;
+        xe += ye;
+      }
+    }
+    if (lane == 63) {
+      s_scan[wave] = xl;
+      s_scan2[wave] = xe;
+    }
+    __syncthreads();
+    int bl = 0, be = 0, tl = 0;
+    for (int w = 0; w < kWaves; ++w) {
+      if (w < wave) {
+        bl += s_scan[w];
+        be += s_scan2[w];
+      }
+      tl += s_scan[w];
+    }
+    int pl = bl + xl - lt;        // exclusive position among keys < tau
+    int pe = be + xe - eq;        // exclusive position among keys == tau
+    const int r = keff - tl;      // keys == tau to take
+#pragma unroll
+    for (int i = 0; i < SPT; ++i) {
+      const uint32_t kv = key[i];
+      const uint64_t packed = ((uint64_t)kv << 32) | (uint32_t)(s0 + i);
+      if (kv < tau) {
+        s_sel[pl++] = packed;
+      } else if (kv == tau && kv != kSentinel) {
+        if (pe < r) s_sel[tl + pe] = packed;
+        ++pe;
+      }
+    }
+    __syncthreads();
+    // rank sort of the keff survivors by (tick, slot)
+    if (tid < keff) {
+      const uint64_t mine = s_sel[tid];
+      int rank = 0;
+      for (int j = 0; j < keff; ++j) rank += s_sel[j] < mine;
+      s_vic[rank] = (int32_t)(mine & 0xFFFFFFFFu);
+    }
+    __syncthreads();
+  }
+  if (tid < a.K) pb.victims[tid] = tid < keff ? s_vic[tid] : -1;
+
+  // -------------------------------------------------------------- 5. rewrite
+  const int q = s_q;
+  if (tid < q) {
+    const int uu = s_miss[tid];
+    const int s = s_vic[tid];
+    const int old = a.slot2id[s];
+    if (old >= 0) {
+      a.id2slot[old] = -1;
+      atomicAdd(&s_evict, 1);
+    }
+    a.slot2id[s] = uu;
+    a.id2slot[uu] = s;
+    a.slot_ts[s] = tick;
+    s_eslot[uu - a.layer * E] = s;
+    pb.fill_u[tid] = uu;
+    pb.fill_slot[tid] = s;
+    pb.fill_old[tid] = old;
+  }
+  const int mm = s_m;
+  for (int i = q + tid; i < mm; i += kPlanThreads) pb.cpu_u[i - q] = s_miss[i];
+  __syncthreads();
+
+  // slot map (device and host block); GPU list in ascending u
+  HostBlockHeader* hb = (HostBlockHeader*)pb.hblock;
+  int32_t* hb_ids = (int32_t*)(pb.hblock + sizeof(HostBlockHeader));
+  int32_t* hb_map = hb_ids + Tk;
+  for (int i = tid; i < Tk; i += kPlanThreads) {
+    int ee = a.ids[i];
+    int sl = (ee >= 0 && ee < E) ? s_eslot[ee] : -1;
+    pb.slot_map[i] = sl;
+    hb_ids[i] = ee;
+    hb_map[i] = sl;
+  }
+  const bool on_gpu = present && s_eslot[e] >= 0;
+  const uint64_t b_gpu = __ballot(on_gpu);
+  if (lane == 0) s_cnt[0][wave] = __builtin_popcountll(b_gpu);
+  __syncthreads();
+  int n_gpu;
+  const int o_gpu = wave_offset(s_cnt[0], wave, &n_gpu);
+  if (on_gpu) {
+    int p = o_gpu + lane_rank(b_gpu, lane);
+    pb.gpu_u[p] = u;
+    pb.gpu_slot[p] = s_eslot[e];
+  }
+  if (tid == 0) {
+    moe_plan_counts c;
+    c.n_uniq = s_nuniq;
+    c.n_hit = s_nhit;
+    c.n_miss = mm;
+    c.q = q;
+    c.n_cpu = mm - q;
+    c.n_gpu = n_gpu;
+    c.K = a.K;
+    c.tick_lo = (int32_t)tick;
+    *pb.counts = c;
+    hb->c = c;
+    hb->layer = a.layer;
+    hb->T = a.T;
+    DevState* st = a.st;
+    st->tick = tick;
+    st->plans += 1;
+    st->hits += s_nhit;
+    st->fills += q;
+    st->cpu += mm - q;
+    st->evictions += s_evict;
+  }
+}
+
+hipError_t launch_plan(moe_ctx* ctx, int layer, const int32_t* ids, int T, hipStream_t s) {
+  PlanArgs a;
+  a.ids = ids;
+  a.T = T;
+  a.k = ctx->cfg.top_k;
+  a.layer = layer;
+  a.E = ctx->cfg.n_experts;
+  a.n = ctx->n_slots;
+  int64_t K = std::min<int64_t>((int64_t)ctx->cfg.max_tokens * ctx->cfg.top_k, ctx->cfg.n_experts);
+  K = std::min<int64_t>(K, a.n);
+  if (ctx->cfg.max_fetch > 0) K = std::min<int64_t>(K, ctx->cfg.max_fetch);
+  a.K = (int32_t)K;
+  a.mode = ctx->cfg.mode;
+  a.max_fetch = ctx->cfg.max_fetch;
+  a.bwp = ctx->cfg.bw_pcie_mbps;
+  a.bwh = ctx->cfg.bw_host_mbps;
+  a.id2slot = ctx->id2slot;
+  a.slot2id = ctx->slot2id;
+  a.slot_ts = ctx->slot_ts;
+  a.st = ctx->dstate;
+  a.pb = ctx->plan;
+  dim3 g(1), b(kPlanThreads);
+  const int n = a.n;
+  if (n <= kPlanThreads * 1) hipLaunchKernelGGL(plan_kernel<1>, g, b, 0, s, a);
+  else if (n <= kPlanThreads * 2) hipLaunchKernelGGL(plan_kernel<2>, g, b, 0, s, a);
+  else if (n <= kPlanThreads * 4) hipLaunchKernelGGL(plan_kernel<4>, g, b, 0, s, a);
+  else if (n <= kPlanThreads * 8) hipLaunchKernelGGL(plan_kernel<8>, g, b, 0, s, a);
+  else if (n <= kPlanThreads * 16) hipLaunchKernelGGL(plan_kernel<16>, g, b, 0, s, a);
+  else hipLaunchKernelGGL(plan_kernel<32>, g, b, 0, s, a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- prefill admission
+// Buffer b = layer % 2 is slots [b*E, (b+1)*E); expert e of the layer sits in
+// slot b*E + e with one tick for the layer.  The buffer's previous occupants
+// are evicted and any other slot still holding an expert of this layer is
+// emptied (satyajit, "Prefill: hide the pool behind the wire").
+__global__ __launch_bounds__(kMaxExperts) void prefill_admit_kernel(int layer, int E, int32_t* id2slot,
+                                                                    int32_t* slot2id, int64_t* slot_ts,
+                                                                    DevState* st) {
+  __shared__ int64_t s_tick;
+  const int e = threadIdx.x;
+  const int b = layer & 1;
+  if (e == 0) s_tick = st->tick + 1;
+  // other slots holding this layer's experts (outside the buffer) are emptied
+  if (e < E) {
+    const int u = layer * E + e;
+    const int s = id2slot[u];
+    if (s >= 0 && (s < b * E || s >= (b + 1) * E)) {
+      slot2id[s] = -1;
+      slot_ts[s] = -1;
+    }
+  }
+  __syncthreads();
+  // evict the buffer's occupants
+  if (e < E) {
+    const int s = b * E + e;
+    const int old = slot2id[s];
+    if (old >= 0) id2slot[old] = -1;
+  }
+  __syncthreads();
+  if (e < E) {
+    const int s = b * E + e, u = layer * E + e;
+    slot2id[s] = u;
+    id2slot[u] = s;
+    slot_ts[s] = s_tick;
+  }
+  if (e == 0) {
+    st->tick = s_tick;
+    st->prefill_layers += 1;
+  }
+}
+
+hipError_t launch_prefill_admit(moe_ctx* ctx, int layer, hipStream_t s) {
+  hipLaunchKernelGGL(prefill_admit_kernel, dim3(1), dim3(kMaxExperts), 0, s, layer,
+                     ctx->cfg.n_experts, ctx->id2slot, ctx->slot2id, ctx->slot_ts, ctx->dstate);
+  return hipGetLastError();
+}
+
+}  // namespace moert
