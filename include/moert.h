@@ -87,6 +87,7 @@ typedef struct {
   int32_t mode;          /* moe_mode                                          */
   int32_t cpu_threads;   /* host worker threads; 0 = one per available core   */
   int32_t max_prefill_tokens; /* largest prefill chunk; 0 disables prefill    */
+  int32_t timing;        /* 1: time every launched phase with HIP events      */
 } moe_config;
 
 /* Bytes of one expert bank == one device slot stride (expert bytes rounded up
@@ -229,6 +230,22 @@ typedef struct {
 } moe_stats;
 
 moe_status moe_ctx_stats(moe_ctx* ctx, moe_stats* out);
+
+/* Device time per phase, summed since creation (or the last reset), when the
+ * context was created with cfg.timing = 1: each call brackets the kernels it
+ * launches with a pair of HIP events on the stream they run on.  HOST is the
+ * wall time of the host branch callback.  Synchronises the device; not for
+ * the hot path.  MOE_EINVAL if timing is off. */
+enum {
+  MOE_T_ROUTE = 0, MOE_T_PLAN = 1, MOE_T_FILL = 2, MOE_T_FFN = 3, MOE_T_MERGE = 4,
+  MOE_T_HOST = 5, MOE_T_PREFILL_COPY = 6, MOE_T_PREFILL_GEMM = 7, MOE_T_COUNT = 8
+};
+typedef struct {
+  int64_t calls[MOE_T_COUNT];
+  double ms[MOE_T_COUNT];
+} moe_timing;
+
+moe_status moe_ctx_timing(moe_ctx* ctx, moe_timing* out, int32_t reset);
 
 const char* moe_strerror(moe_status s);
 /* Text of the last error on the calling thread ("" if none). */

@@ -31,7 +31,7 @@ class MoeConfig(ctypes.Structure):
                 ("max_tokens", ctypes.c_int32), ("bw_pcie_mbps", ctypes.c_int64),
                 ("bw_host_mbps", ctypes.c_int64), ("max_fetch", ctypes.c_int32),
                 ("mode", ctypes.c_int32), ("cpu_threads", ctypes.c_int32),
-                ("max_prefill_tokens", ctypes.c_int32)]
+                ("max_prefill_tokens", ctypes.c_int32), ("timing", ctypes.c_int32)]
 
 
 class PlanCounts(ctypes.Structure):
@@ -57,6 +57,16 @@ class Stats(ctypes.Structure):
                 ("plans", ctypes.c_int64), ("hits", ctypes.c_int64), ("fills", ctypes.c_int64),
                 ("cpu", ctypes.c_int64), ("evictions", ctypes.c_int64),
                 ("prefill_layers", ctypes.c_int64), ("resizes", ctypes.c_int64)]
+
+
+PHASES = ("route", "plan", "fill", "ffn", "merge", "host", "prefill_copy", "prefill_gemm")
+
+
+class Timing(ctypes.Structure):
+    _fields_ = [("calls", ctypes.c_int64 * 8), ("ms", ctypes.c_double * 8)]
+
+    def as_dict(self):
+        return {p: dict(calls=self.calls[i], ms=self.ms[i]) for i, p in enumerate(PHASES)}
 
 
 class MoertError(RuntimeError):
@@ -93,6 +103,7 @@ def lib():
             "moe_prefill_layer": ([vp, i32, vp, i32, vp, vp, vp, vp], i32),
             "moe_plan_view_get": ([vp, ctypes.POINTER(PlanView)], i32),
             "moe_ctx_stats": ([vp, ctypes.POINTER(Stats)], i32),
+            "moe_ctx_timing": ([vp, ctypes.POINTER(Timing), i32], i32),
             "moe_strerror": ([i32], ctypes.c_char_p),
             "moe_last_error": ([], ctypes.c_char_p),
         }
@@ -131,10 +142,11 @@ def _stream(s) -> int | None:
 
 def config(L, E, k, H, I, w_dtype, act_dtype, n_slots, max_slots=None, max_tokens=1,
            bw_pcie_mbps=1, bw_host_mbps=1, max_fetch=0, mode=MOE_HYBRID, cpu_threads=0,
-           max_prefill_tokens=0) -> MoeConfig:
+           max_prefill_tokens=0, timing=0) -> MoeConfig:
     return MoeConfig(L, E, k, H, I, DTYPES.get(w_dtype, w_dtype), DTYPES.get(act_dtype, act_dtype),
                      n_slots, n_slots if max_slots is None else max_slots, max_tokens,
-                     bw_pcie_mbps, bw_host_mbps, max_fetch, mode, cpu_threads, max_prefill_tokens)
+                     bw_pcie_mbps, bw_host_mbps, max_fetch, mode, cpu_threads, max_prefill_tokens,
+                     timing)
 
 
 # ------------------------------------------------------------------ the C-ABI calls
@@ -200,6 +212,12 @@ def moe_ctx_stats(ctx) -> Stats:
     s = Stats()
     _check(lib().moe_ctx_stats(ctx, ctypes.byref(s)), "moe_ctx_stats")
     return s
+
+
+def moe_ctx_timing(ctx, reset=False) -> dict:
+    t = Timing()
+    _check(lib().moe_ctx_timing(ctx, ctypes.byref(t), 1 if reset else 0), "moe_ctx_timing")
+    return t.as_dict()
 
 
 def moe_strerror(status: int) -> str:

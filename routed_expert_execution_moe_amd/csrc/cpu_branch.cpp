@@ -4,23 +4,29 @@
 // in place; "Technical Moats": a persistent worker pool pinned to cores with
 // SIMD and in-kernel dequantisation).
 //
-// It runs inside a HIP host-function callback on the context's side stream,
-// so it never calls HIP.  Inputs: the plan's host block (layer, T, ids,
-// slot map) and the activations, copied to pinned staging by the side stream.
-// Output: fp32 rows P_cpu[t*k + j][H] for every pair whose slot map is -1, in
-// pinned, device-mapped memory the merge kernel reads.
+// Hand-off without host synchronisation: when a call has host work the control
+// kernel writes the plan, ids, slot map and activations into pinned,
+// device-mapped memory and then rings a doorbell (a sequence number).  A
+// persistent poller thread of the context sees it, runs the host experts with
+// its worker pool, writes fp32 rows P_cpu[t*k + j][H] for every pair whose
+// slot map is -1 into pinned, device-mapped memory, and publishes the
+// sequence number as done.  The merge kernel of that call waits for it (only
+// for tokens with host pairs), with a time limit.  The poller never calls HIP.
 #include <immintrin.h>
 #include <pthread.h>
 #include <sched.h>
 
 #include <algorithm>
 #include <atomic>
+#include <chrono>
 #include <cmath>
 #include <condition_variable>
 #include <functional>
 #include <mutex>
 #include <thread>
 #include <vector>
+#include <cstdio>
+#include <cstdlib>
 
 #include "internal.h"
 
@@ -86,13 +92,16 @@ CpuPool* cpu_pool_create(int threads) {
   if (sched_getaffinity(0, sizeof cs, &cs) == 0)
     for (int c = 0; c < CPU_SETSIZE; ++c)
       if (CPU_ISSET(c, &cs)) cores.push_back(c);
+  // Workers 1..n-1 are pinned to the highest cores, one each, when there are
+  // enough; the callback thread (worker 0), the caller's issue thread and the
+  // HIP runtime threads keep the low cores.
+  const bool pin = (int)cores.size() >= p->n + 2;
   for (int i = 1; i < p->n; ++i) {
     p->th.emplace_back([p, i] { p->worker(i); });
-    if (cores.size() > 1) {
-      // keep the first core for the caller's threads, spread workers over the rest
+    if (pin) {
       cpu_set_t one;
       CPU_ZERO(&one);
-      CPU_SET(cores[1 + (i - 1) % (cores.size() - 1)], &one);
+      CPU_SET(cores[cores.size() - i], &one);
       pthread_setaffinity_np(p->th.back().native_handle(), sizeof one, &one);
     }
   }
@@ -198,7 +207,103 @@ struct Expert {
   std::vector<int> pairs;  // t*k + j
 };
 
-void cpu_branch_run(moe_ctx* ctx) {
+static void cpu_branch_body(moe_ctx* ctx);
+
+// Opt-in phase trace of the host branch (MOERT_HOST_TRACE=1): averages of the
+// gate/up and down phases over calls with host work, on stderr.
+struct HostTrace {
+  bool on = false;
+  int64_t calls = 0, experts = 0;
+  double p1 = 0, p2 = 0;
+};
+static HostTrace g_trace = [] {
+  HostTrace t;
+  const char* v = getenv("MOERT_HOST_TRACE");
+  t.on = v && v[0] == '1';
+  return t;
+}();
+
+static inline double now_us() {
+  return std::chrono::duration<double, std::micro>(
+             std::chrono::steady_clock::now().time_since_epoch()).count();
+}
+
+struct HostBranch {
+  std::thread th;
+  std::atomic<bool> stop{false};
+  std::atomic<int64_t> last{0};  // last doorbell value answered
+};
+
+static void poller(moe_ctx* ctx) {
+  HostBranch* hb = ctx->hb;
+  const volatile int64_t* bell = (const volatile int64_t*)ctx->hstage;  // HostBlockHeader::seq
+  int64_t last = 0;
+  int idle = 0;
+  while (!hb->stop.load(std::memory_order_relaxed)) {
+    const int64_t s = *bell;
+    if (s == last) {
+      // spin while calls are arriving; back off to short sleeps when idle
+      if (++idle < (1 << 16)) {
+        _mm_pause();
+      } else {
+        std::this_thread::sleep_for(std::chrono::microseconds(20));
+      }
+      continue;
+    }
+    idle = 0;
+    std::atomic_thread_fence(std::memory_order_acquire);
+    if (ctx->timing) {
+      auto t0 = std::chrono::steady_clock::now();
+      cpu_branch_body(ctx);
+      auto ns = std::chrono::duration_cast<std::chrono::nanoseconds>(
+          std::chrono::steady_clock::now() - t0);
+      ctx->timing->host_ns += ns.count();
+      ctx->timing->host_calls += 1;
+    } else {
+      cpu_branch_body(ctx);
+    }
+    last = s;
+    // rows first, then the completion word (x86 stores are not reordered)
+    std::atomic_thread_fence(std::memory_order_release);
+    ((volatile HostSync*)ctx->sync)->done = s;
+    hb->last.store(s, std::memory_order_release);
+  }
+}
+
+bool host_branch_start(moe_ctx* ctx) {
+  ctx->hb = new (std::nothrow) HostBranch();
+  if (!ctx->hb) return false;
+  ctx->hb->th = std::thread(poller, ctx);
+  // the poller is worker 0: keep it off the workers' cores
+  cpu_set_t cs;
+  std::vector<int> cores;
+  if (sched_getaffinity(0, sizeof cs, &cs) == 0)
+    for (int c = 0; c < CPU_SETSIZE; ++c)
+      if (CPU_ISSET(c, &cs)) cores.push_back(c);
+  if ((int)cores.size() >= ctx->cpu_threads + 2) {
+    cpu_set_t one;
+    CPU_ZERO(&one);
+    CPU_SET(cores[cores.size() - ctx->cpu_threads], &one);
+    pthread_setaffinity_np(ctx->hb->th.native_handle(), sizeof one, &one);
+  }
+  return true;
+}
+
+void host_branch_stop(moe_ctx* ctx) {
+  if (!ctx->hb) return;
+  ctx->hb->stop = true;
+  if (ctx->hb->th.joinable()) ctx->hb->th.join();
+  delete ctx->hb;
+  ctx->hb = nullptr;
+}
+
+bool host_branch_idle(moe_ctx* ctx) {
+  if (!ctx->hb) return true;
+  const volatile int64_t* bell = (const volatile int64_t*)ctx->hstage;
+  return ctx->hb->last.load(std::memory_order_acquire) == *bell;
+}
+
+static void cpu_branch_body(moe_ctx* ctx) {
   const moe_config& c = ctx->cfg;
   const HostBlockHeader* hb = (const HostBlockHeader*)ctx->hstage;
   const int n_cpu = hb->c.n_cpu;
@@ -226,6 +331,8 @@ void cpu_branch_run(moe_ctx* ctx) {
   if (!any || ex.empty()) return;
   (void)n_cpu;
   const int nex = (int)ex.size();
+  const double t_start = g_trace.on ? now_us() : 0.0;
+  double t_p1 = 0.0, t_p2 = 0.0;
 
   // activations in fp32 (MXFP4: nibble order per 32-block)
   std::vector<float> xf((size_t)T * H);
@@ -303,6 +410,7 @@ void cpu_branch_run(moe_ctx* ctx) {
     }
   });
   (void)eb;
+  if (g_trace.on) t_p1 = now_us();
   // phase 2: down rows
   ctx->cpu->run([&](int wi, int nw) {
     const int64_t R = (int64_t)nex * H;
@@ -331,6 +439,19 @@ void cpu_branch_run(moe_ctx* ctx) {
       for (int t = 0; t < nt; ++t) ctx->p_cpu[(size_t)X.pairs[t] * H + row] = o[t];
     }
   });
+  if (g_trace.on) {
+    t_p2 = now_us();
+    HostTrace& tr = g_trace;
+    tr.calls += 1;
+    tr.experts += nex;
+    tr.p2 += t_p2 - t_p1;
+    tr.p1 += t_p1 - t_start;
+    (void)tr;
+    if (tr.calls % 2000 == 0)
+      fprintf(stderr, "[moert host] %lld calls with host work, %.2f experts/call, gate+up %.1f us, "
+              "down %.1f us per call (%d threads)\n", (long long)tr.calls,
+              (double)tr.experts / tr.calls, tr.p1 / tr.calls, tr.p2 / tr.calls, ctx->cpu_threads);
+  }
 }
 
 }  // namespace moert

@@ -235,7 +235,9 @@ static int32_t victim_bound(const moe_config& c, int32_t n_slots) {
   return (int32_t)K;
 }
 
-static void CUDA_free_all(moe_ctx* ctx);
+static void free_all(moe_ctx* ctx);
+static moe_status timing_create(moe_ctx* ctx);
+static void timing_destroy(moe_ctx* ctx);
 
 extern "C" moe_status moe_create(const moe_config* cfg, void* host_pool, size_t host_pool_bytes,
                                  moe_ctx** out) {
@@ -260,7 +262,7 @@ extern "C" moe_status moe_create(const moe_config* cfg, void* host_pool, size_t 
   ctx->host_pool_bytes = host_pool_bytes;
   moe_status st = MOE_OK;
   auto bail = [&](moe_status s) {
-    CUDA_free_all(ctx);
+    free_all(ctx);
     delete ctx;
     return s;
   };
@@ -306,8 +308,6 @@ extern "C" moe_status moe_create(const moe_config* cfg, void* host_pool, size_t 
            o_fo = take(4 * ctx->kmax);
     size_t o_cpu = take(4 * ctx->umax), o_gu = take(4 * ctx->umax), o_gs = take(4 * ctx->umax);
     size_t o_sm = take(4 * maxTk);
-    size_t hb = sizeof(HostBlockHeader) + 2 * 4 * (size_t)maxTk;
-    size_t o_hb = take(hb);
     ALLOC(ctx->plan_alloc, off);
     uint8_t* b = ctx->plan_alloc;
     PlanBufs& p = ctx->plan;
@@ -323,38 +323,50 @@ extern "C" moe_status moe_create(const moe_config* cfg, void* host_pool, size_t 
     p.gpu_u = (int32_t*)(b + o_gu);
     p.gpu_slot = (int32_t*)(b + o_gs);
     p.slot_map = (int32_t*)(b + o_sm);
-    p.hblock = b + o_hb;
-    p.hblock_bytes = hb;
+    p.hblock_bytes = sizeof(HostBlockHeader) + 2 * 4 * (size_t)maxTk;
+    p.x_offset = (p.hblock_bytes + 255) / 256 * 256;
+    p.act_bytes = dtype_bytes(cfg->act_dtype);
   }
 #undef ALLOC
 
-  // pinned staging: the host branch's inputs and its output rows
+  // pinned, device-mapped memory: the host block (control kernel -> host
+  // branch) and the host branch's output rows (host branch -> merge)
   {
     void* p = nullptr;
-    e = hipHostMalloc(&p, ctx->plan.hblock_bytes, hipHostMallocDefault);
-    if (e != hipSuccess) return bail(hip_fail(ctx, e, "hipHostMalloc hstage"));
+    size_t hb = ctx->plan.x_offset + (size_t)cfg->max_tokens * H * ctx->plan.act_bytes;
+    e = hipHostMalloc(&p, hb, hipHostMallocMapped | hipHostMallocCoherent);
+    if (e != hipSuccess) return bail(hip_fail(ctx, e, "hipHostMalloc host block"));
     ctx->hstage = (uint8_t*)p;
-    e = hipHostMalloc(&p, (size_t)cfg->max_tokens * H * dtype_bytes(cfg->act_dtype), hipHostMallocDefault);
-    if (e != hipSuccess) return bail(hip_fail(ctx, e, "hipHostMalloc xstage"));
-    ctx->xstage = (uint8_t*)p;
+    ctx->xstage = ctx->hstage + ctx->plan.x_offset;
+    memset(p, 0, hb);
+    void* d = nullptr;
+    e = hipHostGetDevicePointer(&d, p, 0);
+    if (e != hipSuccess) return bail(hip_fail(ctx, e, "hipHostGetDevicePointer host block"));
+    ctx->plan.hblock = (uint8_t*)d;
+    e = hipHostMalloc(&p, sizeof(HostSync), hipHostMallocMapped | hipHostMallocCoherent);
+    if (e != hipSuccess) return bail(hip_fail(ctx, e, "hipHostMalloc host sync"));
+    ctx->sync = (HostSync*)p;
+    memset(p, 0, sizeof(HostSync));
+    e = hipHostGetDevicePointer(&d, p, 0);
+    if (e != hipSuccess) return bail(hip_fail(ctx, e, "hipHostGetDevicePointer host sync"));
+    ctx->sync_dev = (HostSync*)d;
     e = hipHostMalloc(&p, sizeof(float) * maxTk * H, hipHostMallocMapped | hipHostMallocCoherent);
     if (e != hipSuccess) return bail(hip_fail(ctx, e, "hipHostMalloc p_cpu"));
     ctx->p_cpu = (float*)p;
     memset(p, 0, sizeof(float) * maxTk * H);
-    void* d = nullptr;
     e = hipHostGetDevicePointer(&d, p, 0);
     if (e != hipSuccess) return bail(hip_fail(ctx, e, "hipHostGetDevicePointer p_cpu"));
     ctx->p_cpu_dev = (const float*)d;
   }
 
-  e = hipStreamCreateWithFlags(&ctx->side, hipStreamNonBlocking);
-  if (e != hipSuccess) return bail(hip_fail(ctx, e, "hipStreamCreate side"));
   e = hipStreamCreateWithFlags(&ctx->copy, hipStreamNonBlocking);
   if (e != hipSuccess) return bail(hip_fail(ctx, e, "hipStreamCreate copy"));
-  e = hipEventCreateWithFlags(&ctx->ev_plan, hipEventDisableTiming);
-  if (e != hipSuccess) return bail(hip_fail(ctx, e, "hipEventCreate"));
-  e = hipEventCreateWithFlags(&ctx->ev_cpu, hipEventDisableTiming);
-  if (e != hipSuccess) return bail(hip_fail(ctx, e, "hipEventCreate"));
+  {
+    int khz = 0;
+    (void)hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, ctx->device);
+    if (khz <= 0) khz = 100000;
+    ctx->wait_ticks = (uint64_t)khz * 1000ull * 10ull;  // the merge waits at most 10 s
+  }
 
   // empty tables, tick 0
   e = launch_table_reset(ctx, ctx->copy);
@@ -362,25 +374,30 @@ extern "C" moe_status moe_create(const moe_config* cfg, void* host_pool, size_t 
   e = hipStreamSynchronize(ctx->copy);
   if (e != hipSuccess) return bail(hip_fail(ctx, e, "table reset sync"));
 
+  // Host expert bandwidth saturates well before every core is busy, and the
+  // caller's issue thread and the HIP runtime threads need cores too: by
+  // default use half the available cores, at most 8.
   int threads = cfg->cpu_threads;
   if (threads == 0) {
     cpu_set_t cs;
     int avail = (sched_getaffinity(0, sizeof cs, &cs) == 0) ? CPU_COUNT(&cs) : 1;
-    threads = std::max(1, avail - 1);
+    threads = std::max(1, std::min(8, avail / 2));
   }
   ctx->cpu_threads = threads;
   ctx->cpu = cpu_pool_create(threads);
   if (!ctx->cpu) return bail(fail(nullptr, MOE_ENOMEM, "host worker pool"));
-  ctx->job.ctx = ctx;
+  if (!host_branch_start(ctx)) return bail(fail(nullptr, MOE_ENOMEM, "host branch poller"));
+  if (cfg->timing && (st = timing_create(ctx)) != MOE_OK) return bail(st);
   *out = ctx;
   return MOE_OK;
 }
 
-static void CUDA_free_all(moe_ctx* ctx) {
+static void free_all(moe_ctx* ctx) {
+  if (ctx->copy) (void)hipStreamSynchronize(ctx->copy);
+  host_branch_stop(ctx);
+  timing_destroy(ctx);
   if (ctx->cpu) cpu_pool_destroy(ctx->cpu);
   ctx->cpu = nullptr;
-  if (ctx->side) (void)hipStreamSynchronize(ctx->side);
-  if (ctx->copy) (void)hipStreamSynchronize(ctx->copy);
   auto F = [](void* p) {
     if (p) (void)hipFree(p);
   };
@@ -392,11 +409,8 @@ static void CUDA_free_all(moe_ctx* ctx) {
     if (pf.ev_copied[b]) (void)hipEventDestroy(pf.ev_copied[b]);
   if (pf.ev_start) (void)hipEventDestroy(pf.ev_start);
   if (ctx->hstage) (void)hipHostFree(ctx->hstage);
-  if (ctx->xstage) (void)hipHostFree(ctx->xstage);
   if (ctx->p_cpu) (void)hipHostFree(ctx->p_cpu);
-  if (ctx->ev_plan) (void)hipEventDestroy(ctx->ev_plan);
-  if (ctx->ev_cpu) (void)hipEventDestroy(ctx->ev_cpu);
-  if (ctx->side) (void)hipStreamDestroy(ctx->side);
+  if (ctx->sync) (void)hipHostFree(ctx->sync);
   if (ctx->copy) (void)hipStreamDestroy(ctx->copy);
   pool_destroy(ctx);
 }
@@ -404,8 +418,88 @@ static void CUDA_free_all(moe_ctx* ctx) {
 extern "C" moe_status moe_destroy(moe_ctx* ctx) {
   if (!ctx) return MOE_OK;
   (void)hipDeviceSynchronize();
-  CUDA_free_all(ctx);
+  free_all(ctx);
   delete ctx;
+  return MOE_OK;
+}
+
+// ------------------------------------------------------------------ timing
+static moe_status timing_create(moe_ctx* ctx) {
+  ctx->timing = new (std::nothrow) Timing();
+  if (!ctx->timing) return fail(ctx, MOE_ENOMEM, "timing ring");
+  Timing& T = *ctx->timing;
+  T.a.resize(Timing::kRing);
+  T.b.resize(Timing::kRing);
+  T.phase.resize(Timing::kRing);
+  for (int i = 0; i < Timing::kRing; ++i) {
+    MOE_HIP(ctx, hipEventCreate(&T.a[i]));
+    MOE_HIP(ctx, hipEventCreate(&T.b[i]));
+  }
+  return MOE_OK;
+}
+
+static void timing_destroy(moe_ctx* ctx) {
+  if (!ctx->timing) return;
+  for (auto e : ctx->timing->a) (void)hipEventDestroy(e);
+  for (auto e : ctx->timing->b) (void)hipEventDestroy(e);
+  delete ctx->timing;
+  ctx->timing = nullptr;
+}
+
+// fold the oldest recorded pair into the totals
+static hipError_t timing_harvest_one(Timing& T) {
+  int idx = (T.head - T.used + Timing::kRing) % Timing::kRing;
+  hipError_t e = hipEventSynchronize(T.b[idx]);
+  if (e != hipSuccess) return e;
+  float ms = 0.f;
+  e = hipEventElapsedTime(&ms, T.a[idx], T.b[idx]);
+  if (e != hipSuccess) return e;
+  T.ms[T.phase[idx]] += ms;
+  T.calls[T.phase[idx]] += 1;
+  T.used -= 1;
+  return hipSuccess;
+}
+
+hipError_t moert::timing_begin(moe_ctx* ctx, int phase, hipStream_t s) {
+  if (!ctx->timing) return hipSuccess;
+  Timing& T = *ctx->timing;
+  if (T.used == Timing::kRing) {
+    hipError_t e = timing_harvest_one(T);
+    if (e != hipSuccess) return e;
+  }
+  T.phase[T.head] = phase;
+  return hipEventRecord(T.a[T.head], s);
+}
+
+hipError_t moert::timing_end(moe_ctx* ctx, hipStream_t s) {
+  if (!ctx->timing) return hipSuccess;
+  Timing& T = *ctx->timing;
+  hipError_t e = hipEventRecord(T.b[T.head], s);
+  T.head = (T.head + 1) % Timing::kRing;
+  T.used += 1;
+  return e;
+}
+
+extern "C" moe_status moe_ctx_timing(moe_ctx* ctx, moe_timing* out, int32_t reset) {
+  if (!ctx || !out) return fail(nullptr, MOE_EINVAL, "moe_ctx_timing: NULL argument");
+  if (!ctx->timing) return fail(ctx, MOE_EINVAL, "moe_ctx_timing: context created without timing");
+  MOE_HIP(ctx, hipDeviceSynchronize());
+  Timing& T = *ctx->timing;
+  while (T.used > 0) MOE_HIP(ctx, timing_harvest_one(T));
+  for (int i = 0; i < MOE_T_COUNT; ++i) {
+    out->calls[i] = T.calls[i];
+    out->ms[i] = T.ms[i];
+  }
+  out->calls[MOE_T_HOST] = T.host_calls.load();
+  out->ms[MOE_T_HOST] = T.host_ns.load() * 1e-6;
+  if (reset) {
+    for (int i = 0; i < MOE_T_COUNT; ++i) {
+      T.calls[i] = 0;
+      T.ms[i] = 0;
+    }
+    T.host_calls = 0;
+    T.host_ns = 0;
+  }
   return MOE_OK;
 }
 
@@ -413,6 +507,8 @@ extern "C" moe_status moe_destroy(moe_ctx* ctx) {
 #define CHECK_CTX(ctx)                                                        \
   do {                                                                        \
     if (!(ctx)) return fail(nullptr, MOE_EINVAL, "context is NULL");          \
+    if ((ctx)->sync && ((volatile HostSync*)(ctx)->sync)->error && (ctx)->err == MOE_OK) \
+      fail((ctx), MOE_EHIP, "merge gave up waiting for the host branch (10 s limit)"); \
     if ((ctx)->err != MOE_OK) {                                               \
       set_last_error((ctx)->err_msg);                                         \
       return (ctx)->err;                                                      \
@@ -425,14 +521,11 @@ extern "C" moe_status moe_route_topk(moe_ctx* ctx, const float* logits, int32_t 
   int tmax = std::max(ctx->cfg.max_tokens, ctx->cfg.max_prefill_tokens);
   if (!logits || !ids || !w || T < 1 || T > tmax)
     return fail(ctx, MOE_EINVAL, "moe_route_topk: bad arguments");
+  MOE_HIP(ctx, timing_begin(ctx, MOE_T_ROUTE, (hipStream_t)stream));
   MOE_HIP(ctx, launch_route_topk(logits, T, ctx->cfg.n_experts, ctx->cfg.top_k, ids, w,
                                  (hipStream_t)stream));
+  MOE_HIP(ctx, timing_end(ctx, (hipStream_t)stream));
   return MOE_OK;
-}
-
-static void host_branch_cb(void* user) {
-  moe_ctx* ctx = (moe_ctx*)user;
-  cpu_branch_run(ctx);
 }
 
 extern "C" moe_status moe_cache_plan(moe_ctx* ctx, int32_t layer, const int32_t* ids, int32_t T,
@@ -440,24 +533,25 @@ extern "C" moe_status moe_cache_plan(moe_ctx* ctx, int32_t layer, const int32_t*
   CHECK_CTX(ctx);
   if (!ids || !x || layer < 0 || layer >= ctx->cfg.n_layers || T < 1 || T > ctx->cfg.max_tokens)
     return fail(ctx, MOE_EINVAL, "moe_cache_plan: bad arguments");
+  if (((uintptr_t)x & 15) || ((uintptr_t)ids & 3))
+    return fail(ctx, MOE_EINVAL, "moe_cache_plan: x must be 16-byte aligned, ids 4-byte aligned");
   if (ctx->state != kIdle)
     return fail(ctx, MOE_EINVAL, "moe_cache_plan: previous layer call was not merged");
   hipStream_t s = (hipStream_t)stream;
   moe_status pst = prefill_settle(ctx, s);
   if (pst != MOE_OK) return pst;
-  MOE_HIP(ctx, launch_plan(ctx, layer, ids, T, s));
-  MOE_HIP(ctx, hipEventRecord(ctx->ev_plan, s));
-  // host branch first: plan + activations to the host, then the host experts
-  MOE_HIP(ctx, hipStreamWaitEvent(ctx->side, ctx->ev_plan, 0));
-  MOE_HIP(ctx, hipMemcpyAsync(ctx->hstage, ctx->plan.hblock, ctx->plan.hblock_bytes,
-                              hipMemcpyDeviceToHost, ctx->side));
-  MOE_HIP(ctx, hipMemcpyAsync(ctx->xstage, x,
-                              (size_t)T * ctx->cfg.hidden * dtype_bytes(ctx->cfg.act_dtype),
-                              hipMemcpyDeviceToHost, ctx->side));
-  MOE_HIP(ctx, hipLaunchHostFunc(ctx->side, host_branch_cb, ctx));
-  MOE_HIP(ctx, hipEventRecord(ctx->ev_cpu, ctx->side));
+  // The control kernel hands the host branch its work first (doorbell in
+  // pinned memory, answered by the poller thread); the GPU miss path follows.
+  const int64_t seq = ++ctx->call_seq;
+  MOE_HIP(ctx, timing_begin(ctx, MOE_T_PLAN, s));
+  MOE_HIP(ctx, launch_plan(ctx, layer, ids, T, x, seq, s));
+  MOE_HIP(ctx, timing_end(ctx, s));
   // GPU miss path: batched copy of the admitted experts into their slots
-  MOE_HIP(ctx, launch_fill(ctx, s));
+  if (ctx->n_slots > 0 && ctx->cfg.mode != MOE_CPU) {
+    MOE_HIP(ctx, timing_begin(ctx, MOE_T_FILL, s));
+    MOE_HIP(ctx, launch_fill(ctx, s));
+    MOE_HIP(ctx, timing_end(ctx, s));
+  }
   ctx->state = kPlanned;
   ctx->cur_layer = layer;
   ctx->cur_T = T;
@@ -469,7 +563,10 @@ extern "C" moe_status moe_expert_ffn(moe_ctx* ctx, int32_t layer, const void* x,
   CHECK_CTX(ctx);
   if (!x || ctx->state != kPlanned || layer != ctx->cur_layer || T != ctx->cur_T)
     return fail(ctx, MOE_EINVAL, "moe_expert_ffn: must follow moe_cache_plan of the same layer and T");
+  if ((uintptr_t)x & 15) return fail(ctx, MOE_EINVAL, "moe_expert_ffn: x must be 16-byte aligned");
+  MOE_HIP(ctx, timing_begin(ctx, MOE_T_FFN, (hipStream_t)stream));
   MOE_HIP(ctx, launch_ffn(ctx, x, T, (hipStream_t)stream));
+  MOE_HIP(ctx, timing_end(ctx, (hipStream_t)stream));
   ctx->state = kEvaluated;
   return MOE_OK;
 }
@@ -480,8 +577,9 @@ extern "C" moe_status moe_merge(moe_ctx* ctx, const float* w, int32_t T, void* y
   if (!w || !y || ctx->state != kEvaluated || T != ctx->cur_T)
     return fail(ctx, MOE_EINVAL, "moe_merge: must follow moe_expert_ffn with the same T");
   hipStream_t s = (hipStream_t)stream;
-  MOE_HIP(ctx, hipStreamWaitEvent(s, ctx->ev_cpu, 0));
-  MOE_HIP(ctx, launch_merge(ctx, w, T, y, s));
+  MOE_HIP(ctx, timing_begin(ctx, MOE_T_MERGE, s));
+  MOE_HIP(ctx, launch_merge(ctx, w, T, y, ctx->call_seq, s));
+  MOE_HIP(ctx, timing_end(ctx, s));
   ctx->state = kIdle;
   return MOE_OK;
 }
@@ -532,8 +630,8 @@ static moe_status drain(moe_ctx* ctx, int32_t timeout_ms) {
     return hip_fail(ctx, e, "hipEventRecord");
   }
   for (;;) {
-    bool done = hipEventQuery(ev) == hipSuccess && hipStreamQuery(ctx->side) == hipSuccess &&
-                hipStreamQuery(ctx->copy) == hipSuccess;
+    bool done = hipEventQuery(ev) == hipSuccess && hipStreamQuery(ctx->copy) == hipSuccess &&
+                host_branch_idle(ctx);
     if (done) break;
     double ms = std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t0).count();
     if (timeout_ms >= 0 && ms > timeout_ms) {
@@ -636,9 +734,11 @@ static moe_status prefill_issue(moe_ctx* ctx, int32_t layer) {
   int b = layer % 2;
   const int E = ctx->cfg.n_experts;
   MOE_HIP(ctx, hipStreamWaitEvent(ctx->copy, pf.ev_start, 0));
+  MOE_HIP(ctx, timing_begin(ctx, MOE_T_PREFILL_COPY, ctx->copy));
   MOE_HIP(ctx, hipMemcpyAsync(ctx->pool.base + (size_t)b * E * ctx->stride,
                               ctx->host_pool + (size_t)layer * E * ctx->stride, (size_t)E * ctx->stride,
                               hipMemcpyHostToDevice, ctx->copy));
+  MOE_HIP(ctx, timing_end(ctx, ctx->copy));
   MOE_HIP(ctx, hipEventRecord(pf.ev_copied[b], ctx->copy));
   pf.buf_layer[b] = layer;
   pf.admitted[b] = false;
@@ -687,6 +787,8 @@ extern "C" moe_status moe_prefill_layer(moe_ctx* ctx, int32_t layer, const void*
     MOE_HIP(ctx, launch_prefill_admit(ctx, layer, s));
     pf.admitted[b] = true;
   }
+  MOE_HIP(ctx, timing_begin(ctx, MOE_T_PREFILL_GEMM, s));
   MOE_HIP(ctx, launch_prefill_compute(ctx, layer, x, T, ids, w, y, s));
+  MOE_HIP(ctx, timing_end(ctx, s));
   return MOE_OK;
 }

@@ -381,19 +381,43 @@ hipError_t launch_ffn(moe_ctx* ctx, const void* x, int T, hipStream_t s) {
 // y[t] = sum over ascending j of w[t][j] * P[t][j], P from the GPU rows or the
 // host rows by the sign of slot_map (snackonai, "What It Actually Does";
 // satyajit, "Decode: the one equation").  fp32, one rounding to the output.
+// A token with host pairs first waits for the host branch to publish this
+// call's sequence number (bounded: after wait_ticks it flags an error).
 template <int AT>
 __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ w,
                                                     const int32_t* __restrict__ slot_map,
                                                     const float* __restrict__ pg,
-                                                    const float* __restrict__ pc, int k, int H,
-                                                    void* __restrict__ y) {
+                                                    const float* pc, int k, int H,
+                                                    void* __restrict__ y, HostSync* sync,
+                                                    int64_t seq, uint64_t wait_ticks) {
+  __shared__ int s_ok;
   const int t = blockIdx.y;
+  bool host = false;
+  for (int j = 0; j < k; ++j) host |= slot_map[t * k + j] < 0;
+  if (host) {
+    if (threadIdx.x == 0) {
+      const uint64_t t0 = wall_clock64();
+      int ok = 1;
+      while (__hip_atomic_load(&sync->done, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_SYSTEM) < seq) {
+        if (wall_clock64() - t0 > wait_ticks) {
+          __hip_atomic_store(&sync->error, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+          ok = 0;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+      }
+      s_ok = ok;
+    }
+    __syncthreads();
+  }
   const int h = blockIdx.x * blockDim.x + threadIdx.x;
   if (h >= H) return;
   float acc = 0.f;
   for (int j = 0; j < k; ++j) {
     const int p = t * k + j;
-    const float v = slot_map[p] >= 0 ? pg[(size_t)p * H + h] : pc[(size_t)p * H + h];
+    float v;
+    if (slot_map[p] >= 0) v = pg[(size_t)p * H + h];
+    else v = __hip_atomic_load(pc + (size_t)p * H + h, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     acc = fmaf(w[p], v, acc);
   }
   if constexpr (AT == MOE_F32) {
@@ -405,15 +429,15 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ w,
   }
 }
 
-hipError_t launch_merge(moe_ctx* ctx, const float* w, int T, void* y, hipStream_t s) {
+hipError_t launch_merge(moe_ctx* ctx, const float* w, int T, void* y, int64_t seq, hipStream_t s) {
   const int H = ctx->cfg.hidden;
   dim3 grid((H + 255) / 256, T), block(256);
   if (ctx->cfg.act_dtype == MOE_F32)
     hipLaunchKernelGGL(merge_kernel<MOE_F32>, grid, block, 0, s, w, ctx->plan.slot_map, ctx->p_gpu,
-                       ctx->p_cpu_dev, ctx->cfg.top_k, H, y);
+                       ctx->p_cpu_dev, ctx->cfg.top_k, H, y, ctx->sync_dev, seq, ctx->wait_ticks);
   else
     hipLaunchKernelGGL(merge_kernel<MOE_BF16>, grid, block, 0, s, w, ctx->plan.slot_map, ctx->p_gpu,
-                       ctx->p_cpu_dev, ctx->cfg.top_k, H, y);
+                       ctx->p_cpu_dev, ctx->cfg.top_k, H, y, ctx->sync_dev, seq, ctx->wait_ticks);
   return hipGetLastError();
 }
 

@@ -29,11 +29,22 @@ struct DevState {
   int32_t pad;
 };
 
-// Everything the host branch needs from one plan, packed so a single
-// device-to-host copy moves it.  Written by the control kernel.
+// Everything the host branch needs from one plan, in pinned host memory the
+// control kernel writes directly.  `seq` is the doorbell: the kernel writes
+// it last (after a system-scope fence), and only when the call has host work.
 struct HostBlockHeader {
+  int64_t seq;
   moe_plan_counts c;
   int32_t layer, T;
+};
+
+// Completion word of the host branch (pinned, mapped): the poller publishes
+// the doorbell value it finished; the merge kernel waits for it; a merge that
+// gives up after its time limit sets `error`.
+struct HostSync {
+  int64_t done;
+  int32_t error;
+  int32_t pad[13];
 };
 
 // Fixed-shape plan outputs in device memory (one allocation).
@@ -41,9 +52,12 @@ struct PlanBufs {
   moe_plan_counts* counts;
   int32_t *uniq, *hits, *misses, *victims, *fill_u, *fill_slot, *fill_old;
   int32_t *cpu_u, *gpu_u, *gpu_slot, *slot_map;
-  // host block mirror: header | ids[maxTk] | slot_map[maxTk]
-  uint8_t* hblock;
-  size_t hblock_bytes;
+  // host block in pinned, device-mapped memory, written by the control kernel:
+  // header | ids[maxTk] | slot_map[maxTk] | x[max_tokens][H] (act dtype)
+  uint8_t* hblock;        // device address of the mapping
+  size_t hblock_bytes;    // header + ids + slot map
+  size_t x_offset;        // byte offset of the activations copy
+  int act_bytes;          // bytes per activation element
 };
 
 // One physical chunk of the slot pool mapped into the reserved range.
@@ -61,14 +75,21 @@ struct SlotPool {
   std::vector<PoolChunk> chunks;
 };
 
-struct CpuPool;  // host worker pool (cpu_branch.cpp)
-
-// Work description handed to the host branch callback.
-struct CpuJob {
-  moe_ctx* ctx;
-};
+struct CpuPool;     // host worker pool (cpu_branch.cpp)
+struct HostBranch;  // doorbell poller (cpu_branch.cpp)
 
 enum CallState { kIdle = 0, kPlanned = 1, kEvaluated = 2 };
+
+// Ring of event pairs bracketing launched phases (timing mode only).
+struct Timing {
+  static constexpr int kRing = 2048;
+  std::vector<hipEvent_t> a, b;
+  std::vector<int> phase;
+  int head = 0, used = 0;
+  int64_t calls[MOE_T_COUNT] = {};
+  double ms[MOE_T_COUNT] = {};
+  std::atomic<int64_t> host_ns{0}, host_calls{0};
+};
 
 }  // namespace moert
 
@@ -105,17 +126,20 @@ struct moe_ctx {
   const float* p_cpu_dev = nullptr;
   float* h_mid = nullptr;      // device [max_tokens*k][I]
 
-  // host staging for the host branch (pinned)
-  uint8_t* hstage = nullptr;   // plan host block copy
-  uint8_t* xstage = nullptr;   // x copy [max_tokens][H] act dtype
+  // host block (pinned, mapped): the control kernel writes it, the host branch reads it
+  uint8_t* hstage = nullptr;   // host address
+  uint8_t* xstage = nullptr;   // host address of its activations copy
 
-  // streams and events owned by the context
-  hipStream_t side = nullptr;  // host branch
+  // host branch hand-off
+  moert::HostSync* sync = nullptr;        // host address
+  moert::HostSync* sync_dev = nullptr;    // device address
+  int64_t call_seq = 0;                   // doorbell value of the current call
+  uint64_t wait_ticks = 0;                // merge's wait limit in wall-clock ticks
+
   hipStream_t copy = nullptr;  // prefill transfers
-  hipEvent_t ev_plan = nullptr, ev_cpu = nullptr;
 
   moert::CpuPool* cpu = nullptr;
-  moert::CpuJob job{};
+  moert::HostBranch* hb = nullptr;
 
   // decode call order
   int state = moert::kIdle;
@@ -139,6 +163,8 @@ struct moe_ctx {
     int32_t max_tiles = 0;
   } pf;
 
+  moert::Timing* timing = nullptr;
+
   moe_status err = MOE_OK;     // latched HIP error
   std::string err_msg;
 };
@@ -161,21 +187,28 @@ inline int dtype_bytes(int d) { return d == MOE_F32 ? 4 : 2; }
 // kernel launchers (defined in the .hip files) -------------------------------
 hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w,
                              hipStream_t s);
-hipError_t launch_plan(moe_ctx* ctx, int layer, const int32_t* ids, int T, hipStream_t s);
+hipError_t launch_plan(moe_ctx* ctx, int layer, const int32_t* ids, int T, const void* x,
+                       int64_t seq, hipStream_t s);
 hipError_t launch_fill(moe_ctx* ctx, hipStream_t s);
 hipError_t launch_ffn(moe_ctx* ctx, const void* x, int T, hipStream_t s);
-hipError_t launch_merge(moe_ctx* ctx, const float* w, int T, void* y, hipStream_t s);
+hipError_t launch_merge(moe_ctx* ctx, const float* w, int T, void* y, int64_t seq, hipStream_t s);
 hipError_t launch_prefill_admit(moe_ctx* ctx, int layer, hipStream_t s);
 hipError_t launch_prefill_compute(moe_ctx* ctx, int layer, const void* x, int T,
                                   const int32_t* ids, const float* w, void* y, hipStream_t s);
 hipError_t launch_table_reset(moe_ctx* ctx, hipStream_t s);
 moe_status prefill_settle(moe_ctx* ctx, hipStream_t s);
 
+// timing mode: bracket a launch; no-ops when timing is off
+hipError_t timing_begin(moe_ctx* ctx, int phase, hipStream_t s);
+hipError_t timing_end(moe_ctx* ctx, hipStream_t s);
+
 // host branch -----------------------------------------------------------------
 CpuPool* cpu_pool_create(int threads);
 void cpu_pool_destroy(CpuPool* p);
-// Runs on the HIP host-function thread: evaluates the CPU-assigned experts of
-// the staged plan into ctx->p_cpu.
-void cpu_branch_run(moe_ctx* ctx);
+// Start / stop the doorbell poller of a context (worker 0 of its pool).
+bool host_branch_start(moe_ctx* ctx);
+void host_branch_stop(moe_ctx* ctx);
+// True when every rung doorbell has been answered.
+bool host_branch_idle(moe_ctx* ctx);
 
 }  // namespace moert

@@ -24,7 +24,10 @@ constexpr int kWaves = kPlanThreads / 64;
 constexpr uint32_t kSentinel = 0xFFFFFFFFu;
 
 struct PlanArgs {
+  int64_t seq;          // doorbell value of this call
   const int32_t* ids;
+  const uint8_t* x;     // activations [T][H], act dtype
+  int64_t x_bytes;      // T * H * element bytes
   int32_t T, k, layer, E, K, n, mode, max_fetch;
   int64_t bwp, bwh;
   int32_t* id2slot;
@@ -68,7 +71,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   __shared__ int32_t s_scan2[kPlanThreads];
   __shared__ uint64_t s_sel[kMaxExperts];
   __shared__ int64_t s_tick;
-  __shared__ int32_t s_nuniq, s_nhit, s_m, s_q, s_keff, s_evict, s_ngpu;
+  __shared__ int32_t s_nuniq, s_nhit, s_m, s_q, s_keff, s_evict, s_ngpu, s_bad;
   __shared__ uint32_t s_prefix, s_pmask, s_kk;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -82,6 +85,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   if (tid == 0) {
     s_tick = a.st->tick + 1;
     s_evict = 0;
+    s_bad = 0;
   }
   __syncthreads();
   const int64_t tick = s_tick;
@@ -90,6 +94,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   for (int i = tid; i < Tk; i += kPlanThreads) {
     int e = a.ids[i];
     if (e >= 0 && e < E) atomicOr(&s_mask[e >> 5], 1u << (e & 31));
+    else atomicAdd(&s_bad, 1);  // out-of-range ids: zero rows from the host branch
   }
   __syncthreads();
 
@@ -294,6 +299,9 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   __syncthreads();
 
   // slot map (device and host block); GPU list in ascending u
+  // slot map; when the call has host work, the host block in pinned host
+  // memory gets ids, slot map and a copy of the activations
+  const int n_cpu = mm - q + (s_bad > 0);  // > 0: the host branch has work
   HostBlockHeader* hb = (HostBlockHeader*)pb.hblock;
   int32_t* hb_ids = (int32_t*)(pb.hblock + sizeof(HostBlockHeader));
   int32_t* hb_map = hb_ids + Tk;
@@ -301,8 +309,15 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     int ee = a.ids[i];
     int sl = (ee >= 0 && ee < E) ? s_eslot[ee] : -1;
     pb.slot_map[i] = sl;
-    hb_ids[i] = ee;
-    hb_map[i] = sl;
+    if (n_cpu > 0) {
+      hb_ids[i] = ee;
+      hb_map[i] = sl;
+    }
+  }
+  if (n_cpu > 0) {
+    const uint4* xs = (const uint4*)a.x;
+    uint4* xd = (uint4*)(pb.hblock + pb.x_offset);
+    for (int64_t i = tid; i < a.x_bytes / 16; i += kPlanThreads) xd[i] = xs[i];
   }
   const bool on_gpu = present && s_eslot[e] >= 0;
   const uint64_t b_gpu = __ballot(on_gpu);
@@ -315,6 +330,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     pb.gpu_u[p] = u;
     pb.gpu_slot[p] = s_eslot[e];
   }
+  __threadfence_system();  // host block writes visible before the doorbell
+  __syncthreads();
   if (tid == 0) {
     moe_plan_counts c;
     c.n_uniq = s_nuniq;
@@ -326,9 +343,14 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     c.K = a.K;
     c.tick_lo = (int32_t)tick;
     *pb.counts = c;
-    hb->c = c;
-    hb->layer = a.layer;
-    hb->T = a.T;
+    if (n_cpu > 0) {
+      hb->c = c;
+      hb->layer = a.layer;
+      hb->T = a.T;
+      __threadfence_system();
+      *(volatile int64_t*)&hb->seq = a.seq;  // ring the host branch
+      __threadfence_system();
+    }
     DevState* st = a.st;
     st->tick = tick;
     st->plans += 1;
@@ -339,9 +361,13 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   }
 }
 
-hipError_t launch_plan(moe_ctx* ctx, int layer, const int32_t* ids, int T, hipStream_t s) {
+hipError_t launch_plan(moe_ctx* ctx, int layer, const int32_t* ids, int T, const void* x,
+                       int64_t seq, hipStream_t s) {
   PlanArgs a;
+  a.seq = seq;
   a.ids = ids;
+  a.x = (const uint8_t*)x;
+  a.x_bytes = (int64_t)T * ctx->cfg.hidden * ctx->plan.act_bytes;
   a.T = T;
   a.k = ctx->cfg.top_k;
   a.layer = layer;

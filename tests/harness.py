@@ -208,5 +208,20 @@ def compare_plan(gp: dict, op, T):
 
 
 def rel_err(y_gpu, y_ref):
-    rms = float(np.sqrt(np.mean(y_ref ** 2)))
-    return float(np.max(np.abs(y_gpu - y_ref))) / max(rms, 1e-300), rms
+    """max |y_gpu - y_ref| / RMS(y_ref), per token row (each row is one
+    stream's MoE-layer output), maximised over rows."""
+    y_gpu = np.atleast_2d(y_gpu)
+    y_ref = np.atleast_2d(y_ref)
+    rms = np.sqrt(np.mean(y_ref ** 2, axis=1))
+    err = np.max(np.abs(y_gpu - y_ref), axis=1) / np.maximum(rms, 1e-300)
+    return float(err.max()), float(rms.min())
+
+
+def bf16_round_err(y_ref):
+    """The part of rel_err that rounding the exact output to bfloat16 alone
+    already causes (round-to-nearest-even on the fp64 -> fp32 value)."""
+    y32 = np.atleast_2d(y_ref).astype(np.float32)
+    u = y32.view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
+    yb = u.astype(np.uint32).view(np.float32).astype(np.float64)
+    return rel_err(yb, y_ref)[0]

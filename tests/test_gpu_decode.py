@@ -1,0 +1,136 @@
+"""GPU parity of the decode path at the real expert shapes.
+
+Mid-size cases use the Qwen-shaped bf16 and DeepSeek-shaped MXFP4 experts
+with fewer layers and steps (every plan, table and output checked).  Full
+cases run the stated workloads end to end: every plan and table bit-exact on
+every call; outputs compared with the fp64 oracle on sampled calls (the
+oracle's dequantised fp64 expert evaluation is the slow part).
+Tolerance for bf16 / MXFP4: max |y - y_oracle| <= 2e-2 x RMS(y_oracle)."""
+import dataclasses
+
+import numpy as np
+import pytest
+
+import workload as W
+from tests.harness import (GpuRun, OracleRun, bf16_round_err, compare_plan, log, rel_err,
+                           x_f64)
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 2e-2, "mxfp4": 2e-2}
+
+
+def run_decode(wl, mode=0, check_output=lambda s, l: True, check_fill=lambda s, l: False,
+               resize=None, n_slots=None, max_fetch=0):
+    resize = wl.resize if resize is None else resize
+    g = GpuRun(wl, mode=mode, n_slots=n_slots, max_fetch=max_fetch)
+    try:
+        o = OracleRun(wl, g.bank, mode=mode, n_slots=n_slots, max_fetch=max_fetch)
+        logits = W.router_logits(wl)
+        worst, worst_round, checked, stats = 0.0, 0.0, 0, dict(hit=0, q=0, cpu=0)
+        for s in range(wl.steps):
+            if s in resize:
+                g.B.moe_cache_resize(g.ctx, resize[s], 60_000)
+                o.resize(resize[s])
+                i2s, s2i, ts, tick = g.tables()
+                assert i2s == o.st.id2slot and s2i == o.st.slot2id and ts == o.st.slot_ts, s
+                log(f"  resized to {resize[s]} before step {s}")
+            for l in range(wl.L):
+                x = W.hidden(wl, s, l)
+                ids_g, w_g = g.decode_call(l, logits[s, l], x)
+                ids_o, w_o = o.route(logits[s, l])
+                assert np.array_equal(ids_g, ids_o), (s, l)
+                assert np.allclose(w_g, w_o, rtol=2e-6, atol=1e-7)
+                op = o.plan(l, ids_o)
+                gp = g.plan_view(wl.T)
+                compare_plan(gp, op, wl.T)
+                stats["hit"] += len(op.hits)
+                stats["q"] += op.q
+                stats["cpu"] += len(op.cpu)
+                if check_fill(s, l):
+                    for (u, sl, old) in op.fills:
+                        assert np.array_equal(g.slot_bytes(sl), g.bank(u)), (s, l, u, sl)
+                if check_output(s, l):
+                    y_ref = o.output(l, x_f64(wl, x), ids_o, w_o)
+                    err, rms = rel_err(g.y_f64(), y_ref)
+                    if err > worst:
+                        worst = err
+                        worst_round = bf16_round_err(y_ref) if wl.act_dtype == "bf16" else 0.0
+                    checked += 1
+                    assert err <= TOL[wl.w_dtype], (s, l, err)
+            if s % 32 == 0 or s == wl.steps - 1:
+                i2s, s2i, ts, tick = g.tables()
+                assert i2s == o.st.id2slot and s2i == o.st.slot2id, s
+                assert ts == o.st.slot_ts and tick == o.st.tick, s
+                log(f"  step {s}: worst rel err {worst:.3e} (bf16 output rounding alone: "
+                    f"{worst_round:.3e}) over {checked} outputs; {stats}")
+        st = g.B.moe_ctx_stats(g.ctx)
+        assert st.hits == stats["hit"] and st.fills == stats["q"] and st.cpu == stats["cpu"]
+        return worst, checked, stats
+    finally:
+        g.close()
+
+
+def mini(wl, **kw):
+    return dataclasses.replace(wl, **kw)
+
+
+@pytest.mark.parametrize("mode", [0, 1, 2])
+def test_bf16_mini_every_call(mode):
+    wl = mini(W.QWEN_BF16, L=4, steps=20, n_slots=189)
+    log(f"bf16 mini mode={mode}")
+    worst, n, st = run_decode(wl, mode=mode, check_fill=lambda s, l: True)
+    log(f"bf16 mini mode={mode}: worst {worst:.3e} over {n} outputs {st}")
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+def test_mxfp4_mini_every_call(mode):
+    wl = mini(W.DSV4_MXFP4, L=2, steps=12, n_slots=56)
+    log(f"mxfp4 mini mode={mode}")
+    worst, n, st = run_decode(wl, mode=mode, check_fill=lambda s, l: True)
+    log(f"mxfp4 mini mode={mode}: worst {worst:.3e} over {n} outputs {st}")
+
+
+def test_bf16_streams_mini_with_resizes():
+    wl = mini(W.QWEN_ELASTIC, L=3, steps=24, n_slots=141, resize={6: 57, 12: 115, 18: 115})
+    log("bf16 8-stream mini")
+    worst, n, st = run_decode(wl, check_fill=lambda s, l: True)
+    log(f"bf16 8-stream mini: worst {worst:.3e} over {n} outputs {st}")
+
+
+def test_tiny_pool_and_max_fetch_edges():
+    # empty pool: everything on the host; then a fetch cap of 1
+    wl = mini(W.QWEN_BF16, L=2, steps=6, n_slots=0)
+    run_decode(wl, n_slots=0)
+    wl = mini(W.QWEN_BF16, L=2, steps=6, n_slots=40)
+    run_decode(wl, n_slots=40, max_fetch=1, mode=1)
+
+
+# ------------------------------------------------------------------ full workloads
+@pytest.mark.timeout(900)
+def test_qwen_bf16_full():
+    wl = W.QWEN_BF16
+    log("qwen bf16 full: 48 layers x 256 steps, n=2273")
+    worst, n, st = run_decode(
+        wl, check_output=lambda s, l: (s % 16 == 0 and l < 4) or s == wl.steps - 1,
+        check_fill=lambda s, l: s % 64 == 1)
+    log(f"qwen bf16 full: worst {worst:.3e} over {n} outputs {st}")
+
+
+@pytest.mark.timeout(900)
+def test_dsv4_mxfp4_full():
+    wl = W.DSV4_MXFP4
+    log("dsv4 mxfp4 full: 8 layers x 128 steps, n=225")
+    worst, n, st = run_decode(
+        wl, check_output=lambda s, l: s % 16 == 0 or s == wl.steps - 1,
+        check_fill=lambda s, l: s % 32 == 1)
+    log(f"dsv4 mxfp4 full: worst {worst:.3e} over {n} outputs {st}")
+
+
+@pytest.mark.timeout(1200)
+def test_qwen_elastic_full():
+    wl = W.QWEN_ELASTIC
+    log("qwen elastic 8 streams full: 48 layers x 512 steps, resizes " + str(wl.resize))
+    worst, n, st = run_decode(
+        wl, check_output=lambda s, l: (s % 64 == 0 and l < 2) or s in (127, 128, 255, 256, 383, 384, 511) and l < 2)
+    log(f"qwen elastic full: worst {worst:.3e} over {n} outputs {st}")
