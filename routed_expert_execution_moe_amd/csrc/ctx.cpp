@@ -714,7 +714,9 @@ static moe_status prefill_setup(moe_ctx* ctx) {
   const moe_config& c = ctx->cfg;
   const size_t Tk = (size_t)c.max_prefill_tokens * c.top_k;
   MOE_HIP(ctx, hipMalloc((void**)&pf.counts, 4 * (size_t)c.n_experts));
-  MOE_HIP(ctx, hipMalloc((void**)&pf.offsets, 4 * (size_t)(c.n_experts + 1)));
+  MOE_HIP(ctx, hipMalloc((void**)&pf.offsets, 4 * (size_t)(c.n_experts + 2)));
+  pf.max_tiles = (int32_t)(Tk / 128 + c.n_experts);
+  MOE_HIP(ctx, hipMalloc((void**)&pf.tiles, 4 * (size_t)pf.max_tiles));
   MOE_HIP(ctx, hipMalloc((void**)&pf.cursor, 4 * (size_t)c.n_experts));
   MOE_HIP(ctx, hipMalloc((void**)&pf.perm, 4 * Tk));
   MOE_HIP(ctx, hipMalloc((void**)&pf.hmid, 2 * Tk * c.inter));
@@ -769,6 +771,12 @@ extern "C" moe_status moe_prefill_layer(moe_ctx* ctx, int32_t layer, const void*
   if (!x || !ids || !w || !y || layer < 0 || layer >= c.n_layers || T < 1 || T > c.max_prefill_tokens)
     return fail(ctx, MOE_EINVAL, "moe_prefill_layer: bad arguments");
   if (ctx->state != kIdle) return fail(ctx, MOE_EINVAL, "moe_prefill_layer: a decode layer call is open");
+  if (c.w_dtype != MOE_MXFP4 || c.act_dtype != MOE_BF16 || c.hidden % 256 || c.inter % 128)
+    return fail(ctx, MOE_EUNSUPPORTED,
+                "moe_prefill_layer: the grouped GEMM takes MXFP4 experts, bf16 activations, "
+                "hidden % 256 == 0 and inter % 128 == 0");
+  if (((uintptr_t)x & 15) || ((uintptr_t)ids & 3) || ((uintptr_t)w & 3) || ((uintptr_t)y & 3))
+    return fail(ctx, MOE_EINVAL, "moe_prefill_layer: x must be 16-byte aligned");
   if (ctx->n_slots < 2 * c.n_experts)
     return fail(ctx, MOE_ENOSPC, "moe_prefill_layer: two full-layer buffers do not fit in the slot pool");
   moe_status st = prefill_setup(ctx);

@@ -1,11 +1,381 @@
-// Prefill compute: grouped expert GEMM over a full-layer buffer (in progress).
+// Prefill compute for one chunk of T tokens of one MoE layer whose E experts
+// sit in the full-layer buffer b = layer % 2, slots [b*E, (b+1)*E)
+// (satyajit, "Prefill: hide the pool behind the wire").
+//
+//   1. group    per-expert counts of the T*k routed pairs, offsets, the list
+//               of 128-row M-tiles, and the permutation pos -> pair (pairs of
+//               an expert contiguous; order inside an expert is not
+//               significant: every output row is computed independently with
+//               the same arithmetic);
+//   2. GEMM1    per expert, gathered token rows x [n_e, H] times the gate and
+//               up matrices [I, H] (MXFP4, dequantised to bf16 in registers)
+//               with bf16 MFMA and fp32 accumulation; epilogue
+//               h = silu(g) * u rounded to bf16, rows in pos order;
+//   3. GEMM2    h [n_e, I] times the down matrix [H, I] -> fp32 rows per pair;
+//   4. merge    y[t] = sum over ascending j of w[t][j] * P[t*k + j], fp32,
+//               one rounding to the output dtype.
+// Everything is deterministic: no atomics touch outputs.
+//
+// GEMM tiling (gfx950, v_mfma_f32_32x32x16_bf16): a workgroup of 4 waves owns
+// a 128-row M-tile of one expert and a 256-column N-tile, the waves in a 2x2
+// grid of 64 x 128 wave tiles (2 x 4 MFMA tiles); K steps of 64 staged in LDS
+// with the 16-byte chunks of each row XOR-swizzled by (row % 8), and the next
+// K step prefetched into registers while the MFMAs run.  For GEMM1 the 256
+// B-tile rows are 128 gate rows then the matching 128 up rows, so a wave's
+// gate and up accumulators share lanes and the SiLU * up epilogue needs no
+// exchange.  Workgroups are mapped so that the N-tiles of one M-tile run on
+// the same XCD (shared A rows in that XCD's L2).
 #include "internal.h"
 
 namespace moert {
 
-hipError_t launch_prefill_compute(moe_ctx*, int, const void*, int, const int32_t*, const float*,
-                                  void*, hipStream_t) {
-  return hipErrorNotSupported;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kBM = 128, kBN = 256, kBK = 64;
+constexpr int kGemmThreads = 256;
+constexpr int kRowBytes = kBK * 2;  // one LDS row: 64 bf16
+
+// ------------------------------------------------------------------ grouping
+__global__ void group_zero_kernel(int32_t* counts, int32_t* cursor, int E) {
+  int e = blockIdx.x * blockDim.x + threadIdx.x;
+  if (e < E) {
+    counts[e] = 0;
+    cursor[e] = 0;
+  }
+}
+
+__global__ __launch_bounds__(256) void group_hist_kernel(const int32_t* __restrict__ ids, int Tk, int E,
+                                                         int32_t* counts) {
+  __shared__ int32_t h[kMaxExperts];
+  for (int e = threadIdx.x; e < E; e += blockDim.x) h[e] = 0;
+  __syncthreads();
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < Tk; i += gridDim.x * blockDim.x) {
+    int e = ids[i];
+    if (e >= 0 && e < E) atomicAdd(&h[e], 1);
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += blockDim.x)
+    if (h[e]) atomicAdd(&counts[e], h[e]);
+}
+
+// offsets[E+1]; M-tile list tiles[i] = (e << 20) | m0/kBM; tiles_n written to
+// offsets[E+1].
+__global__ __launch_bounds__(1024) void group_scan_kernel(const int32_t* counts, int E,
+                                                          int32_t* offsets, int32_t* tiles) {
+  __shared__ int32_t s_off[kMaxExperts + 1];
+  __shared__ int32_t s_toff[kMaxExperts + 1];
+  if (threadIdx.x == 0) {
+    int o = 0, t = 0;
+    for (int e = 0; e < E; ++e) {
+      s_off[e] = o;
+      s_toff[e] = t;
+      o += counts[e];
+      t += (counts[e] + kBM - 1) / kBM;
+    }
+    s_off[E] = o;
+    s_toff[E] = t;
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e <= E; e += blockDim.x) offsets[e] = s_off[e];
+  if (threadIdx.x == 0) offsets[E + 1] = s_toff[E];
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    const int nt = (counts[e] + kBM - 1) / kBM;
+    for (int m = 0; m < nt; ++m) tiles[s_toff[e] + m] = (e << 20) | m;
+  }
+}
+
+__global__ __launch_bounds__(256) void group_scatter_kernel(const int32_t* __restrict__ ids, int Tk,
+                                                            int E, const int32_t* offsets,
+                                                            int32_t* cursor, int32_t* perm) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < Tk; i += gridDim.x * blockDim.x) {
+    int e = ids[i];
+    if (e >= 0 && e < E) perm[offsets[e] + atomicAdd(&cursor[e], 1)] = i;
+  }
+}
+
+// ------------------------------------------------------------------ MXFP4 -> bf16
+__device__ inline uint32_t e2m1_bits(uint32_t c) {
+  const uint32_t m = c & 7u;
+  uint32_t bits = m >= 2u ? ((((m >> 1) + 126u) << 23) | ((m & 1u) << 22)) : (m ? 0x3F000000u : 0u);
+  return bits | ((c & 8u) << 28);
+}
+
+// 16 code bytes (32 elements) with one E8M0 scale -> 32 bf16 in 4 x 16 bytes.
+// e2m1 * 2^(s-127) is exact in bf16 (2 significant bits, fp32 exponent range).
+__device__ inline void dequant32(uint4 codes, uint32_t s, uint4 out[4]) {
+  const float sc = s ? __uint_as_float(s << 23) : __uint_as_float(0x00400000u);
+  const uint32_t w[4] = {codes.x, codes.y, codes.z, codes.w};
+  uint32_t o[16];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const uint32_t byte = (w[i] >> (8 * b)) & 0xFFu;
+      const uint32_t lo = __float_as_uint(__uint_as_float(e2m1_bits(byte & 15u)) * sc) >> 16;
+      const uint32_t hi = __float_as_uint(__uint_as_float(e2m1_bits(byte >> 4)) * sc) >> 16;
+      o[4 * i + b] = lo | (hi << 16);
+    }
+  }
+  out[0] = make_uint4(o[0], o[1], o[2], o[3]);
+  out[1] = make_uint4(o[4], o[5], o[6], o[7]);
+  out[2] = make_uint4(o[8], o[9], o[10], o[11]);
+  out[3] = make_uint4(o[12], o[13], o[14], o[15]);
+}
+
+__device__ inline int swz(int row, int chunk) { return row * kRowBytes + ((chunk ^ (row & 7)) << 4); }
+
+struct GemmArgs {
+  const uint8_t* slot_base;   // slot s at slot_base + s * stride
+  size_t stride;
+  int slot0;                  // b * E
+  int E, k;
+  int K;                      // contraction: H (GEMM1) or I (GEMM2)
+  int N;                      // output columns per matrix: I (GEMM1) or H (GEMM2)
+  size_t off0, off1;          // code offsets of matrix 0 (gate / down) and 1 (up)
+  size_t soff0, soff1;        // scale offsets
+  const int32_t* offsets;     // [E+2]
+  const int32_t* tiles;       // M-tile list
+  const int32_t* perm;        // pos -> pair
+  const uint16_t* a_src;      // GEMM1: x [T][H] (rows by token); GEMM2: h [Tk][I] by pos
+  uint16_t* h_out;            // GEMM1 output [Tk][I] by pos
+  float* p_out;               // GEMM2 output [Tk][H] by pair
+  int n_ntiles;               // N-tiles per M-tile
+  int max_mtiles;             // grid bound on M-tiles
+};
+
+template <bool GLU>
+__global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_kernel(GemmArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t s_a[kBM * kRowBytes];   // 16 KB
+  __shared__ __attribute__((aligned(16))) uint8_t s_b[kBN * kRowBytes];   // 32 KB
+  __shared__ int32_t s_rowsrc[kBM];  // A source row per tile row, -1 = padding
+
+  // XCD-aware mapping: consecutive workgroups go round-robin over 8 XCDs;
+  // give every N-tile of one M-tile to the same XCD.
+  const int bid = blockIdx.x;
+  const int xcd = bid & 7, local = bid >> 3;
+  const int mt = (local / a.n_ntiles) * 8 + xcd;
+  const int nt = local % a.n_ntiles;
+  const int n_mtiles = a.offsets[a.E + 1];
+  if (mt >= n_mtiles) return;
+  const int tile = a.tiles[mt];
+  const int e = tile >> 20, m0 = (tile & 0xFFFFF) * kBM;
+  const int pos0 = a.offsets[e] + m0;
+  const int rows = min(kBM, a.offsets[e + 1] - pos0);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  if (tid < kBM) {
+    int src = -1;
+    if (tid < rows) src = GLU ? a.perm[pos0 + tid] / a.k : pos0 + tid;
+    s_rowsrc[tid] = src;
+  }
+  __syncthreads();
+
+  const uint8_t* slot = a.slot_base + (size_t)(a.slot0 + e) * a.stride;
+  // B tile rows: GLU -> gate rows n0..n0+127 then up rows n0..n0+127 (n0 = nt*128);
+  // down -> rows n0..n0+255 (n0 = nt*256)
+  const int n0 = GLU ? nt * (kBN / 2) : nt * kBN;
+  const int K = a.K;
+  const int nk = K / kBK;
+
+  // per-thread load assignments
+  // A: 128 rows x 8 chunks = 1024 chunks, 4 per thread: rows tid/8 + 32*i, chunk tid%8
+  const int a_chunk = tid & 7;
+  // B: 256 rows x 2 halves (32 elements each): row tid, halves 0 and 1
+  const int b_row = tid;
+  const uint8_t* b_codes;
+  const uint8_t* b_scales;
+  {
+    int mrow;
+    size_t coff, soff;
+    if (GLU) {
+      const bool up = b_row >= kBN / 2;
+      mrow = n0 + (up ? b_row - kBN / 2 : b_row);
+      coff = up ? a.off1 : a.off0;
+      soff = up ? a.soff1 : a.soff0;
+    } else {
+      mrow = n0 + b_row;
+      coff = a.off0;
+      soff = a.soff0;
+    }
+    b_codes = slot + coff + (size_t)mrow * (K / 2);
+    b_scales = slot + soff + (size_t)mrow * (K / 32);
+  }
+
+  uint4 pa[4];
+  uint4 pb[2];
+  uint32_t ps[2];
+  auto load_k = [&](int kt) {
+    const int k0 = kt * kBK;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = (tid >> 3) + 32 * i;
+      const int src = s_rowsrc[r];
+      if (src >= 0)
+        pa[i] = *(const uint4*)(a.a_src + (size_t)src * K + k0 + a_chunk * 8);
+      else
+        pa[i] = make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      pb[h] = *(const uint4*)(b_codes + (k0 >> 1) + 16 * h);
+      ps[h] = b_scales[(k0 >> 5) + h];
+    }
+  };
+  auto store_k = [&]() {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = (tid >> 3) + 32 * i;
+      *(uint4*)(s_a + swz(r, a_chunk)) = pa[i];
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      uint4 d[4];
+      dequant32(pb[h], ps[h], d);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) *(uint4*)(s_b + swz(b_row, 4 * h + c)) = d[c];
+    }
+  };
+
+  f32x16 acc[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+
+  // wave tile: rows wm*64 + {0,32}, B rows: GLU -> gate wn*64 + {0,32}, up 128 + wn*64 + {0,32};
+  // down -> wn*128 + {0,32,64,96}
+  int brow[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if (GLU) brow[j] = (j < 2 ? 0 : kBN / 2) + wn * 64 + (j & 1) * 32;
+    else brow[j] = wn * 128 + j * 32;
+  }
+  const int lr = lane & 31, kg = lane >> 5;
+
+  load_k(0);
+  for (int kt = 0; kt < nk; ++kt) {
+    __syncthreads();  // previous step's LDS reads are done
+    store_k();
+    __syncthreads();
+    if (kt + 1 < nk) load_k(kt + 1);
+#pragma unroll
+    for (int ks = 0; ks < kBK / 16; ++ks) {
+      const int chunk = ks * 2 + kg;
+      bf16x8 af[2], bfg[4];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) af[i] = *(const bf16x8*)(s_a + swz(wm * 64 + i * 32 + lr, chunk));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) bfg[j] = *(const bf16x8*)(s_b + swz(brow[j] + lr, chunk));
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfg[j], acc[i][j], 0, 0, 0);
+    }
+  }
+
+  // epilogue: C element r of lane: row 8*(r/4) + 4*kg + r%4, column lr
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = wm * 64 + i * 32 + 8 * (r >> 2) + 4 * kg + (r & 3);
+      if (row >= rows) continue;
+      if (GLU) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const float g = acc[i][j][r], u = acc[i][j + 2][r];
+          const float hv = g / (1.f + expf(-g)) * u;
+          uint32_t bits = __float_as_uint(hv);
+          bits += 0x7FFFu + ((bits >> 16) & 1u);
+          const int col = n0 + wn * 64 + j * 32 + lr;
+          a.h_out[(size_t)(pos0 + row) * a.N + col] = (uint16_t)(bits >> 16);
+        }
+      } else {
+        const int pair = a.perm[pos0 + row];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int col = n0 + wn * 128 + j * 32 + lr;
+          a.p_out[(size_t)pair * a.N + col] = acc[i][j][r];
+        }
+      }
+    }
+  }
+}
+
+// y[t] = sum over ascending j of w[t][j] * P[t*k + j]
+template <int AT>
+__global__ __launch_bounds__(256) void prefill_merge_kernel(const float* __restrict__ w,
+                                                            const int32_t* __restrict__ ids,
+                                                            const float* __restrict__ P, int k, int H,
+                                                            int E, void* __restrict__ y) {
+  const int t = blockIdx.y;
+  const int h = blockIdx.x * blockDim.x + threadIdx.x;
+  if (h >= H) return;
+  float acc = 0.f;
+  for (int j = 0; j < k; ++j) {
+    const int p = t * k + j;
+    const int e = ids[p];
+    if (e >= 0 && e < E) acc = fmaf(w[p], P[(size_t)p * H + h], acc);
+  }
+  if constexpr (AT == MOE_F32) {
+    ((float*)y)[(size_t)t * H + h] = acc;
+  } else {
+    uint32_t u = __float_as_uint(acc);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    ((uint16_t*)y)[(size_t)t * H + h] = (uint16_t)(u >> 16);
+  }
+}
+
+hipError_t launch_prefill_compute(moe_ctx* ctx, int layer, const void* x, int T, const int32_t* ids,
+                                  const float* w, void* y, hipStream_t s) {
+  const moe_config& c = ctx->cfg;
+  if (c.w_dtype != MOE_MXFP4 || c.act_dtype != MOE_BF16) return hipErrorNotSupported;
+  const int E = c.n_experts, k = c.top_k, H = c.hidden, I = c.inter;
+  const int Tk = T * k;
+  auto& pf = ctx->pf;
+  hipLaunchKernelGGL(group_zero_kernel, dim3((E + 255) / 256), dim3(256), 0, s, pf.counts, pf.cursor, E);
+  const int gb = std::min(1024, (Tk + 255) / 256);
+  hipLaunchKernelGGL(group_hist_kernel, dim3(gb), dim3(256), 0, s, ids, Tk, E, pf.counts);
+  hipLaunchKernelGGL(group_scan_kernel, dim3(1), dim3(1024), 0, s, pf.counts, E, pf.offsets, pf.tiles);
+  hipLaunchKernelGGL(group_scatter_kernel, dim3(gb), dim3(256), 0, s, ids, Tk, E, pf.offsets,
+                     pf.cursor, pf.perm);
+  GemmArgs a{};
+  a.slot_base = ctx->pool.base;
+  a.stride = ctx->stride;
+  a.slot0 = (layer & 1) * E;
+  a.E = E;
+  a.k = k;
+  a.offsets = pf.offsets;
+  a.tiles = pf.tiles;
+  a.perm = pf.perm;
+  a.max_mtiles = Tk / kBM + E;
+  const int grid_m = (a.max_mtiles + 7) / 8 * 8;
+  // GEMM1: gate/up, K = H, N = I
+  a.K = H;
+  a.N = I;
+  a.off0 = 0;
+  a.off1 = (size_t)I * H / 2;
+  a.soff0 = 3 * (size_t)H * I / 2;
+  a.soff1 = a.soff0 + (size_t)I * H / 32;
+  a.a_src = (const uint16_t*)x;
+  a.h_out = pf.hmid;
+  a.n_ntiles = I / (kBN / 2);
+  hipLaunchKernelGGL(grouped_gemm_kernel<true>, dim3(grid_m * a.n_ntiles), dim3(kGemmThreads), 0, s, a);
+  // GEMM2: down, K = I, N = H
+  a.K = I;
+  a.N = H;
+  a.off0 = (size_t)I * H;
+  a.soff0 = 3 * (size_t)H * I / 2 + 2 * (size_t)I * H / 32;
+  a.a_src = pf.hmid;
+  a.p_out = pf.prow;
+  a.n_ntiles = H / kBN;
+  hipLaunchKernelGGL(grouped_gemm_kernel<false>, dim3(grid_m * a.n_ntiles), dim3(kGemmThreads), 0, s, a);
+  dim3 mg((H + 255) / 256, T);
+  hipLaunchKernelGGL(prefill_merge_kernel<MOE_BF16>, mg, dim3(256), 0, s, w, ids, pf.prow, k, H, E, y);
+  return hipGetLastError();
 }
 
 }  // namespace moert

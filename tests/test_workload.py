@@ -66,3 +66,13 @@ def test_reuse_calibration():
     Qwen-shaped decode workload (measured on its own first 128 steps)."""
     lg = W.decode_logits(W.QWEN_BF16, steps=128)
     assert abs(W.reuse_fraction(lg, W.QWEN_BF16.k) - 0.60) <= 0.01
+
+
+def test_uniforms_strictly_inside_unit_interval_and_logits_finite():
+    u = W.uniform(1005, W.TAG_NOISE, 0, 0, 1 << 20)
+    assert u.min() > 0.0 and u.max() < 1.0
+    # the largest possible draw stays below 1 and gives a finite Gumbel
+    top = ((2 ** 24 - 1) + 0.5) / 2 ** 24
+    assert top < 1.0 and np.isfinite(-np.log(-np.log(top)))
+    lg = W.decode_logits(W.QWEN_ELASTIC, steps=160)
+    assert np.isfinite(lg).all()

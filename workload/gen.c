@@ -12,7 +12,9 @@
  * Block j yields four 32-bit words; element i of a stream uses word i % 4 of
  * block i / 4.
  *
- * Uniforms: u = ((w >> 8) + 0.5) * 2^-24, strictly inside (0, 1).
+ * Uniforms: u = ((w >> 8) + 0.5) * 2^-24, strictly inside (0, 1) in double
+ * (the float path used for normals may round the top values to 1.0, which
+ * only yields a zero normal).
  * Normals: Box-Muller on word pairs (0,1) and (2,3) of a block, in float.
  *
  * Expert-bank byte layout (one bank == one device slot; H = hidden,
@@ -120,11 +122,13 @@ static void normals_range(uint64_t seed, uint32_t a, uint32_t b, uint32_t c,
   }
 }
 
+/* Uniforms in double: ((w >> 8) + 0.5) * 2^-24 is exact there and lies
+ * strictly inside (0, 1) (in float the top values round up to 1.0). */
 void wl_uniform_f64(uint64_t seed, uint32_t a, uint32_t b, uint32_t c, int64_t n, double* out) {
   uint32_t w[4];
   for (int64_t i = 0; i < n; ++i) {
     if ((i & 3) == 0) block(seed, (uint32_t)(i >> 2), a, b, c, w);
-    out[i] = (double)u01(w[i & 3]);
+    out[i] = ((double)(w[i & 3] >> 8) + 0.5) * (1.0 / 16777216.0);
   }
 }
 
