@@ -29,6 +29,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "MoE-layer decode µs/layer + expert-FFN HBM GB/s (% of peak); prefill TFLOP/s"
 HBM_PEAK_GBPS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0
 
 
 def parse():
@@ -40,7 +41,80 @@ def parse():
     ap.add_argument("--mode", default="hybrid", choices=["hybrid", "offload", "cpu"])
     ap.add_argument("--cpu-baseline-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
     return ap.parse_args()
+
+
+def bench_prefill():
+    """One untimed pass and one timed pass of the DeepSeek-shaped MXFP4
+    prefill chunk (8 layers x 8,192 tokens, two full-layer buffers of 256
+    experts, the next layer's slab streamed while the current one computes).
+    Returns the grouped-GEMM TFLOP/s (HIP events around the two GEMM kernels),
+    the wall time per layer and the slab copy rate."""
+    import ctypes  # noqa: F401
+
+    import numpy as np
+    import torch
+
+    import routed_expert_execution_moe_amd as B
+    import workload as W
+
+    wl = W.DSV4_PREFILL
+    dev = torch.device("cuda:0")
+    cfg = B.config(wl.L, wl.E, wl.k, wl.H, wl.I, wl.w_dtype, wl.act_dtype, wl.n_slots,
+                   max_tokens=1, bw_pcie_mbps=wl.bw_pcie_mbps, bw_host_mbps=wl.bw_host_mbps,
+                   max_prefill_tokens=wl.T, timing=1)
+    stride = B.moe_expert_bytes(cfg)
+    pool_bytes = wl.n_ids * stride
+    pool = B.moe_host_pool_alloc(pool_bytes)
+    ctx = None
+    try:
+        W.fill_banks(wl, pool, 0, wl.n_ids)
+        ctx = B.moe_create(cfg, pool, pool_bytes)
+        lg = torch.from_numpy(np.stack([W.prefill_logits(wl, l) for l in range(wl.L)])).to(dev)
+        xs = np.stack([W.hidden(wl, 0, l) for l in range(wl.L)])
+        x = torch.from_numpy(xs.view(np.int16)).to(dev).view(torch.bfloat16)
+        ids = torch.empty((wl.L, wl.T, wl.k), dtype=torch.int32, device=dev)
+        w = torch.empty((wl.L, wl.T, wl.k), dtype=torch.float32, device=dev)
+        y = torch.empty((wl.L, wl.T, wl.H), dtype=torch.bfloat16, device=dev)
+
+        def one_pass():
+            for l in range(wl.L):
+                B.moe_route_topk(ctx, lg[l], wl.T, ids[l], w[l])
+                B.moe_prefill_layer(ctx, l, x[l], wl.T, ids[l], w[l], y[l])
+
+        one_pass()
+        torch.cuda.synchronize()
+        B.moe_ctx_timing(ctx, reset=True)
+        t0 = time.perf_counter()
+        one_pass()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        tm = B.moe_ctx_timing(ctx)
+        flops = wl.L * 6.0 * wl.H * wl.I * wl.T * wl.k
+        gemm_ms = tm["prefill_gemm"]["ms"]
+        tflops = flops / (gemm_ms * 1e-3) / 1e12
+        slab = wl.E * W.expert_bytes(wl)
+        copy_ms = tm["prefill_copy"]["ms"]
+        copies = tm["prefill_copy"]["calls"]
+        return {
+            "prefill_workload": wl.name,
+            "prefill_tflops": round(tflops, 1),
+            "prefill_roofline": {"bound": "mfma", "kernel": "grouped GEMM1 + GEMM2 (bf16 MFMA, "
+                                 "MXFP4 dequantised in registers)", "achieved": round(tflops, 1),
+                                 "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                 "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4), "traffic": None},
+            "prefill_gemm_ms_per_layer": round(gemm_ms / wl.L, 3),
+            "prefill_group_ms_per_layer": round(tm["prefill_group"]["ms"] / wl.L, 3),
+            "prefill_merge_ms_per_layer": round(tm["prefill_merge"]["ms"] / wl.L, 3),
+            "prefill_layer_ms": round(wall / wl.L * 1e3, 3),
+            "prefill_chunk_tok_s": round(wl.T / wall, 1),
+            "prefill_copy_gbps": round(slab * copies / (copy_ms * 1e-3) / 1e9, 1) if copy_ms else None,
+        }
+    finally:
+        if ctx:
+            B.moe_destroy(ctx)
+        B.moe_host_pool_free(pool)
 
 
 def cpu_baseline(wl, pool_np, stride, logits, xs, steps_range, budget_s):
@@ -107,25 +181,26 @@ def main():
     dev = torch.device("cuda:0")
 
     t_setup = time.perf_counter()
-    cfg = B.config(wl.L, wl.E, wl.k, wl.H, wl.I, wl.w_dtype, wl.act_dtype, wl.n_slots,
-                   max_slots=max([wl.n_slots] + list(wl.resize.values())), max_tokens=wl.T,
-                   bw_pcie_mbps=wl.bw_pcie_mbps, bw_host_mbps=wl.bw_host_mbps, mode=mode,
-                   timing=1)
-    stride = B.moe_expert_bytes(cfg)
+
+    def make_cfg(timing):
+        return B.config(wl.L, wl.E, wl.k, wl.H, wl.I, wl.w_dtype, wl.act_dtype, wl.n_slots,
+                        max_slots=max([wl.n_slots] + list(wl.resize.values())), max_tokens=wl.T,
+                        bw_pcie_mbps=wl.bw_pcie_mbps, bw_host_mbps=wl.bw_host_mbps, mode=mode,
+                        timing=timing)
+
+    stride = B.moe_expert_bytes(make_cfg(0))
     pool_bytes = wl.n_ids * stride
     pool = B.moe_host_pool_alloc(pool_bytes)
     W.fill_banks(wl, pool, 0, wl.n_ids)
     pool_np = np.ctypeslib.as_array((ctypes.c_uint8 * pool_bytes).from_address(pool))
-    ctx = B.moe_create(cfg, pool, pool_bytes)
     n_run = warmup + steps
     logits = W.router_logits(wl)[:n_run]
     lg_d = torch.from_numpy(np.ascontiguousarray(logits)).to(dev)           # [S, L, T, E]
+    xs_np = np.stack([np.stack([W.hidden(wl, s, l) for l in range(wl.L)]) for s in range(n_run)])
     if wl.act_dtype == "bf16":
-        xs_np = np.stack([np.stack([W.hidden(wl, s, l) for l in range(wl.L)]) for s in range(n_run)])
         x_d = torch.from_numpy(xs_np.view(np.int16)).to(dev).view(torch.bfloat16)
         act = torch.bfloat16
     else:
-        xs_np = np.stack([np.stack([W.hidden(wl, s, l) for l in range(wl.L)]) for s in range(n_run)])
         x_d = torch.from_numpy(xs_np).to(dev)
         act = torch.float32
     ids = torch.empty((wl.L, wl.T, wl.k), dtype=torch.int32, device=dev)
@@ -137,27 +212,39 @@ def main():
           f"{wl.n_slots} slots, warmup {warmup} steps, timed {steps} steps", file=sys.stderr,
           flush=True)
 
-    def step(s):
-        for l in range(wl.L):
-            B.moe_route_topk(ctx, lg_d[s, l], wl.T, ids[l], w[l])
-            B.moe_cache_plan(ctx, l, ids[l], wl.T, x_d[s, l])
-            B.moe_expert_ffn(ctx, l, x_d[s, l], wl.T)
-            B.moe_merge(ctx, w[l], wl.T, y[l])
+    def run(timing):
+        """Fresh context (cold cache), warmup steps, then the timed steps."""
+        ctx = B.moe_create(make_cfg(timing), pool, pool_bytes)
 
-    for s in range(warmup):
-        step(s)
-    torch.cuda.synchronize()
-    B.moe_ctx_timing(ctx, reset=True)
-    st0 = B.moe_ctx_stats(ctx)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(warmup, n_run):
-        step(s)
-    torch.cuda.synchronize()
-    dt = time.perf_counter() - t0
-    tm = B.moe_ctx_timing(ctx)
-    st1 = B.moe_ctx_stats(ctx)
+        def step(s):
+            for l in range(wl.L):
+                B.moe_route_topk(ctx, lg_d[s, l], wl.T, ids[l], w[l])
+                B.moe_cache_plan(ctx, l, ids[l], wl.T, x_d[s, l])
+                B.moe_expert_ffn(ctx, l, x_d[s, l], wl.T)
+                B.moe_merge(ctx, w[l], wl.T, y[l])
 
+        try:
+            for s in range(warmup):
+                step(s)
+            torch.cuda.synchronize()
+            if timing:
+                B.moe_ctx_timing(ctx, reset=True)
+            st0 = B.moe_ctx_stats(ctx)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for s in range(warmup, n_run):
+                step(s)
+            torch.cuda.synchronize()
+            dt = time.perf_counter() - t0
+            tm = B.moe_ctx_timing(ctx) if timing else None
+            st1 = B.moe_ctx_stats(ctx)
+        finally:
+            B.moe_destroy(ctx)
+        return dt, tm, st0, st1
+
+    # the number: events off; the per-phase breakdown: a second run with events on
+    dt, _, st0, st1 = run(0)
+    dt_timed, tm, _, _ = run(1)
     calls = steps * wl.L
     us_per_layer = dt / calls * 1e6
     n_gpu_experts = (st1.hits - st0.hits) + (st1.fills - st0.fills)
@@ -209,6 +296,7 @@ def main():
         },
         "cpu_baseline": cpu,
         "breakdown_us_per_call": per,
+        "breakdown_run_us_per_layer": round(dt_timed / (steps * wl.L) * 1e6, 2),
         "control_kernel_us": per.get("plan"),
         "ffn_us_per_layer": per.get("ffn"),
         "ffn_bytes_per_layer": round(ffn_bytes / calls),
@@ -216,12 +304,12 @@ def main():
         "miss_rate": round(1 - (st1.hits - st0.hits) / max(accesses, 1), 4),
         "fills_per_layer": round((st1.fills - st0.fills) / calls, 3),
         "cpu_experts_per_layer": round((st1.cpu - st0.cpu) / calls, 3),
-        "prefill_tflops": None,
     }
-    print(json.dumps(out), flush=True)
-    B.moe_destroy(ctx)
     pool_np = None
     B.moe_host_pool_free(pool)
+    if not a.no_prefill:
+        out.update(bench_prefill())
+    print(json.dumps(out), flush=True)
 
 
 if __name__ == "__main__":

@@ -234,11 +234,13 @@ moe_status moe_ctx_stats(moe_ctx* ctx, moe_stats* out);
 /* Device time per phase, summed since creation (or the last reset), when the
  * context was created with cfg.timing = 1: each call brackets the kernels it
  * launches with a pair of HIP events on the stream they run on.  HOST is the
- * wall time of the host branch callback.  Synchronises the device; not for
+ * wall time of the host branch (poller thread) per call with host work;
+ * PREFILL_GEMM covers the two grouped GEMM kernels only.  Synchronises the device; not for
  * the hot path.  MOE_EINVAL if timing is off. */
 enum {
   MOE_T_ROUTE = 0, MOE_T_PLAN = 1, MOE_T_FILL = 2, MOE_T_FFN = 3, MOE_T_MERGE = 4,
-  MOE_T_HOST = 5, MOE_T_PREFILL_COPY = 6, MOE_T_PREFILL_GEMM = 7, MOE_T_COUNT = 8
+  MOE_T_HOST = 5, MOE_T_PREFILL_COPY = 6, MOE_T_PREFILL_GROUP = 7, MOE_T_PREFILL_GEMM = 8,
+  MOE_T_PREFILL_MERGE = 9, MOE_T_COUNT = 10
 };
 typedef struct {
   int64_t calls[MOE_T_COUNT];

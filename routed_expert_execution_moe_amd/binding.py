@@ -59,11 +59,12 @@ class Stats(ctypes.Structure):
                 ("prefill_layers", ctypes.c_int64), ("resizes", ctypes.c_int64)]
 
 
-PHASES = ("route", "plan", "fill", "ffn", "merge", "host", "prefill_copy", "prefill_gemm")
+PHASES = ("route", "plan", "fill", "ffn", "merge", "host", "prefill_copy", "prefill_group",
+          "prefill_gemm", "prefill_merge")
 
 
 class Timing(ctypes.Structure):
-    _fields_ = [("calls", ctypes.c_int64 * 8), ("ms", ctypes.c_double * 8)]
+    _fields_ = [("calls", ctypes.c_int64 * len(PHASES)), ("ms", ctypes.c_double * len(PHASES))]
 
     def as_dict(self):
         return {p: dict(calls=self.calls[i], ms=self.ms[i]) for i, p in enumerate(PHASES)}

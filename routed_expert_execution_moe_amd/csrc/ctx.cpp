@@ -53,16 +53,11 @@ static size_t expert_bytes_of(const moe_config* c) {
 // Row chunk (elements per 16-byte weight load) of a weight dtype.
 static int chunk_elems(int w_dtype) { return w_dtype == MOE_F32 ? 4 : w_dtype == MOE_BF16 ? 8 : 32; }
 
-// The decode kernels split a row of K elements into NCH = K / chunk chunks
-// handled by G = (largest power of two dividing NCH, at most 64) lanes and
-// KS = NCH / G waves; G must be >= 16 and KS <= 4.
+// The decode GEMV gives every lane of a wave up to 8 of the NCH = K / chunk
+// 16-byte chunks of a row, so NCH <= 512.
 static bool row_split_ok(int K, int w_dtype) {
   int ch = chunk_elems(w_dtype);
-  if (K % ch) return false;
-  int nch = K / ch;
-  int g = 1;
-  while (g < 64 && nch % (2 * g) == 0) g *= 2;
-  return g >= 16 && nch / g <= 4;
+  return K % ch == 0 && K / ch <= 512;
 }
 
 static std::string validate(const moe_config* c) {
@@ -75,7 +70,7 @@ static std::string validate(const moe_config* c) {
   if (c->hidden < 1 || c->inter < 1) return "hidden and inter must be positive";
   if (c->hidden % 64 || c->inter % 64) return "hidden and inter must be multiples of 64";
   if (!row_split_ok(c->hidden, c->w_dtype) || !row_split_ok(c->inter, c->w_dtype))
-    return "hidden/inter must split into at most 4 waves of 16..64-lane groups (e.g. bf16: 128..2048 in steps of 128 with an odd factor <= 3)";
+    return "hidden/inter too large for the decode GEMV (at most 512 sixteen-byte chunks per row)";
   if (c->max_slots < 0 || c->max_slots > kMaxSlots) return "max_slots must be in 0..32768";
   if (c->n_slots < 0 || c->n_slots > c->max_slots) return "n_slots must be in 0..max_slots";
   if (c->max_tokens < 1 || c->max_tokens > kMaxDecodeTokens) return "max_tokens must be in 1..256";
@@ -795,8 +790,6 @@ extern "C" moe_status moe_prefill_layer(moe_ctx* ctx, int32_t layer, const void*
     MOE_HIP(ctx, launch_prefill_admit(ctx, layer, s));
     pf.admitted[b] = true;
   }
-  MOE_HIP(ctx, timing_begin(ctx, MOE_T_PREFILL_GEMM, s));
   MOE_HIP(ctx, launch_prefill_compute(ctx, layer, x, T, ids, w, y, s));
-  MOE_HIP(ctx, timing_end(ctx, s));
   return MOE_OK;
 }

@@ -177,8 +177,7 @@ struct GemvArgs {
   const int32_t* slot_map;
   int Tk, k;
   int K, rows;          // contraction length, output rows per matrix
-  int G, KS, RPW;       // lanes per row, waves per workgroup, rows per wave per group
-  int items;            // row-block items per expert
+  int items;            // row blocks of RW rows per expert
   size_t off0, off1;    // matrix byte offsets inside a slot
   size_t soff0, soff1;  // MX scale offsets
   const void* x;        // input vectors
@@ -188,137 +187,149 @@ struct GemvArgs {
 
 __device__ inline float silu(float g) { return g / (1.f + expf(-g)); }
 
-// GLU: two matrices (gate, up) and out = silu(gate) * up; else one matrix.
-template <int WT, int XT, int NT, int RB, bool GLU>
+// One item per wave: RW consecutive rows of one GPU expert (of both the gate
+// and the up matrix when GLU).  Lane l owns chunks l, l+64, ... (CPL of them)
+// of every row; the weights are loaded first and stay in registers while the
+// wave loops over the expert's routed tokens, so they are read once however
+// many tokens share the expert.  Rows are reduced across the wave with xor
+// shuffles; no LDS, no barriers.
+template <int WT, int XT, int NT, int RW, int CPL, bool GLU>
 __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
   constexpr int CH = WChunk<WT>::CH;
   constexpr int NM = GLU ? 2 : 1;
-  extern __shared__ float s_red[];  // [KS][RB*RPW][NM][NT]
-  __shared__ int s_np;
-  __shared__ int s_pairs[kMaxDecodeTokens];
-
-  const int g = blockIdx.x / a.items;
-  const int rb = blockIdx.x - g * a.items;
-  if (g >= a.counts->n_gpu) return;
+  const int lane = threadIdx.x & 63;
+  const int item = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  const int g = item / a.items;
+  const int n_gpu = a.counts->n_gpu;
+  if (g >= n_gpu) return;  // wave-uniform
+  const int rb = item - g * a.items;
   const int slot = a.gpu_slot[g];
-  const int tid = threadIdx.x;
-  if (tid == 0) s_np = 0;
-  __syncthreads();
-  for (int i = tid; i < a.Tk; i += blockDim.x)
-    if (a.slot_map[i] == slot) {
-      const int pos = atomicAdd(&s_np, 1);
-      if (pos < kMaxDecodeTokens) s_pairs[pos] = i;
-    }
-  __syncthreads();
-  const int np = min(s_np, kMaxDecodeTokens);
+  const uint8_t* sp = a.slot_base + (size_t)slot * a.stride;
+  const int row0 = rb * RW;
+  const int nch = a.K / CH;
 
-  const int w = tid >> 6, l = tid & 63;
-  const int ro = l / a.G, cl = l - ro * a.G;
-  const int c = w * a.G + cl;  // chunk index along K
-  const int RR = RB * a.RPW;   // rows per item
-  const int row0 = rb * RR;
-  const uint8_t* slotp = a.slot_base + (size_t)slot * a.stride;
-  const uint8_t* m0 = slotp + a.off0;
-  const uint8_t* m1 = slotp + a.off1;
-  const uint8_t* s0 = slotp + a.soff0;
-  const uint8_t* s1 = slotp + a.soff1;
-
-  for (int tg = 0; tg < np; tg += NT) {
-    const int nt = min(NT, np - tg);
-    float xr[NT][CH];
+  Raw<WT> wr[NM][RW][CPL];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      if (t < nt) {
-        const int p = s_pairs[tg + t];
-        load_x<XT, CH>(a.x, a.x_by_token ? p / a.k : p, a.K, c, xr[t]);
+  for (int i = 0; i < RW; ++i) {
+    const int row = min(row0 + i, a.rows - 1);
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      const int ch = lane + 64 * c;
+      if (ch < nch) {
+        wr[0][i][c] = load_chunk<WT>(sp + a.off0, sp + a.soff0, row, a.K, ch);
+        if constexpr (GLU) wr[1][i][c] = load_chunk<WT>(sp + a.off1, sp + a.soff1, row, a.K, ch);
       } else {
 #pragma unroll
-        for (int j = 0; j < CH; ++j) xr[t][j] = 0.f;
+        for (int m = 0; m < NM; ++m) {
+          wr[m][i][c].v = make_uint4(0, 0, 0, 0);
+          wr[m][i][c].scale = 127;
+        }
       }
     }
-    Raw<WT> wr[NM][RB];
+  }
+
+  // the expert's routed pairs, NT at a time (ballots are wave-uniform)
+  int base = 0;
+  uint64_t bm = __ballot(lane < a.Tk && a.slot_map[lane] == slot);
+  for (;;) {
+    int pr[NT];
+    int nt = 0;
 #pragma unroll
-    for (int i = 0; i < RB; ++i) {
-      const int row = row0 + i * a.RPW + ro;
-      wr[0][i] = load_chunk<WT>(m0, s0, row, a.K, c);
-      if constexpr (GLU) wr[1][i] = load_chunk<WT>(m1, s1, row, a.K, c);
-    }
-    float acc[NM][RB][NT];
-#pragma unroll
-    for (int mm = 0; mm < NM; ++mm)
-#pragma unroll
-      for (int i = 0; i < RB; ++i)
-#pragma unroll
-        for (int t = 0; t < NT; ++t) acc[mm][i][t] = chunk_dot<WT>(wr[mm][i], xr[t]);
-    // reduce within the lane group of each row
-    for (int off = a.G >> 1; off >= 1; off >>= 1) {
-#pragma unroll
-      for (int mm = 0; mm < NM; ++mm)
-#pragma unroll
-        for (int i = 0; i < RB; ++i)
-#pragma unroll
-          for (int t = 0; t < NT; ++t) acc[mm][i][t] += __shfl_xor(acc[mm][i][t], off);
-    }
-    if (cl == 0) {
-#pragma unroll
-      for (int mm = 0; mm < NM; ++mm)
-#pragma unroll
-        for (int i = 0; i < RB; ++i)
-#pragma unroll
-          for (int t = 0; t < NT; ++t)
-            s_red[((w * RR + i * a.RPW + ro) * NM + mm) * NT + t] = acc[mm][i][t];
-    }
-    __syncthreads();
-    // fixed-order combination over the waves, then the epilogue
-    for (int idx = tid; idx < RR * nt; idx += blockDim.x) {
-      const int rl = idx / nt, t = idx - rl * nt;
-      float v0 = 0.f, v1 = 0.f;
-      for (int ww = 0; ww < a.KS; ++ww) {
-        v0 += s_red[((ww * RR + rl) * NM + 0) * NT + t];
-        if constexpr (GLU) v1 += s_red[((ww * RR + rl) * NM + 1) * NT + t];
+    for (int t = 0; t < NT; ++t) {
+      while (bm == 0 && base + 64 < a.Tk) {
+        base += 64;
+        bm = __ballot(base + lane < a.Tk && a.slot_map[base + lane] == slot);
       }
-      const float o = GLU ? silu(v0) * v1 : v0;
-      const int p = s_pairs[tg + t];
-      a.out[(size_t)p * a.rows + row0 + rl] = o;
+      pr[t] = -1;
+      if (bm) {
+        pr[t] = base + __builtin_ctzll(bm);
+        bm &= bm - 1;
+        ++nt;
+      }
     }
-    __syncthreads();
+    if (nt == 0) break;
+    float acc[NM][RW][NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+#pragma unroll
+      for (int m = 0; m < NM; ++m)
+#pragma unroll
+        for (int i = 0; i < RW; ++i) acc[m][i][t] = 0.f;
+      if (pr[t] < 0) continue;
+      const int idx = a.x_by_token ? pr[t] / a.k : pr[t];
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) {
+        const int ch = lane + 64 * c;
+        if (ch >= nch) continue;
+        float xv[CH];
+        load_x<XT, CH>(a.x, idx, a.K, ch, xv);
+#pragma unroll
+        for (int m = 0; m < NM; ++m)
+#pragma unroll
+          for (int i = 0; i < RW; ++i) acc[m][i][t] += chunk_dot<WT>(wr[m][i][c], xv);
+      }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1)
+#pragma unroll
+      for (int m = 0; m < NM; ++m)
+#pragma unroll
+        for (int i = 0; i < RW; ++i)
+#pragma unroll
+          for (int t = 0; t < NT; ++t) acc[m][i][t] += __shfl_xor(acc[m][i][t], off);
+#pragma unroll
+    for (int i = 0; i < RW; ++i)
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+        if (lane == (i * NT + t) % 64 && pr[t] >= 0 && row0 + i < a.rows) {
+          const float o = GLU ? silu(acc[0][i][t]) * acc[GLU ? 1 : 0][i][t] : acc[0][i][t];
+          a.out[(size_t)pr[t] * a.rows + row0 + i] = o;
+        }
   }
 }
 
-// lanes per row G, waves KS and rows per wave RPW for a contraction of K
-static void split_of(int K, int CH, int* G, int* KS, int* RPW) {
+// chunks per lane for a contraction of K
+static int cpl_of(int K, int CH) {
   int nch = K / CH;
-  int g = 1;
-  while (g < 64 && nch % (2 * g) == 0) g *= 2;
-  *G = g;
-  *KS = nch / g;
-  *RPW = 64 / g;
+  return nch <= 64 ? 1 : nch <= 128 ? 2 : nch <= 256 ? 4 : 8;
 }
 
-template <int WT, int XT, bool GLU>
-static hipError_t launch_gemv_t(GemvArgs a, int umax, int T, hipStream_t s) {
+template <int WT, int XT, int NT, bool GLU>
+static hipError_t launch_gemv_nt(GemvArgs a, int umax, hipStream_t s) {
   constexpr int CH = WChunk<WT>::CH;
-  split_of(a.K, CH, &a.G, &a.KS, &a.RPW);
-  // tokens held in registers per pass, and row groups per wave
-  int nt = T <= 1 ? 1 : T <= 2 ? 2 : T <= 4 ? 4 : 8;
-  if (WT == MOE_MXFP4 && nt > 2) nt = 2;
-  auto go = [&](auto NTc, auto RBc) -> hipError_t {
-    constexpr int NT = decltype(NTc)::value, RB = decltype(RBc)::value;
-    const int RR = RB * a.RPW;
-    a.items = (a.rows + RR - 1) / RR;
-    if (a.rows % RR) return hipErrorInvalidValue;
-    size_t shm = sizeof(float) * a.KS * RR * (GLU ? 2 : 1) * NT;
-    hipLaunchKernelGGL((gemv_kernel<WT, XT, NT, RB, GLU>), dim3(umax * a.items), dim3(64 * a.KS), shm, s, a);
+  const int cpl = cpl_of(a.K, CH);
+  // about 16 sixteen-byte weight loads in flight per lane
+  auto go = [&](auto CPLc, auto RWc) -> hipError_t {
+    constexpr int C = decltype(CPLc)::value, R = decltype(RWc)::value;
+    a.items = (a.rows + R - 1) / R;
+    const int waves = umax * a.items;
+    hipLaunchKernelGGL((gemv_kernel<WT, XT, NT, R, C, GLU>), dim3((waves + 3) / 4), dim3(256), 0, s, a);
     return hipGetLastError();
   };
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
   using I4 = std::integral_constant<int, 4>;
   using I8 = std::integral_constant<int, 8>;
-  if (nt == 1) return go(I1{}, I8{});
-  if (nt == 2) return go(I2{}, I8{});
-  if (nt == 4) return go(I4{}, I4{});
-  return go(I8{}, I2{});
+  using I16 = std::integral_constant<int, 16>;
+  if constexpr (GLU) {
+    if (cpl == 1) return go(I1{}, I8{});
+    if (cpl == 2) return go(I2{}, I4{});
+    if (cpl == 4) return go(I4{}, I2{});
+    return go(I8{}, I1{});
+  } else {
+    if (cpl == 1) return go(I1{}, I16{});
+    if (cpl == 2) return go(I2{}, I8{});
+    if (cpl == 4) return go(I4{}, I4{});
+    return go(I8{}, I2{});
+  }
+}
+
+template <int WT, int XT, bool GLU>
+static hipError_t launch_gemv_t(GemvArgs a, int umax, int T, hipStream_t s) {
+  if (T <= 1) return launch_gemv_nt<WT, XT, 1, GLU>(a, umax, s);
+  if (T <= 2) return launch_gemv_nt<WT, XT, 2, GLU>(a, umax, s);
+  if (T <= 4) return launch_gemv_nt<WT, XT, 4, GLU>(a, umax, s);
+  return launch_gemv_nt<WT, XT, 8, GLU>(a, umax, s);
 }
 
 template <int WT>

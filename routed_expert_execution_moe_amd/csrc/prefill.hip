@@ -336,12 +336,16 @@ hipError_t launch_prefill_compute(moe_ctx* ctx, int layer, const void* x, int T,
   const int E = c.n_experts, k = c.top_k, H = c.hidden, I = c.inter;
   const int Tk = T * k;
   auto& pf = ctx->pf;
+  hipError_t e = timing_begin(ctx, MOE_T_PREFILL_GROUP, s);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(group_zero_kernel, dim3((E + 255) / 256), dim3(256), 0, s, pf.counts, pf.cursor, E);
   const int gb = std::min(1024, (Tk + 255) / 256);
   hipLaunchKernelGGL(group_hist_kernel, dim3(gb), dim3(256), 0, s, ids, Tk, E, pf.counts);
   hipLaunchKernelGGL(group_scan_kernel, dim3(1), dim3(1024), 0, s, pf.counts, E, pf.offsets, pf.tiles);
   hipLaunchKernelGGL(group_scatter_kernel, dim3(gb), dim3(256), 0, s, ids, Tk, E, pf.offsets,
                      pf.cursor, pf.perm);
+  if ((e = timing_end(ctx, s)) != hipSuccess) return e;
+  if ((e = timing_begin(ctx, MOE_T_PREFILL_GEMM, s)) != hipSuccess) return e;
   GemmArgs a{};
   a.slot_base = ctx->pool.base;
   a.stride = ctx->stride;
@@ -373,9 +377,12 @@ hipError_t launch_prefill_compute(moe_ctx* ctx, int layer, const void* x, int T,
   a.p_out = pf.prow;
   a.n_ntiles = H / kBN;
   hipLaunchKernelGGL(grouped_gemm_kernel<false>, dim3(grid_m * a.n_ntiles), dim3(kGemmThreads), 0, s, a);
+  if ((e = timing_end(ctx, s)) != hipSuccess) return e;
+  if ((e = timing_begin(ctx, MOE_T_PREFILL_MERGE, s)) != hipSuccess) return e;
   dim3 mg((H + 255) / 256, T);
   hipLaunchKernelGGL(prefill_merge_kernel<MOE_BF16>, mg, dim3(256), 0, s, w, ids, pf.prow, k, H, E, y);
-  return hipGetLastError();
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  return timing_end(ctx, s);
 }
 
 }  // namespace moert

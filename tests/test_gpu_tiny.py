@@ -45,21 +45,32 @@ def test_tiny_end_to_end(mode):
         g.close()
 
 
-def test_tiny_prefill_needs_two_buffers():
+def test_prefill_refusals():
+    """The grouped GEMM takes MXFP4 experts with bf16 activations
+    (MOE_EUNSUPPORTED otherwise), and two full-layer buffers must fit in the
+    pool: the library refuses (MOE_ENOSPC) rather than oversubscribe."""
+    import dataclasses
+
     import torch
     import routed_expert_execution_moe_amd as B
-    wl = W.TINY
-    g = GpuRun(wl, max_prefill_tokens=16)
-    try:
-        x = torch.zeros((4, wl.H), dtype=torch.float32, device="cuda")
-        ids = torch.zeros((4, wl.k), dtype=torch.int32, device="cuda")
-        w = torch.zeros((4, wl.k), dtype=torch.float32, device="cuda")
-        y = torch.zeros((4, wl.H), dtype=torch.float32, device="cuda")
-        with pytest.raises(B.MoertError) as e:
-            B.moe_prefill_layer(g.ctx, 0, x, 4, ids, w, y)
-        assert e.value.status == -3
-    finally:
-        g.close()
+
+    def call(wl):
+        g = GpuRun(wl, max_prefill_tokens=16)
+        try:
+            dt = torch.float32 if wl.act_dtype == "f32" else torch.bfloat16
+            x = torch.zeros((4, wl.H), dtype=dt, device="cuda")
+            ids = torch.zeros((4, wl.k), dtype=torch.int32, device="cuda")
+            w = torch.zeros((4, wl.k), dtype=torch.float32, device="cuda")
+            y = torch.zeros((4, wl.H), dtype=dt, device="cuda")
+            with pytest.raises(B.MoertError) as e:
+                B.moe_prefill_layer(g.ctx, 0, x, 4, ids, w, y)
+            return e.value.status
+        finally:
+            g.close()
+
+    assert call(W.TINY) == -7
+    small = dataclasses.replace(W.DSV4_PREFILL, L=2, E=16, k=2, H=512, I=512, T=16, n_slots=31)
+    assert call(small) == -3
 
 
 def test_call_order_enforced():
