@@ -20,7 +20,10 @@
 // a 128-row M-tile of one expert and a 256-column N-tile, the waves in a 2x2
 // grid of 64 x 128 wave tiles (2 x 4 MFMA tiles); K steps of 64 staged in LDS
 // with the 16-byte chunks of each row XOR-swizzled by (row % 8), and the next
-// K step prefetched into registers while the MFMAs run.  For GEMM1 the 256
+// K step prefetched into registers while the MFMAs run and stored into the
+// other half of a double-buffered LDS tile.  B stays MXFP4 in LDS (a quarter
+// of its bf16 size) and each lane dequantises its 8-element fragment right
+// before the MFMA with the hardware scaled FP4 -> bf16 convert.  For GEMM1 the 256
 // B-tile rows are 128 gate rows then the matching 128 up rows, so a wave's
 // gate and up accumulators share lanes and the SiLU * up epilogue needs no
 // exchange.  Workgroups are mapped so that the N-tiles of one M-tile run on
@@ -94,36 +97,31 @@ __global__ __launch_bounds__(256) void group_scatter_kernel(const int32_t* __res
   }
 }
 
-// ------------------------------------------------------------------ MXFP4 -> bf16
-__device__ inline uint32_t e2m1_bits(uint32_t c) {
-  const uint32_t m = c & 7u;
-  uint32_t bits = m >= 2u ? ((((m >> 1) + 126u) << 23) | ((m & 1u) << 22)) : (m ? 0x3F000000u : 0u);
-  return bits | ((c & 8u) << 28);
+// ------------------------------------------------------------------ GEMM
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// 8 MXFP4 codes (4 bytes, low nibble first) times 2^(s-127) -> 8 bf16 with
+// the gfx950 scaled convert; e2m1 * 2^k is exact in bf16.
+__device__ inline bf16x8 fp4x8_to_bf16(uint32_t raw, float scale) {
+  const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(raw, scale, 0);
+  const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(raw, scale, 1);
+  const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(raw, scale, 2);
+  const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(raw, scale, 3);
+  bf16x8 r;
+  r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
+  r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
+  return r;
 }
 
-// 16 code bytes (32 elements) with one E8M0 scale -> 32 bf16 in 4 x 16 bytes.
-// e2m1 * 2^(s-127) is exact in bf16 (2 significant bits, fp32 exponent range).
-__device__ inline void dequant32(uint4 codes, uint32_t s, uint4 out[4]) {
-  const float sc = s ? __uint_as_float(s << 23) : __uint_as_float(0x00400000u);
-  const uint32_t w[4] = {codes.x, codes.y, codes.z, codes.w};
-  uint32_t o[16];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const uint32_t byte = (w[i] >> (8 * b)) & 0xFFu;
-      const uint32_t lo = __float_as_uint(__uint_as_float(e2m1_bits(byte & 15u)) * sc) >> 16;
-      const uint32_t hi = __float_as_uint(__uint_as_float(e2m1_bits(byte >> 4)) * sc) >> 16;
-      o[4 * i + b] = lo | (hi << 16);
-    }
-  }
-  out[0] = make_uint4(o[0], o[1], o[2], o[3]);
-  out[1] = make_uint4(o[4], o[5], o[6], o[7]);
-  out[2] = make_uint4(o[8], o[9], o[10], o[11]);
-  out[3] = make_uint4(o[12], o[13], o[14], o[15]);
+__device__ inline float e8m0_scale(uint32_t s) {
+  return s ? __uint_as_float(s << 23) : __uint_as_float(0x00400000u);
 }
 
+// A rows: 64 bf16 = 8 chunks of 16 B, chunk index XOR (row % 8)
 __device__ inline int swz(int row, int chunk) { return row * kRowBytes + ((chunk ^ (row & 7)) << 4); }
+// B rows: 64 codes = 8 words of 4 B, word index XOR ((row / 4) % 8): the 32
+// lanes reading one word of 32 consecutive rows hit 32 distinct banks
+__device__ inline int bswz(int row, int word) { return row * 32 + ((word ^ ((row >> 2) & 7)) << 2); }
 
 struct GemmArgs {
   const uint8_t* slot_base;   // slot s at slot_base + s * stride
@@ -145,9 +143,10 @@ struct GemmArgs {
 };
 
 template <bool GLU>
-__global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_kernel(GemmArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t s_a[kBM * kRowBytes];   // 16 KB
-  __shared__ __attribute__((aligned(16))) uint8_t s_b[kBN * kRowBytes];   // 32 KB
+__global__ __launch_bounds__(kGemmThreads, 2) void grouped_gemm_kernel(GemmArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t s_a[2][kBM * kRowBytes];   // 2 x 16 KB bf16
+  __shared__ __attribute__((aligned(16))) uint8_t s_b[2][kBN * 32];          // 2 x 8 KB fp4 codes
+  __shared__ uint8_t s_s[2][kBN * 2];                                        // 2 x 512 B scales
   __shared__ int32_t s_rowsrc[kBM];  // A source row per tile row, -1 = padding
 
   // XCD-aware mapping: consecutive workgroups go round-robin over 8 XCDs;
@@ -179,10 +178,9 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_kernel(GemmArgs 
   const int K = a.K;
   const int nk = K / kBK;
 
-  // per-thread load assignments
-  // A: 128 rows x 8 chunks = 1024 chunks, 4 per thread: rows tid/8 + 32*i, chunk tid%8
+  // loads: A 128 rows x 8 chunks (4 per thread: rows tid/8 + 32 i, chunk tid%8);
+  // B row tid: 32 code bytes and 2 scale bytes per K step
   const int a_chunk = tid & 7;
-  // B: 256 rows x 2 halves (32 elements each): row tid, halves 0 and 1
   const int b_row = tid;
   const uint8_t* b_codes;
   const uint8_t* b_scales;
@@ -202,40 +200,33 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_kernel(GemmArgs 
     b_codes = slot + coff + (size_t)mrow * (K / 2);
     b_scales = slot + soff + (size_t)mrow * (K / 32);
   }
+  int a_src_row[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) a_src_row[i] = s_rowsrc[(tid >> 3) + 32 * i];
 
   uint4 pa[4];
   uint4 pb[2];
-  uint32_t ps[2];
+  uint32_t ps;
   auto load_k = [&](int kt) {
     const int k0 = kt * kBK;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int r = (tid >> 3) + 32 * i;
-      const int src = s_rowsrc[r];
-      if (src >= 0)
-        pa[i] = *(const uint4*)(a.a_src + (size_t)src * K + k0 + a_chunk * 8);
+      if (a_src_row[i] >= 0)
+        pa[i] = *(const uint4*)(a.a_src + (size_t)a_src_row[i] * K + k0 + a_chunk * 8);
       else
         pa[i] = make_uint4(0, 0, 0, 0);
     }
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      pb[h] = *(const uint4*)(b_codes + (k0 >> 1) + 16 * h);
-      ps[h] = b_scales[(k0 >> 5) + h];
-    }
+    pb[0] = *(const uint4*)(b_codes + (k0 >> 1));
+    pb[1] = *(const uint4*)(b_codes + (k0 >> 1) + 16);
+    ps = *(const uint16_t*)(b_scales + (k0 >> 5));
   };
-  auto store_k = [&]() {
+  auto store_k = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = (tid >> 3) + 32 * i;
-      *(uint4*)(s_a + swz(r, a_chunk)) = pa[i];
-    }
+    for (int i = 0; i < 4; ++i) *(uint4*)(&s_a[buf][swz((tid >> 3) + 32 * i, a_chunk)]) = pa[i];
+    const uint32_t w[8] = {pb[0].x, pb[0].y, pb[0].z, pb[0].w, pb[1].x, pb[1].y, pb[1].z, pb[1].w};
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      uint4 d[4];
-      dequant32(pb[h], ps[h], d);
-#pragma unroll
-      for (int c = 0; c < 4; ++c) *(uint4*)(s_b + swz(b_row, 4 * h + c)) = d[c];
-    }
+    for (int q = 0; q < 8; ++q) *(uint32_t*)(&s_b[buf][bswz(b_row, q)]) = w[q];
+    *(uint16_t*)(&s_s[buf][b_row * 2]) = (uint16_t)ps;
   };
 
   f32x16 acc[2][4];
@@ -244,8 +235,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_kernel(GemmArgs 
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
 
-  // wave tile: rows wm*64 + {0,32}, B rows: GLU -> gate wn*64 + {0,32}, up 128 + wn*64 + {0,32};
-  // down -> wn*128 + {0,32,64,96}
+  // wave tile: rows wm*64 + {0,32}; B rows: GLU -> gate wn*64 + {0,32} and up
+  // 128 + wn*64 + {0,32}; down -> wn*128 + {0,32,64,96}
   int brow[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -255,25 +246,32 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_kernel(GemmArgs 
   const int lr = lane & 31, kg = lane >> 5;
 
   load_k(0);
+  store_k(0);
+  __syncthreads();
   for (int kt = 0; kt < nk; ++kt) {
-    __syncthreads();  // previous step's LDS reads are done
-    store_k();
-    __syncthreads();
+    const int buf = kt & 1;
     if (kt + 1 < nk) load_k(kt + 1);
 #pragma unroll
     for (int ks = 0; ks < kBK / 16; ++ks) {
-      const int chunk = ks * 2 + kg;
+      const int chunk = ks * 2 + kg;  // A: 16-byte chunk; B: 4-byte word
       bf16x8 af[2], bfg[4];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) af[i] = *(const bf16x8*)(s_a + swz(wm * 64 + i * 32 + lr, chunk));
+      for (int i = 0; i < 2; ++i) af[i] = *(const bf16x8*)(&s_a[buf][swz(wm * 64 + i * 32 + lr, chunk)]);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) bfg[j] = *(const bf16x8*)(s_b + swz(brow[j] + lr, chunk));
+      for (int j = 0; j < 4; ++j) {
+        const int n = brow[j] + lr;
+        const uint32_t raw = *(const uint32_t*)(&s_b[buf][bswz(n, chunk)]);
+        const float sc = e8m0_scale(s_s[buf][n * 2 + (ks >> 1)]);
+        bfg[j] = fp4x8_to_bf16(raw, sc);
+      }
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfg[j], acc[i][j], 0, 0, 0);
     }
+    if (kt + 1 < nk) store_k(buf ^ 1);
+    __syncthreads();
   }
 
   // epilogue: C element r of lane: row 8*(r/4) + 4*kg + r%4, column lr
