@@ -42,6 +42,8 @@ def parse():
     ap.add_argument("--cpu-baseline-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="run only the prefill leg (for profiling); prints its fields")
     return ap.parse_args()
 
 
@@ -172,6 +174,9 @@ def main():
     import routed_expert_execution_moe_amd as B
     import workload as W
 
+    if a.prefill_only:
+        print(json.dumps(bench_prefill()), flush=True)
+        return
     wl = {w.name: w for w in W.WORKLOADS}[a.workload]
     assert not wl.prefill, "decode workloads only"
     warmup = a.warmup if a.warmup is not None else min(32, wl.steps // 8)
