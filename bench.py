@@ -44,6 +44,9 @@ def parse():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--prefill-only", action="store_true",
                     help="run only the prefill leg (for profiling); prints its fields")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain streaming kernel of known size, whose "
+                         "FETCH_SIZE / WRITE_SIZE counter readings scale those counters to bytes")
     return ap.parse_args()
 
 
@@ -119,6 +122,22 @@ def bench_prefill():
         B.moe_host_pool_free(pool)
 
 
+def copy_calibration():
+    """Four launches of an elementwise kernel (negate) that reads 1 GiB and
+    writes 1 GiB of float32: the HBM traffic counters of these launches are
+    what a counter reads for a known number of bytes."""
+    import torch
+    n = 1 << 28
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(4):
+        torch.neg(a, out=b)
+    torch.cuda.synchronize()
+    assert float(b[-1]) == -1.0
+    return {"calibration_kernel": "torch.neg float32, 2^28 elements", "bytes_read": n * 4,
+            "bytes_written": n * 4, "launches": 4}
+
+
 def cpu_baseline(wl, pool_np, stride, logits, xs, steps_range, budget_s):
     """The oracle as it stands (route, integer plan, fp64 expert FFN, merge),
     on the same calls in order, until the time budget is spent."""
@@ -176,6 +195,9 @@ def main():
 
     if a.prefill_only:
         print(json.dumps(bench_prefill()), flush=True)
+        return
+    if a.copy_calibration:
+        print(json.dumps(copy_calibration()), flush=True)
         return
     wl = {w.name: w for w in W.WORKLOADS}[a.workload]
     assert not wl.prefill, "decode workloads only"
