@@ -19,7 +19,8 @@ BUILD = os.path.join(ROOT, "_build")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 HIPCC = os.path.join(ROCM, "bin", "hipcc")
 
-HIP_SOURCES = ["route.hip", "plan.hip", "decode.hip", "prefill.hip", "ctx.cpp"]
+HIP_SOURCES = ["route.hip", "plan.hip", "decode.hip", "ffn_f32.hip", "ffn_bf16.hip", "ffn_mx.hip",
+               "prefill.hip", "ctx.cpp"]
 HOST_SOURCES = ["cpu_branch.cpp"]
 HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-Wall",
              "-Wno-unused-function", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -303,6 +303,7 @@ extern "C" moe_status moe_create(const moe_config* cfg, void* host_pool, size_t 
            o_fo = take(4 * ctx->kmax);
     size_t o_cpu = take(4 * ctx->umax), o_gu = take(4 * ctx->umax), o_gs = take(4 * ctx->umax);
     size_t o_sm = take(4 * maxTk);
+    size_t o_fd = take(4 * (size_t)kFfnDoneStride * kFfnSub * ctx->umax);
     ALLOC(ctx->plan_alloc, off);
     uint8_t* b = ctx->plan_alloc;
     PlanBufs& p = ctx->plan;
@@ -318,6 +319,7 @@ extern "C" moe_status moe_create(const moe_config* cfg, void* host_pool, size_t 
     p.gpu_u = (int32_t*)(b + o_gu);
     p.gpu_slot = (int32_t*)(b + o_gs);
     p.slot_map = (int32_t*)(b + o_sm);
+    p.ffn_done = (int32_t*)(b + o_fd);
     p.hblock_bytes = sizeof(HostBlockHeader) + 2 * 4 * (size_t)maxTk;
     p.x_offset = (p.hblock_bytes + 255) / 256 * 256;
     p.act_bytes = dtype_bytes(cfg->act_dtype);
@@ -361,6 +363,7 @@ extern "C" moe_status moe_create(const moe_config* cfg, void* host_pool, size_t 
     (void)hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, ctx->device);
     if (khz <= 0) khz = 100000;
     ctx->wait_ticks = (uint64_t)khz * 1000ull * 10ull;  // the merge waits at most 10 s
+    ctx->ffn_wait_ticks = (uint64_t)khz * 1000ull;      // an FFN down item waits at most 1 s
   }
 
   // empty tables, tick 0
@@ -503,7 +506,9 @@ extern "C" moe_status moe_ctx_timing(moe_ctx* ctx, moe_timing* out, int32_t rese
   do {                                                                        \
     if (!(ctx)) return fail(nullptr, MOE_EINVAL, "context is NULL");          \
     if ((ctx)->sync && ((volatile HostSync*)(ctx)->sync)->error && (ctx)->err == MOE_OK) \
-      fail((ctx), MOE_EHIP, "merge gave up waiting for the host branch (10 s limit)"); \
+      fail((ctx), MOE_EHIP, ((volatile HostSync*)(ctx)->sync)->error == 2                \
+                                ? "expert FFN gave up waiting for its gate/up items (1 s limit)" \
+                                : "merge gave up waiting for the host branch (10 s limit)");      \
     if ((ctx)->err != MOE_OK) {                                               \
       set_last_error((ctx)->err_msg);                                         \
       return (ctx)->err;                                                      \

@@ -1,0 +1,514 @@
+// Decode expert FFN: one launch per layer call over every GPU-resident routed
+// expert of the last plan (snackonai, "The Code, Annotated": grouped
+// evaluation after the cache update and the batched copy).
+//
+// Decode reads each routed expert's complete weights once per call, so the
+// launch is an HBM stream with a dependency in the middle: the down
+// projection of an expert needs its whole SiLU(gate) * up intermediate.  One
+// grid holds both halves:
+//   * gate/up items (the first waves of the grid, expert by expert): RW_A rows
+//     of W_gate and W_up of one expert.  The wave finds its expert's first
+//     routed pair and requests that token's inputs, then loads its weight rows
+//     into registers (lane l holds 16-byte chunks l, l+64, ... of each row),
+//     evaluates every routed token of the expert, reduces the rows across the
+//     wave, stores h = silu(g) * u (fp32) per token and bumps the expert's
+//     counter;
+//   * down items (the later workgroups, four row blocks of one expert each):
+//     RW_B rows of W_down per wave.  The waves load their rows first (they
+//     stream behind the gate/up weights), one wave waits for the expert's
+//     counters to be complete, the workgroup stages h of each routed pair in
+//     LDS, and every wave writes its fp32 partial rows.
+// Memory serves requests roughly in issue order, so the gate/up halves
+// finish while the down weights are still streaming and the wait is mostly
+// already over when a down wave gets its data.  Workgroups are dispatched in
+// index order and every gate/up item precedes every down item, so a waiting
+// down item only waits for items that are already running; the wait is still
+// bounded (wall clock) and flags an error instead of hanging.  The control
+// kernel zeroes the counters of each call.
+//
+// The intermediate crosses compute dies (each XCD has its own L2), so it
+// moves with device-coherent accesses instead of cache-wide fences: the
+// gate/up wave stores h with device scope, waits for its stores to complete,
+// then bumps one of its expert's counters; the down workgroup polls the
+// counters with device-scope loads and reads h with device-scope vector
+// loads (buffer loads with the device-scope cache policy), rather than an L2
+// write-back and invalidate paid by every wave.  Gate/up items spread their
+// counts over several counters on separate lines: same-address atomics from
+// hundreds of waves queue behind each other.
+//
+// Arithmetic: bf16 x bf16 uses the two-term bf16 dot with fp32 accumulation;
+// MXFP4 weights are expanded with the gfx950 scaled FP4 converts (to bf16
+// pairs against bf16 activations, to fp32 pairs against fp32 inputs), the
+// E8M0 scale applied in the convert; everything accumulates in fp32.  Row
+// totals use a transpose reduction: at each xor step a lane keeps half of its
+// values and sends the other half, so R rows cost R - 1 + 6 - log2(R)
+// shuffles instead of 6 R.
+#pragma once
+
+#include <algorithm>
+#include <type_traits>
+
+#include "internal.h"
+
+namespace moert {
+
+typedef __bf16 ffn_bf16x2 __attribute__((ext_vector_type(2)));
+typedef float ffn_f32x2 __attribute__((ext_vector_type(2)));
+
+struct FfnArgs {
+  const uint8_t* slot_base;
+  size_t stride;
+  const moe_plan_counts* counts;
+  const int32_t* gpu_slot;    // [n_gpu] slot of each GPU-resident routed expert
+  const int32_t* slot_map;    // [Tk] slot of each (token, rank) pair, -1 = host
+  int Tk, k, H, I;
+  size_t og, ou, od;          // byte offsets of W_gate, W_up, W_down (codes for MXFP4)
+  size_t sg, su, sd;          // byte offsets of their E8M0 scales (MXFP4)
+  const void* x;              // [T][H] activations
+  float* h;                   // [Tk][I] fp32 intermediate
+  uint32_t h_bytes;           // bytes of h (buffer descriptor range)
+  float* p;                   // [Tk][H] fp32 partial rows
+  int32_t* done;              // [umax] finished gate/up items per GPU expert
+  HostSync* sync;             // error word (2 = a down item gave up waiting)
+  uint64_t wait_ticks;
+  int umax;
+  int itemsA, itemsB;         // row blocks per expert
+  int blocksA;                // workgroups of gate/up items
+  int blocksB;                // down workgroups per expert
+  int cplA, cplB;             // 16-byte chunks per lane per row
+};
+
+template <int WT> struct FfnChunk;
+template <> struct FfnChunk<MOE_F32> { static constexpr int CH = 4; };
+template <> struct FfnChunk<MOE_BF16> { static constexpr int CH = 8; };
+template <> struct FfnChunk<MOE_MXFP4> { static constexpr int CH = 32; };
+
+constexpr int kCpolDevice = 16;  // SC1: device-scope coherent buffer access
+
+// chunk slots per lane: gate/up items hold kRegA per matrix, down items kRegB
+constexpr int kRegA = 8;
+template <int WT> struct FfnRegB { static constexpr int N = WT == MOE_MXFP4 ? 8 : 16; };
+
+__device__ inline float ffn_bf_lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ inline float ffn_bf_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
+
+// OCP MX E8M0: 2^(s - 127); s = 0 is 2^-127 (a float subnormal).
+__device__ inline float ffn_e8m0(uint32_t s) {
+  return s ? __uint_as_float(s << 23) : __uint_as_float(0x00400000u);
+}
+
+struct WChunk16 {
+  uint4 v;     // 16 raw bytes
+  uint32_t s;  // E8M0 scale byte (MXFP4)
+};
+
+// An empty asm that claims to rewrite the chunk: keeps the compiler from
+// hoisting its expansion (bf16 or FP4 to fp32) out of the token loop, which
+// would hold every weight in fp32 registers and cut occupancy.
+template <int WT>
+__device__ inline void ffn_pin(WChunk16& c) {
+  asm volatile("" : "+v"(c.v.x), "+v"(c.v.y), "+v"(c.v.z), "+v"(c.v.w));
+  if constexpr (WT == MOE_MXFP4) asm volatile("" : "+v"(c.s));
+}
+
+template <int WT>
+__device__ inline WChunk16 ffn_load_w(const uint8_t* __restrict__ mat, const uint8_t* __restrict__ sc,
+                                      int row, int K, int ch) {
+  WChunk16 c;
+  if constexpr (WT == MOE_F32) {
+    c.v = *(const uint4*)(mat + ((size_t)row * K + (size_t)ch * 4) * 4);
+    c.s = 127;
+  } else if constexpr (WT == MOE_BF16) {
+    c.v = *(const uint4*)(mat + ((size_t)row * K + (size_t)ch * 8) * 2);
+    c.s = 127;
+  } else {
+    c.v = *(const uint4*)(mat + (size_t)row * (K / 2) + (size_t)ch * 16);
+    c.s = sc[(size_t)row * (K / 32) + ch];
+  }
+  return c;
+}
+
+// The input values matching one weight chunk, as 32-bit words.
+template <int WT, int XT> struct XWords {
+  static constexpr int N = FfnChunk<WT>::CH * (XT == MOE_F32 ? 4 : 2) / 4;
+  uint32_t w[N];
+};
+
+template <int WT, int XT>
+__device__ inline void ffn_load_x(const void* __restrict__ x, size_t elem0, int ch, XWords<WT, XT>& o) {
+  constexpr int CH = FfnChunk<WT>::CH;
+  constexpr int EB = XT == MOE_F32 ? 4 : 2;
+  constexpr int N = XWords<WT, XT>::N;
+  const uint8_t* p = (const uint8_t*)x + (elem0 + (size_t)ch * CH) * EB;
+  if constexpr (N % 4 == 0) {
+#pragma unroll
+    for (int i = 0; i < N / 4; ++i) {
+      const uint4 v = ((const uint4*)p)[i];
+      o.w[4 * i] = v.x; o.w[4 * i + 1] = v.y; o.w[4 * i + 2] = v.z; o.w[4 * i + 3] = v.w;
+    }
+  } else {
+    const uint2 v = *(const uint2*)p;
+    o.w[0] = v.x; o.w[1] = v.y;
+  }
+}
+
+template <int SEL, int XT>
+__device__ inline float ffn_mx_pair(uint32_t word, float scale, const uint32_t* xw, float acc) {
+  // elements 2*SEL and 2*SEL+1 of this word's eight (low nibble = even)
+  if constexpr (XT == MOE_BF16) {
+    const ffn_bf16x2 wp = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, scale, SEL);
+    return __builtin_amdgcn_fdot2_f32_bf16(wp, __builtin_bit_cast(ffn_bf16x2, xw[SEL]), acc, false);
+  } else {
+    const ffn_f32x2 wp = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, scale, SEL);
+    acc = fmaf(wp[0], __uint_as_float(xw[2 * SEL]), acc);
+    return fmaf(wp[1], __uint_as_float(xw[2 * SEL + 1]), acc);
+  }
+}
+
+// acc + <weight chunk, input chunk>
+template <int WT, int XT>
+__device__ inline float ffn_dot(const WChunk16& c, const XWords<WT, XT>& x, float acc) {
+  const uint32_t w[4] = {c.v.x, c.v.y, c.v.z, c.v.w};
+  if constexpr (WT == MOE_F32) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float xv;
+      if constexpr (XT == MOE_F32) xv = __uint_as_float(x.w[i]);
+      else xv = (i & 1) ? ffn_bf_hi(x.w[i >> 1]) : ffn_bf_lo(x.w[i >> 1]);
+      acc = fmaf(__uint_as_float(w[i]), xv, acc);
+    }
+  } else if constexpr (WT == MOE_BF16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if constexpr (XT == MOE_BF16) {
+        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(ffn_bf16x2, w[i]),
+                                              __builtin_bit_cast(ffn_bf16x2, x.w[i]), acc, false);
+      } else {
+        acc = fmaf(ffn_bf_lo(w[i]), __uint_as_float(x.w[2 * i]), acc);
+        acc = fmaf(ffn_bf_hi(w[i]), __uint_as_float(x.w[2 * i + 1]), acc);
+      }
+    }
+  } else {
+    const float s = ffn_e8m0(c.s);
+    constexpr int XPW = XT == MOE_BF16 ? 4 : 8;  // input words per weight word
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t* xw = x.w + XPW * i;
+      acc = ffn_mx_pair<0, XT>(w[i], s, xw, acc);
+      acc = ffn_mx_pair<1, XT>(w[i], s, xw, acc);
+      acc = ffn_mx_pair<2, XT>(w[i], s, xw, acc);
+      acc = ffn_mx_pair<3, XT>(w[i], s, xw, acc);
+    }
+  }
+  return acc;
+}
+
+// Transpose reduction of N values across the wave (N a power of two <= 64),
+// starting at xor offset O.  Afterwards lane l holds the wave total of value
+// l >> (6 - log2 N) in v[0].
+template <int N>
+__device__ inline void ffn_xreduce(float* v, int lane, int o) {
+  if constexpr (N > 1) {
+    constexpr int HN = N / 2;
+    const bool up = (lane & o) != 0;
+#pragma unroll
+    for (int i = 0; i < HN; ++i) {
+      const float send = up ? v[i] : v[i + HN];
+      const float keep = up ? v[i + HN] : v[i];
+      v[i] = keep + __shfl_xor(send, o);
+    }
+    ffn_xreduce<HN>(v, lane, o >> 1);
+  } else {
+    for (; o >= 1; o >>= 1) v[0] += __shfl_xor(v[0], o);
+  }
+}
+
+template <int N> struct Log2 { static constexpr int v = 1 + Log2<N / 2>::v; };
+template <> struct Log2<1> { static constexpr int v = 0; };
+
+// Next routed pair of `slot` (ascending pair index), or -1.  `base` / `bm`
+// carry the wave's position in slot_map between calls (wave-uniform).
+__device__ inline int ffn_next_pair(const FfnArgs& a, int slot, int lane, int& base, uint64_t& bm) {
+  while (bm == 0 && base + 64 < a.Tk) {
+    base += 64;
+    bm = __ballot(base + lane < a.Tk && a.slot_map[base + lane] == slot);
+  }
+  if (bm == 0) return -1;
+  const int p = base + __builtin_ctzll(bm);
+  bm &= bm - 1;
+  return p;
+}
+
+__device__ inline float ffn_silu(float g) { return g / (1.f + expf(-g)); }
+
+template <int WT, int XT, int CPL>
+__device__ void ffn_gate_up(const FfnArgs& a, int g, int rb, int lane) {
+  constexpr int CH = FfnChunk<WT>::CH;
+  constexpr int RW = kRegA / CPL;
+  const int K = a.H, nch = K / CH, row0 = rb * RW;
+
+  // the slot and its first routed pair come first, so that pair's inputs
+  // are requested ahead of the weights and arrive with them
+  const int sm0 = lane < a.Tk ? a.slot_map[lane] : -2;
+  const int slot = __builtin_amdgcn_readfirstlane(a.gpu_slot[g]);
+  int base = 0;
+  uint64_t bm = __ballot(sm0 == slot);
+  int p = ffn_next_pair(a, slot, lane, base, bm);
+  XWords<WT, XT> xw[CPL];
+  if (p >= 0) {
+#pragma unroll
+    for (int c = 0; c < CPL; ++c)
+      ffn_load_x<WT, XT>(a.x, (size_t)(p / a.k) * K, min(lane + 64 * c, nch - 1), xw[c]);
+  }
+
+  // every lane loads (chunks past the row end read a valid chunk and are
+  // zeroed), so the loads issue back to back without branches
+  const uint8_t* sp = a.slot_base + (size_t)slot * a.stride;
+  WChunk16 wg[RW][CPL], wu[RW][CPL];
+#pragma unroll
+  for (int r = 0; r < RW; ++r) {
+    const int row = min(row0 + r, a.I - 1);
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      const int ch = min(lane + 64 * c, nch - 1);
+      wg[r][c] = ffn_load_w<WT>(sp + a.og, sp + a.sg, row, K, ch);
+      wu[r][c] = ffn_load_w<WT>(sp + a.ou, sp + a.su, row, K, ch);
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) {
+    if (64 * (c + 1) > nch) {  // uniform: only a partial last column of chunks
+      const bool ok = lane + 64 * c < nch;
+#pragma unroll
+      for (int r = 0; r < RW; ++r) {
+        if (!ok) wg[r][c].v = wu[r][c].v = make_uint4(0, 0, 0, 0);
+      }
+    }
+  }
+
+  while (p >= 0) {
+#pragma unroll
+    for (int r = 0; r < RW; ++r)
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) {
+        ffn_pin<WT>(wg[r][c]);
+        ffn_pin<WT>(wu[r][c]);
+      }
+    float v[2 * RW];
+#pragma unroll
+    for (int i = 0; i < 2 * RW; ++i) v[i] = 0.f;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c)
+#pragma unroll
+      for (int r = 0; r < RW; ++r) {
+        v[r] = ffn_dot<WT, XT>(wg[r][c], xw[c], v[r]);
+        v[RW + r] = ffn_dot<WT, XT>(wu[r][c], xw[c], v[RW + r]);
+      }
+    // gate totals land in lanes 0..31, up totals in lanes 32..63
+    ffn_xreduce<2 * RW>(v, lane, 32);
+    const float up = __shfl_xor(v[0], 32);
+    constexpr int SH = 6 - Log2<2 * RW>::v;
+    const int r = lane >> SH;
+    if (lane < 32 && (lane & ((1 << SH) - 1)) == 0 && row0 + r < a.I)
+      __hip_atomic_store(a.h + (size_t)p * a.I + row0 + r, ffn_silu(v[0]) * up, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    p = ffn_next_pair(a, slot, lane, base, bm);
+    if (p >= 0) {
+#pragma unroll
+      for (int c = 0; c < CPL; ++c)
+        ffn_load_x<WT, XT>(a.x, (size_t)(p / a.k) * K, min(lane + 64 * c, nch - 1), xw[c]);
+    }
+  }
+  // publish: this wave's device-scope stores complete, then the count
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  if (lane == 0)
+    __hip_atomic_fetch_add(a.done + (g * kFfnSub + rb % kFfnSub) * kFfnDoneStride, 1,
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Down items run as whole workgroups of one expert (four row blocks): wave
+// 0 waits for the expert's gate/up counters, then the workgroup stages h of
+// each routed pair in LDS once and every wave reads its chunks from there.
+template <int WT, int CPL>
+__device__ void ffn_down(const FfnArgs& a, int g, int rb, int lane, float* lds_h) {
+  constexpr int CH = FfnChunk<WT>::CH;
+  constexpr int RW = FfnRegB<WT>::N / CPL;
+  typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+  const int slot = __builtin_amdgcn_readfirstlane(a.gpu_slot[g]);
+  const uint8_t* sp = a.slot_base + (size_t)slot * a.stride;
+  const int K = a.I, nch = K / CH, row0 = rb * RW;
+
+  // the weights do not depend on h: load them before waiting (row blocks
+  // past the end, which pad the workgroup, read the last row and write nothing)
+  WChunk16 wd[RW][CPL];
+#pragma unroll
+  for (int r = 0; r < RW; ++r) {
+    const int row = min(row0 + r, a.H - 1);
+#pragma unroll
+    for (int c = 0; c < CPL; ++c)
+      wd[r][c] = ffn_load_w<WT>(sp + a.od, sp + a.sd, row, K, min(lane + 64 * c, nch - 1));
+  }
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) {
+    if (64 * (c + 1) > nch) {
+      const bool ok = lane + 64 * c < nch;
+#pragma unroll
+      for (int r = 0; r < RW; ++r) {
+        if (!ok) wd[r][c].v = make_uint4(0, 0, 0, 0);
+      }
+    }
+  }
+
+  // wave 0 waits: lanes 0..kFfnSub-1 each watch one sub-counter of the expert
+  if (threadIdx.x < 64) {
+    const uint64_t t0 = wall_clock64();
+    const int sub = lane < kFfnSub ? lane : 0;
+    const int want = (a.itemsA - sub + kFfnSub - 1) / kFfnSub;
+    const int32_t* ctr = a.done + (g * kFfnSub + sub) * kFfnDoneStride;
+    for (;;) {
+      const bool ok = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= want;
+      if (__ballot(ok || lane >= kFfnSub) == ~0ull) break;
+      if (wall_clock64() - t0 > a.wait_ticks) {
+        if (lane == 0) __hip_atomic_store(&a.sync->error, 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(8);
+    }
+  }
+  __syncthreads();  // h is read only after the count is complete
+  const __amdgpu_buffer_rsrc_t hr = __builtin_amdgcn_make_buffer_rsrc(a.h, 0, a.h_bytes, 0x00020000);
+
+  int base = 0;
+  uint64_t bm = __ballot(lane < a.Tk && a.slot_map[lane] == slot);
+  for (;;) {
+    const int p = ffn_next_pair(a, slot, lane, base, bm);  // uniform in the workgroup
+    if (p < 0) break;
+    __syncthreads();  // the previous pair's reads of LDS are done
+    for (int i = threadIdx.x; i < K / 4; i += blockDim.x) {
+      const u32x4v v = __builtin_amdgcn_raw_buffer_load_b128(hr, (int)(((size_t)p * K + 4 * i) * 4), 0,
+                                                             kCpolDevice);
+      ((u32x4v*)lds_h)[i] = v;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < RW; ++r)
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) ffn_pin<WT>(wd[r][c]);
+    float v[RW];
+#pragma unroll
+    for (int i = 0; i < RW; ++i) v[i] = 0.f;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      XWords<WT, MOE_F32> hw;
+      const int ch = min(lane + 64 * c, nch - 1);
+#pragma unroll
+      for (int i = 0; i < CH / 4; ++i) {
+        const u32x4v q = ((const u32x4v*)lds_h)[ch * (CH / 4) + i];
+        hw.w[4 * i] = q[0]; hw.w[4 * i + 1] = q[1]; hw.w[4 * i + 2] = q[2]; hw.w[4 * i + 3] = q[3];
+      }
+#pragma unroll
+      for (int r = 0; r < RW; ++r) v[r] = ffn_dot<WT, MOE_F32>(wd[r][c], hw, v[r]);
+    }
+    ffn_xreduce<RW>(v, lane, 32);
+    constexpr int SH = 6 - Log2<RW>::v;
+    const int r = lane >> SH;
+    if ((lane & ((1 << SH) - 1)) == 0 && row0 + r < a.H) a.p[(size_t)p * a.H + row0 + r] = v[0];
+  }
+}
+
+// One kernel per (format, activation type, chunks per lane of the two
+// contraction lengths), so each holds only the registers its shape needs.
+template <int WT, int XT, int CPLA, int CPLB>
+__global__ __launch_bounds__(256) void ffn_kernel(FfnArgs a) {
+  extern __shared__ float lds_h[];  // [I] h of one pair (down workgroups)
+  const int lane = threadIdx.x & 63;
+  // wave-uniform values held in scalar registers: slot addresses then go in
+  // the scalar base of each load, the per-lane part in a 32-bit offset
+  const int wave = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
+  const int n_gpu = a.counts->n_gpu;
+  if ((int)blockIdx.x < a.blocksA) {
+    const int g = wave / a.itemsA;
+    if (g < n_gpu && g < a.umax) ffn_gate_up<WT, XT, CPLA>(a, g, wave - g * a.itemsA, lane);
+  } else {
+    // whole workgroups of one expert, four row blocks each
+    const int b = (int)blockIdx.x - a.blocksA;
+    const int g = b / a.blocksB;
+    const int rb = (b - g * a.blocksB) * 4 + (int)(threadIdx.x >> 6);
+    if (g < n_gpu && g < a.umax) ffn_down<WT, CPLB>(a, g, rb, lane, lds_h);
+  }
+}
+
+// chunks per lane for a row of nch 16-byte chunks (nch <= 512)
+inline int ffn_cpl(int nch) { return nch <= 64 ? 1 : nch <= 128 ? 2 : nch <= 256 ? 4 : 8; }
+
+template <int WT>
+hipError_t launch_ffn_typed(moe_ctx* ctx, const void* x, int T, hipStream_t s) {
+  constexpr int CH = FfnChunk<WT>::CH;
+  const moe_config& c = ctx->cfg;
+  const int H = c.hidden, I = c.inter;
+  FfnArgs a{};
+  a.slot_base = ctx->pool.base;
+  a.stride = ctx->stride;
+  a.counts = ctx->plan.counts;
+  a.gpu_slot = ctx->plan.gpu_slot;
+  a.slot_map = ctx->plan.slot_map;
+  a.Tk = T * c.top_k;
+  a.k = c.top_k;
+  a.H = H;
+  a.I = I;
+  if constexpr (WT == MOE_MXFP4) {
+    a.og = 0;
+    a.ou = (size_t)I * H / 2;
+    a.od = (size_t)I * H;
+    a.sg = 3 * (size_t)H * I / 2;
+    a.su = a.sg + (size_t)I * H / 32;
+    a.sd = a.su + (size_t)I * H / 32;
+  } else {
+    const size_t eb = WT == MOE_F32 ? 4 : 2;
+    a.og = 0;
+    a.ou = (size_t)I * H * eb;
+    a.od = 2 * (size_t)I * H * eb;
+  }
+  a.x = x;
+  a.h = ctx->h_mid;
+  a.h_bytes = (uint32_t)(sizeof(float) * (size_t)ctx->cfg.max_tokens * c.top_k * I);
+  a.p = ctx->p_gpu;
+  a.done = ctx->plan.ffn_done;
+  a.sync = ctx->sync_dev;
+  a.wait_ticks = ctx->ffn_wait_ticks;
+  a.umax = ctx->umax;
+  a.cplA = ffn_cpl(H / CH);
+  a.cplB = ffn_cpl(I / CH);
+  const int rwA = kRegA / a.cplA, rwB = FfnRegB<WT>::N / a.cplB;
+  a.itemsA = (I + rwA - 1) / rwA;
+  a.itemsB = (H + rwB - 1) / rwB;
+  a.blocksA = (int)(((int64_t)a.umax * a.itemsA + 3) / 4);
+  a.blocksB = (a.itemsB + 3) / 4;
+  const dim3 grid((unsigned)(a.blocksA + (int64_t)a.umax * a.blocksB)), block(256);
+  const size_t lds = sizeof(float) * (size_t)I;
+  auto go = [&](auto xt, auto ca, auto cb) {
+    hipLaunchKernelGGL((ffn_kernel<WT, decltype(xt)::value, decltype(ca)::value, decltype(cb)::value>),
+                       grid, block, lds, s, a);
+  };
+  auto by_b = [&](auto xt, auto ca) {
+    switch (a.cplB) {
+      case 1: go(xt, ca, std::integral_constant<int, 1>{}); break;
+      case 2: go(xt, ca, std::integral_constant<int, 2>{}); break;
+      case 4: go(xt, ca, std::integral_constant<int, 4>{}); break;
+      default: go(xt, ca, std::integral_constant<int, 8>{}); break;
+    }
+  };
+  auto by_a = [&](auto xt) {
+    switch (a.cplA) {
+      case 1: by_b(xt, std::integral_constant<int, 1>{}); break;
+      case 2: by_b(xt, std::integral_constant<int, 2>{}); break;
+      case 4: by_b(xt, std::integral_constant<int, 4>{}); break;
+      default: by_b(xt, std::integral_constant<int, 8>{}); break;
+    }
+  };
+  if (c.act_dtype == MOE_F32) by_a(std::integral_constant<int, MOE_F32>{});
+  else by_a(std::integral_constant<int, MOE_BF16>{});
+  return hipGetLastError();
+}
+
+}  // namespace moert

@@ -18,6 +18,11 @@ constexpr int kMaxTopK = 32;
 constexpr int kMaxSlots = 32768;
 constexpr int kMaxDecodeTokens = 256;
 constexpr int kPlanThreads = 1024;
+// expert FFN completion counters: kFfnSub per GPU expert (gate/up item rb
+// counts into sub-counter rb % kFfnSub), each on its own 256-byte line, so
+// that same-address atomics do not queue behind each other
+constexpr int kFfnSub = 8;
+constexpr int kFfnDoneStride = 64;
 
 // Device-resident scalars the control kernel owns: the LRU tick and the
 // running counters of the pool table.
@@ -52,6 +57,7 @@ struct PlanBufs {
   moe_plan_counts* counts;
   int32_t *uniq, *hits, *misses, *victims, *fill_u, *fill_slot, *fill_old;
   int32_t *cpu_u, *gpu_u, *gpu_slot, *slot_map;
+  int32_t* ffn_done;      // [umax * kFfnSub * kFfnDoneStride] gate/up items finished
   // host block in pinned, device-mapped memory, written by the control kernel:
   // header | ids[maxTk] | slot_map[maxTk] | x[max_tokens][H] (act dtype)
   uint8_t* hblock;        // device address of the mapping
@@ -135,6 +141,7 @@ struct moe_ctx {
   moert::HostSync* sync_dev = nullptr;    // device address
   int64_t call_seq = 0;                   // doorbell value of the current call
   uint64_t wait_ticks = 0;                // merge's wait limit in wall-clock ticks
+  uint64_t ffn_wait_ticks = 0;            // expert FFN down items' wait limit
 
   hipStream_t copy = nullptr;  // prefill transfers
 
@@ -191,6 +198,9 @@ hipError_t launch_plan(moe_ctx* ctx, int layer, const int32_t* ids, int T, const
                        int64_t seq, hipStream_t s);
 hipError_t launch_fill(moe_ctx* ctx, hipStream_t s);
 hipError_t launch_ffn(moe_ctx* ctx, const void* x, int T, hipStream_t s);
+hipError_t launch_ffn_f32(moe_ctx* ctx, const void* x, int T, hipStream_t s);
+hipError_t launch_ffn_bf16(moe_ctx* ctx, const void* x, int T, hipStream_t s);
+hipError_t launch_ffn_mx(moe_ctx* ctx, const void* x, int T, hipStream_t s);
 hipError_t launch_merge(moe_ctx* ctx, const float* w, int T, void* y, int64_t seq, hipStream_t s);
 hipError_t launch_prefill_admit(moe_ctx* ctx, int layer, hipStream_t s);
 hipError_t launch_prefill_compute(moe_ctx* ctx, int layer, const void* x, int T,

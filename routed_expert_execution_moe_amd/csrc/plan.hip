@@ -29,6 +29,7 @@ struct PlanArgs {
   const uint8_t* x;     // activations [T][H], act dtype
   int64_t x_bytes;      // T * H * element bytes
   int32_t T, k, layer, E, K, n, mode, max_fetch;
+  int32_t umax;         // plan list bound; the FFN counters to clear
   int64_t bwp, bwh;
   int32_t* id2slot;
   int32_t* slot2id;
@@ -82,6 +83,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   if (tid < kMaxExperts / 32) s_mask[tid] = 0;
   for (int i = tid; i < (n + 31) / 32; i += kPlanThreads) s_hitbits[i] = 0;
   if (tid < E) s_eslot[tid] = -1;
+  for (int i = tid; i < a.umax * kFfnSub; i += kPlanThreads)
+    pb.ffn_done[i * kFfnDoneStride] = 0;  // the expert FFN counts from zero
   if (tid == 0) {
     s_tick = a.st->tick + 1;
     s_evict = 0;
@@ -377,6 +380,7 @@ hipError_t launch_plan(moe_ctx* ctx, int layer, const int32_t* ids, int T, const
   K = std::min<int64_t>(K, a.n);
   if (ctx->cfg.max_fetch > 0) K = std::min<int64_t>(K, ctx->cfg.max_fetch);
   a.K = (int32_t)K;
+  a.umax = ctx->umax;
   a.mode = ctx->cfg.mode;
   a.max_fetch = ctx->cfg.max_fetch;
   a.bwp = ctx->cfg.bw_pcie_mbps;
