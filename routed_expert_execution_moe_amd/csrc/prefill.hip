@@ -146,8 +146,8 @@ template <bool GLU>
 __global__ __launch_bounds__(kGemmThreads, 2) void grouped_gemm_kernel(GemmArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t s_a[2][kBM * kRowBytes];   // 2 x 16 KB bf16
   __shared__ __attribute__((aligned(16))) uint8_t s_b[2][kBN * 32];          // 2 x 8 KB fp4 codes
-  __shared__ uint8_t s_s[2][kBN * 2];                                        // 2 x 512 B scales
-  __shared__ int32_t s_rowsrc[kBM];  // A source row per tile row, -1 = padding
+  __shared__ float s_s[2][kBN * 2];                                          // 2 x 2 KB scales
+  __shared__ int32_t s_rowsrc[kBM];  // A source row per tile row
 
   // XCD-aware mapping: consecutive workgroups go round-robin over 8 XCDs;
   // give every N-tile of one M-tile to the same XCD.
@@ -164,10 +164,11 @@ __global__ __launch_bounds__(kGemmThreads, 2) void grouped_gemm_kernel(GemmArgs 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
 
+  // rows past the expert's end (padding of the last M-tile) read the tile's
+  // first row: no masked loads, and their results are never written
   if (tid < kBM) {
-    int src = -1;
-    if (tid < rows) src = GLU ? a.perm[pos0 + tid] / a.k : pos0 + tid;
-    s_rowsrc[tid] = src;
+    const int r = tid < rows ? tid : 0;
+    s_rowsrc[tid] = GLU ? a.perm[pos0 + r] / a.k : pos0 + r;
   }
   __syncthreads();
 
@@ -200,34 +201,36 @@ __global__ __launch_bounds__(kGemmThreads, 2) void grouped_gemm_kernel(GemmArgs 
     b_codes = slot + coff + (size_t)mrow * (K / 2);
     b_scales = slot + soff + (size_t)mrow * (K / 32);
   }
-  int a_src_row[4];
+  const uint16_t* a_rows[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) a_src_row[i] = s_rowsrc[(tid >> 3) + 32 * i];
+  for (int i = 0; i < 4; ++i)
+    a_rows[i] = a.a_src + (size_t)s_rowsrc[(tid >> 3) + 32 * i] * K + a_chunk * 8;
 
-  uint4 pa[4];
-  uint4 pb[2];
+  // next K step in registers (named, so they stay in registers)
+  uint4 pa0, pa1, pa2, pa3, pb0, pb1;
   uint32_t ps;
-  auto load_k = [&](int kt) {
-    const int k0 = kt * kBK;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (a_src_row[i] >= 0)
-        pa[i] = *(const uint4*)(a.a_src + (size_t)a_src_row[i] * K + k0 + a_chunk * 8);
-      else
-        pa[i] = make_uint4(0, 0, 0, 0);
-    }
-    pb[0] = *(const uint4*)(b_codes + (k0 >> 1));
-    pb[1] = *(const uint4*)(b_codes + (k0 >> 1) + 16);
-    ps = *(const uint16_t*)(b_scales + (k0 >> 5));
-  };
-  auto store_k = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) *(uint4*)(&s_a[buf][swz((tid >> 3) + 32 * i, a_chunk)]) = pa[i];
-    const uint32_t w[8] = {pb[0].x, pb[0].y, pb[0].z, pb[0].w, pb[1].x, pb[1].y, pb[1].z, pb[1].w};
-#pragma unroll
-    for (int q = 0; q < 8; ++q) *(uint32_t*)(&s_b[buf][bswz(b_row, q)]) = w[q];
-    *(uint16_t*)(&s_s[buf][b_row * 2]) = (uint16_t)ps;
-  };
+#define MOERT_LOAD_K(kt)                                        \
+  do {                                                          \
+    const int k0_ = (kt) * kBK;                                 \
+    pa0 = *(const uint4*)(a_rows[0] + k0_);                     \
+    pa1 = *(const uint4*)(a_rows[1] + k0_);                     \
+    pa2 = *(const uint4*)(a_rows[2] + k0_);                     \
+    pa3 = *(const uint4*)(a_rows[3] + k0_);                     \
+    pb0 = *(const uint4*)(b_codes + (k0_ >> 1));                \
+    pb1 = *(const uint4*)(b_codes + (k0_ >> 1) + 16);           \
+    ps = *(const uint16_t*)(b_scales + (k0_ >> 5));             \
+  } while (0)
+#define MOERT_STORE_K(buf)                                                                    \
+  do {                                                                                        \
+    *(uint4*)(&s_a[buf][swz((tid >> 3), a_chunk)]) = pa0;                                     \
+    *(uint4*)(&s_a[buf][swz((tid >> 3) + 32, a_chunk)]) = pa1;                                \
+    *(uint4*)(&s_a[buf][swz((tid >> 3) + 64, a_chunk)]) = pa2;                                \
+    *(uint4*)(&s_a[buf][swz((tid >> 3) + 96, a_chunk)]) = pa3;                                \
+    const uint32_t w_[8] = {pb0.x, pb0.y, pb0.z, pb0.w, pb1.x, pb1.y, pb1.z, pb1.w};          \
+    _Pragma("unroll") for (int q = 0; q < 8; ++q)                                             \
+        *(uint32_t*)(&s_b[buf][bswz(b_row, q)]) = w_[q];                                      \
+    *(float2*)(&s_s[buf][b_row * 2]) = make_float2(e8m0_scale(ps & 0xFFu), e8m0_scale(ps >> 8)); \
+  } while (0)
 
   f32x16 acc[2][4];
 #pragma unroll
@@ -245,34 +248,55 @@ __global__ __launch_bounds__(kGemmThreads, 2) void grouped_gemm_kernel(GemmArgs 
   }
   const int lr = lane & 31, kg = lane >> 5;
 
-  load_k(0);
-  store_k(0);
+  // one 16-deep K slice: A fragments (bf16), raw B codes and their scales
+  struct Frag {
+    bf16x8 a[2];
+    uint32_t raw[4];
+    float sc[4];
+  };
+  auto read_frag = [&](int buf, int ks, Frag& f) {
+    const int chunk = ks * 2 + kg;  // A: 16-byte chunk; B: 4-byte word
+#pragma unroll
+    for (int i = 0; i < 2; ++i) f.a[i] = *(const bf16x8*)(&s_a[buf][swz(wm * 64 + i * 32 + lr, chunk)]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = brow[j] + lr;
+      f.raw[j] = *(const uint32_t*)(&s_b[buf][bswz(n, chunk)]);
+      f.sc[j] = s_s[buf][n * 2 + (ks >> 1)];
+    }
+  };
+  auto mma = [&](const Frag& f) {
+    bf16x8 bfr[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) bfr[j] = fp4x8_to_bf16(f.raw[j], f.sc[j]);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], bfr[j], acc[i][j], 0, 0, 0);
+  };
+
+  MOERT_LOAD_K(0);
+  MOERT_STORE_K(0);
   __syncthreads();
   for (int kt = 0; kt < nk; ++kt) {
     const int buf = kt & 1;
-    if (kt + 1 < nk) load_k(kt + 1);
-#pragma unroll
-    for (int ks = 0; ks < kBK / 16; ++ks) {
-      const int chunk = ks * 2 + kg;  // A: 16-byte chunk; B: 4-byte word
-      bf16x8 af[2], bfg[4];
-#pragma unroll
-      for (int i = 0; i < 2; ++i) af[i] = *(const bf16x8*)(&s_a[buf][swz(wm * 64 + i * 32 + lr, chunk)]);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int n = brow[j] + lr;
-        const uint32_t raw = *(const uint32_t*)(&s_b[buf][bswz(n, chunk)]);
-        const float sc = e8m0_scale(s_s[buf][n * 2 + (ks >> 1)]);
-        bfg[j] = fp4x8_to_bf16(raw, sc);
-      }
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfg[j], acc[i][j], 0, 0, 0);
-    }
-    if (kt + 1 < nk) store_k(buf ^ 1);
+    if (kt + 1 < nk) MOERT_LOAD_K(kt + 1);
+    // the next slice's LDS reads are in flight while this slice's MFMAs run
+    Frag f0, f1;
+    read_frag(buf, 0, f0);
+    read_frag(buf, 1, f1);
+    mma(f0);
+    read_frag(buf, 2, f0);
+    mma(f1);
+    read_frag(buf, 3, f1);
+    mma(f0);
+    mma(f1);
+    if (kt + 1 < nk) MOERT_STORE_K(buf ^ 1);
     __syncthreads();
   }
+#undef MOERT_LOAD_K
+#undef MOERT_STORE_K
 
   // epilogue: C element r of lane: row 8*(r/4) + 4*kg + r%4, column lr
 #pragma unroll
@@ -285,7 +309,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void grouped_gemm_kernel(GemmArgs 
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
           const float g = acc[i][j][r], u = acc[i][j + 2][r];
-          const float hv = g / (1.f + expf(-g)) * u;
+          const float hv = g * u * __builtin_amdgcn_rcpf(1.f + __expf(-g));
           uint32_t bits = __float_as_uint(hv);
           bits += 0x7FFFu + ((bits >> 16) & 1u);
           const int col = n0 + wn * 64 + j * 32 + lr;
