@@ -142,11 +142,33 @@ struct GemmArgs {
   int max_mtiles;             // grid bound on M-tiles
 };
 
+// Three LDS stages per workgroup; the global -> LDS copies of K step kt+2
+// are issued (direct-to-LDS loads, no register staging) while step kt is
+// computed, so each copy has two steps of MFMA work to land.  The copies are
+// issued from inline asm, so the compiler does not serialise LDS reads
+// behind them; completion is tracked by hand with the vector-memory counter
+// and a workgroup barrier per step.
+constexpr int kStageA = kBM * kRowBytes;  // 16 KB: 128 rows x 64 bf16, swizzled
+constexpr int kStageB = kBN * 32;         // 8 KB: 256 rows x 64 fp4 codes
+constexpr int kStageS = kBN * 4;          // 1 KB: 4 E8M0 bytes per B row = 2 K steps
+
+// 16 bytes per lane from sbase + voff into LDS at lds + 16 * lane
+__device__ inline void dma16(const void* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               ::"v"(voff), "s"(sbase), "s"(lds) : "memory", "m0");
+}
+// 4 bytes per lane into LDS at lds + 4 * lane
+__device__ inline void dma4(const void* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
+               ::"v"(voff), "s"(sbase), "s"(lds) : "memory", "m0");
+}
+__device__ inline uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)p; }
+
 template <bool GLU>
 __global__ __launch_bounds__(kGemmThreads, 2) void grouped_gemm_kernel(GemmArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t s_a[2][kBM * kRowBytes];   // 2 x 16 KB bf16
-  __shared__ __attribute__((aligned(16))) uint8_t s_b[2][kBN * 32];          // 2 x 8 KB fp4 codes
-  __shared__ float s_s[2][kBN * 2];                                          // 2 x 2 KB scales
+  __shared__ __attribute__((aligned(1024))) uint8_t s_a0[kStageA], s_a1[kStageA], s_a2[kStageA];
+  __shared__ __attribute__((aligned(1024))) uint8_t s_b0[kStageB], s_b1[kStageB], s_b2[kStageB];
+  __shared__ __attribute__((aligned(1024))) uint8_t s_sc[2][kStageS];
   __shared__ int32_t s_rowsrc[kBM];  // A source row per tile row
 
   // XCD-aware mapping: consecutive workgroups go round-robin over 8 XCDs;
@@ -161,7 +183,8 @@ __global__ __launch_bounds__(kGemmThreads, 2) void grouped_gemm_kernel(GemmArgs 
   const int e = tile >> 20, m0 = (tile & 0xFFFFF) * kBM;
   const int pos0 = a.offsets[e] + m0;
   const int rows = min(kBM, a.offsets[e + 1] - pos0);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
 
   // rows past the expert's end (padding of the last M-tile) read the tile's
@@ -179,58 +202,40 @@ __global__ __launch_bounds__(kGemmThreads, 2) void grouped_gemm_kernel(GemmArgs 
   const int K = a.K;
   const int nk = K / kBK;
 
-  // loads: A 128 rows x 8 chunks (4 per thread: rows tid/8 + 32 i, chunk tid%8);
-  // B row tid: 32 code bytes and 2 scale bytes per K step
-  const int a_chunk = tid & 7;
-  const int b_row = tid;
-  const uint8_t* b_codes;
-  const uint8_t* b_scales;
+  // Copy sources.  A: wave w fills the 1 KB LDS blocks 4w..4w+3 (8 rows
+  // each); lane l fills slot l of a block: row 8*blk + l/8, slot l%8, which
+  // holds chunk (l%8) ^ (row%8) of that row (the XOR swizzle).  B: wave w
+  // fills blocks 2w, 2w+1 (32 rows of 32 bytes); lane l: row 32*blk + l/2,
+  // half l%2.  Scales: wave w fills rows 64w..64w+63, 4 bytes each (the
+  // blocks of two K steps).  Waves 0-1 copy gate rows, 2-3 up rows (GLU).
+  const uint8_t* a_base = (const uint8_t*)a.a_src;
+  uint32_t a_off[4];
   {
-    int mrow;
-    size_t coff, soff;
-    if (GLU) {
-      const bool up = b_row >= kBN / 2;
-      mrow = n0 + (up ? b_row - kBN / 2 : b_row);
-      coff = up ? a.off1 : a.off0;
-      soff = up ? a.soff1 : a.soff0;
-    } else {
-      mrow = n0 + b_row;
-      coff = a.off0;
-      soff = a.soff0;
-    }
-    b_codes = slot + coff + (size_t)mrow * (K / 2);
-    b_scales = slot + soff + (size_t)mrow * (K / 32);
-  }
-  const uint16_t* a_rows[4];
+    const int chunk = (lane & 7) ^ ((lane >> 3) & 7);
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    a_rows[i] = a.a_src + (size_t)s_rowsrc[(tid >> 3) + 32 * i] * K + a_chunk * 8;
+    for (int q = 0; q < 4; ++q) {
+      const int row = (wave * 4 + q) * 8 + (lane >> 3);
+      a_off[q] = (uint32_t)(((size_t)s_rowsrc[row] * K + chunk * 8) * 2);
+    }
+  }
+  const bool up_half = GLU && wave >= 2;
+  const uint8_t* b_base = slot + (up_half ? a.off1 : a.off0);
+  const uint8_t* s_base = slot + (up_half ? a.soff1 : a.soff0);
+  const int mrow_base = n0 - (up_half ? kBN / 2 : 0);
+  uint32_t b_off[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q)
+    b_off[q] = (uint32_t)((mrow_base + (wave * 2 + q) * 32 + (lane >> 1)) * (K / 2) + (lane & 1) * 16);
+  const uint32_t s_off = (uint32_t)((mrow_base + wave * 64 + lane) * (K / 32));
 
-  // next K step in registers (named, so they stay in registers)
-  uint4 pa0, pa1, pa2, pa3, pb0, pb1;
-  uint32_t ps;
-#define MOERT_LOAD_K(kt)                                        \
-  do {                                                          \
-    const int k0_ = (kt) * kBK;                                 \
-    pa0 = *(const uint4*)(a_rows[0] + k0_);                     \
-    pa1 = *(const uint4*)(a_rows[1] + k0_);                     \
-    pa2 = *(const uint4*)(a_rows[2] + k0_);                     \
-    pa3 = *(const uint4*)(a_rows[3] + k0_);                     \
-    pb0 = *(const uint4*)(b_codes + (k0_ >> 1));                \
-    pb1 = *(const uint4*)(b_codes + (k0_ >> 1) + 16);           \
-    ps = *(const uint16_t*)(b_scales + (k0_ >> 5));             \
-  } while (0)
-#define MOERT_STORE_K(buf)                                                                    \
-  do {                                                                                        \
-    *(uint4*)(&s_a[buf][swz((tid >> 3), a_chunk)]) = pa0;                                     \
-    *(uint4*)(&s_a[buf][swz((tid >> 3) + 32, a_chunk)]) = pa1;                                \
-    *(uint4*)(&s_a[buf][swz((tid >> 3) + 64, a_chunk)]) = pa2;                                \
-    *(uint4*)(&s_a[buf][swz((tid >> 3) + 96, a_chunk)]) = pa3;                                \
-    const uint32_t w_[8] = {pb0.x, pb0.y, pb0.z, pb0.w, pb1.x, pb1.y, pb1.z, pb1.w};          \
-    _Pragma("unroll") for (int q = 0; q < 8; ++q)                                             \
-        *(uint32_t*)(&s_b[buf][bswz(b_row, q)]) = w_[q];                                      \
-    *(float2*)(&s_s[buf][b_row * 2]) = make_float2(e8m0_scale(ps & 0xFFu), e8m0_scale(ps >> 8)); \
-  } while (0)
+  auto issue = [&](int kt, const uint8_t* la, const uint8_t* lb) {
+    const int k0 = kt * kBK;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) dma16(a_base, a_off[q] + k0 * 2, lds_addr(la + (wave * 4 + q) * 1024));
+#pragma unroll
+    for (int q = 0; q < 2; ++q) dma16(b_base, b_off[q] + k0 / 2, lds_addr(lb + (wave * 2 + q) * 1024));
+    if ((kt & 1) == 0) dma4(s_base, s_off + k0 / 32, lds_addr(&s_sc[(kt >> 1) & 1][wave * 256]));
+  };
 
   f32x16 acc[2][4];
 #pragma unroll
@@ -248,55 +253,58 @@ __global__ __launch_bounds__(kGemmThreads, 2) void grouped_gemm_kernel(GemmArgs 
   }
   const int lr = lane & 31, kg = lane >> 5;
 
-  // one 16-deep K slice: A fragments (bf16), raw B codes and their scales
-  struct Frag {
-    bf16x8 a[2];
-    uint32_t raw[4];
-    float sc[4];
-  };
-  auto read_frag = [&](int buf, int ks, Frag& f) {
-    const int chunk = ks * 2 + kg;  // A: 16-byte chunk; B: 4-byte word
-#pragma unroll
-    for (int i = 0; i < 2; ++i) f.a[i] = *(const bf16x8*)(&s_a[buf][swz(wm * 64 + i * 32 + lr, chunk)]);
+  // K order inside a step (the same for A and B, so the sum is unchanged):
+  // lane half kg at slice ks takes k = 32*kg + 8*ks + [0, 8), i.e. A chunk
+  // 4*kg + ks and B code word 4*kg + ks; over the step a lane's B codes are
+  // the 16-byte half kg of its row, all under scale block kg.
+  auto compute = [&](int kt, const uint8_t* sa, const uint8_t* sb) {
+    const uint8_t* ss = s_sc[(kt >> 1) & 1];
+    uint4 braw[4];
+    float bsc[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int n = brow[j] + lr;
-      f.raw[j] = *(const uint32_t*)(&s_b[buf][bswz(n, chunk)]);
-      f.sc[j] = s_s[buf][n * 2 + (ks >> 1)];
+      braw[j] = *(const uint4*)(sb + n * 32 + kg * 16);
+      bsc[j] = e8m0_scale(ss[n * 4 + (kt & 1) * 2 + kg]);
+    }
+#pragma unroll
+    for (int ks = 0; ks < kBK / 16; ++ks) {
+      bf16x8 af[2], bfr[4];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) af[i] = *(const bf16x8*)(sa + swz(wm * 64 + i * 32 + lr, 4 * kg + ks));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t w = ks == 0 ? braw[j].x : ks == 1 ? braw[j].y : ks == 2 ? braw[j].z : braw[j].w;
+        bfr[j] = fp4x8_to_bf16(w, bsc[j]);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
     }
   };
-  auto mma = [&](const Frag& f) {
-    bf16x8 bfr[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) bfr[j] = fp4x8_to_bf16(f.raw[j], f.sc[j]);
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], bfr[j], acc[i][j], 0, 0, 0);
-  };
 
-  MOERT_LOAD_K(0);
-  MOERT_STORE_K(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) MOERT_LOAD_K(kt + 1);
-    // the next slice's LDS reads are in flight while this slice's MFMAs run
-    Frag f0, f1;
-    read_frag(buf, 0, f0);
-    read_frag(buf, 1, f1);
-    mma(f0);
-    read_frag(buf, 2, f0);
-    mma(f1);
-    read_frag(buf, 3, f1);
-    mma(f0);
-    mma(f1);
-    if (kt + 1 < nk) MOERT_STORE_K(buf ^ 1);
-    __syncthreads();
+  // one K step on stage (sa, sb); the copies for step kt+2 go to (na, nb)
+  auto step = [&](int kt, const uint8_t* sa, const uint8_t* sb, const uint8_t* na, const uint8_t* nb) {
+    // this wave's copies for step kt are done once at most six (the next
+    // step's, one scale copy aside) are still in flight
+    if (kt + 1 < nk) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();  // every wave's copies for step kt are in LDS; step kt-1's reads are done
+    if (kt + 2 < nk) issue(kt + 2, na, nb);
+    compute(kt, sa, sb);
+  };
+  issue(0, s_a0, s_b0);
+  if (nk > 1) issue(1, s_a1, s_b1);
+  int kt = 0;
+  for (; kt + 3 <= nk; kt += 3) {
+    step(kt, s_a0, s_b0, s_a2, s_b2);
+    step(kt + 1, s_a1, s_b1, s_a0, s_b0);
+    step(kt + 2, s_a2, s_b2, s_a1, s_b1);
   }
-#undef MOERT_LOAD_K
-#undef MOERT_STORE_K
+  if (kt < nk) step(kt, s_a0, s_b0, s_a2, s_b2);
+  if (kt + 1 < nk) step(kt + 1, s_a1, s_b1, s_a0, s_b0);
 
   // epilogue: C element r of lane: row 8*(r/4) + 4*kg + r%4, column lr
 #pragma unroll
