@@ -27,7 +27,8 @@
 // B-tile rows are 128 gate rows then the matching 128 up rows, so a wave's
 // gate and up accumulators share lanes and the SiLU * up epilogue needs no
 // exchange.  Workgroups are mapped so that the N-tiles of one M-tile run on
-// the same XCD (shared A rows in that XCD's L2).
+// the same XCD (shared A rows in that XCD's L2), and each XCD takes a
+// contiguous run of M-tiles (shared B slices of one expert).
 #include "internal.h"
 
 namespace moert {
@@ -171,14 +172,19 @@ __global__ __launch_bounds__(kGemmThreads, 2) void grouped_gemm_kernel(GemmArgs 
   __shared__ __attribute__((aligned(1024))) uint8_t s_sc[2][kStageS];
   __shared__ int32_t s_rowsrc[kBM];  // A source row per tile row
 
-  // XCD-aware mapping: consecutive workgroups go round-robin over 8 XCDs;
-  // give every N-tile of one M-tile to the same XCD.
+  // XCD-aware mapping: consecutive workgroups go round-robin over the 8 XCDs.
+  // XCD x takes the x-th contiguous eighth of the M-tile list, N-tiles of one
+  // M-tile back to back: the N-tiles of an M-tile share its A rows, and the
+  // M-tiles of one expert (adjacent in the list) share its B slices, in that
+  // XCD's L2.
   const int bid = blockIdx.x;
   const int xcd = bid & 7, local = bid >> 3;
-  const int mt = (local / a.n_ntiles) * 8 + xcd;
-  const int nt = local % a.n_ntiles;
   const int n_mtiles = a.offsets[a.E + 1];
-  if (mt >= n_mtiles) return;
+  const int per_xcd = (n_mtiles + 7) >> 3;
+  const int ml = local / a.n_ntiles;
+  const int nt = local % a.n_ntiles;
+  const int mt = xcd * per_xcd + ml;
+  if (ml >= per_xcd || mt >= n_mtiles) return;
   const int tile = a.tiles[mt];
   const int e = tile >> 20, m0 = (tile & 0xFFFFF) * kBM;
   const int pos0 = a.offsets[e] + m0;
