@@ -29,6 +29,8 @@
 // exchange.  Workgroups are mapped so that the N-tiles of one M-tile run on
 // the same XCD (shared A rows in that XCD's L2), and each XCD takes a
 // contiguous run of M-tiles (shared B slices of one expert).
+#include <type_traits>
+
 #include "internal.h"
 
 namespace moert {
@@ -63,8 +65,9 @@ __global__ __launch_bounds__(256) void group_hist_kernel(const int32_t* __restri
     if (h[e]) atomicAdd(&counts[e], h[e]);
 }
 
-// offsets[E+1]; M-tile list tiles[i] = (e << 20) | m0/kBM; tiles_n written to
-// offsets[E+1].
+// offsets[E+1]; M-tile list tiles[i] = (e << 20) | (m0/64 << 1) | half, half
+// marking an expert's last tile when it has at most 64 rows; the tile count
+// is written to offsets[E+1].
 __global__ __launch_bounds__(1024) void group_scan_kernel(const int32_t* counts, int E,
                                                           int32_t* offsets, int32_t* tiles) {
   __shared__ int32_t s_off[kMaxExperts + 1];
@@ -85,7 +88,10 @@ __global__ __launch_bounds__(1024) void group_scan_kernel(const int32_t* counts,
   if (threadIdx.x == 0) offsets[E + 1] = s_toff[E];
   for (int e = threadIdx.x; e < E; e += blockDim.x) {
     const int nt = (counts[e] + kBM - 1) / kBM;
-    for (int m = 0; m < nt; ++m) tiles[s_toff[e] + m] = (e << 20) | m;
+    for (int m = 0; m < nt; ++m) {
+      const int half = counts[e] - m * kBM <= kBM / 2;  // a last tile of at most 64 rows
+      tiles[s_toff[e] + m] = (e << 20) | ((m * kBM / 64) << 1) | half;
+    }
   }
 }
 
@@ -186,9 +192,10 @@ __global__ __launch_bounds__(kGemmThreads, 2) void grouped_gemm_kernel(GemmArgs 
   const int mt = xcd * per_xcd + ml;
   if (ml >= per_xcd || mt >= n_mtiles) return;
   const int tile = a.tiles[mt];
-  const int e = tile >> 20, m0 = (tile & 0xFFFFF) * kBM;
+  const int e = tile >> 20, m0 = ((tile >> 1) & 0x7FFFF) * 64;
+  const bool half = tile & 1;  // at most 64 rows: computed as 64 x 256
   const int pos0 = a.offsets[e] + m0;
-  const int rows = min(kBM, a.offsets[e + 1] - pos0);
+  const int rows = min(half ? kBM / 2 : kBM, a.offsets[e + 1] - pos0);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
@@ -243,102 +250,113 @@ __global__ __launch_bounds__(kGemmThreads, 2) void grouped_gemm_kernel(GemmArgs 
     if ((kt & 1) == 0) dma4(s_base, s_off + k0 / 32, lds_addr(&s_sc[(kt >> 1) & 1][wave * 256]));
   };
 
-  f32x16 acc[2][4];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
-
-  // wave tile: rows wm*64 + {0,32}; B rows: GLU -> gate wn*64 + {0,32} and up
-  // 128 + wn*64 + {0,32}; down -> wn*128 + {0,32,64,96}
-  int brow[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    if (GLU) brow[j] = (j < 2 ? 0 : kBN / 2) + wn * 64 + (j & 1) * 32;
-    else brow[j] = wn * 128 + j * 32;
-  }
   const int lr = lane & 31, kg = lane >> 5;
 
-  // K order inside a step (the same for A and B, so the sum is unchanged):
-  // lane half kg at slice ks takes k = 32*kg + 8*ks + [0, 8), i.e. A chunk
-  // 4*kg + ks and B code word 4*kg + ks; over the step a lane's B codes are
-  // the 16-byte half kg of its row, all under scale block kg.
-  auto compute = [&](int kt, const uint8_t* sa, const uint8_t* sb) {
-    const uint8_t* ss = s_sc[(kt >> 1) & 1];
-    uint4 braw[4];
-    float bsc[4];
+  // The rest runs in one of two shapes.  Full tile: waves in a 2 x 2 grid of
+  // 64 x 128 wave tiles (2 x 4 MFMA tiles); B rows GLU -> gate wn*64 + {0,32}
+  // and up 128 + wn*64 + {0,32}, down -> wn*128 + {0,32,64,96}.  Half tile
+  // (at most 64 rows): the four waves side by side, each 64 x 64 (2 x 2 MFMA
+  // tiles); B rows GLU -> gate 32*w and up 128 + 32*w, down -> 64*w + {0,32}.
+  // The copies are the same in both shapes (the unused A rows repeat row 0).
+  auto run = [&](auto half_c) {
+    constexpr bool HALF = decltype(half_c)::value;
+    constexpr int NJ = HALF ? 2 : 4;
+    const int arow0 = HALF ? 0 : wm * 64;
+    int brow[NJ];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int n = brow[j] + lr;
-      braw[j] = *(const uint4*)(sb + n * 32 + kg * 16);
-      bsc[j] = e8m0_scale(ss[n * 4 + (kt & 1) * 2 + kg]);
+    for (int j = 0; j < NJ; ++j) {
+      if (HALF) brow[j] = GLU ? j * (kBN / 2) + wave * 32 : wave * 64 + j * 32;
+      else brow[j] = GLU ? (j < 2 ? 0 : kBN / 2) + wn * 64 + (j & 1) * 32 : wn * 128 + j * 32;
     }
+    f32x16 acc[2][NJ];
 #pragma unroll
-    for (int ks = 0; ks < kBK / 16; ++ks) {
-      bf16x8 af[2], bfr[4];
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int i = 0; i < 2; ++i) af[i] = *(const bf16x8*)(sa + swz(wm * 64 + i * 32 + lr, 4 * kg + ks));
+      for (int j = 0; j < NJ; ++j) acc[i][j] = f32x16{};
+
+    // K order inside a step (the same for A and B, so the sum is unchanged):
+    // lane half kg at slice ks takes k = 32*kg + 8*ks + [0, 8), i.e. A chunk
+    // 4*kg + ks and B code word 4*kg + ks; over the step a lane's B codes are
+    // the 16-byte half kg of its row, all under scale block kg.
+    auto compute = [&](int kt, const uint8_t* sa, const uint8_t* sb) {
+      const uint8_t* ss = s_sc[(kt >> 1) & 1];
+      uint4 braw[NJ];
+      float bsc[NJ];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t w = ks == 0 ? braw[j].x : ks == 1 ? braw[j].y : ks == 2 ? braw[j].z : braw[j].w;
-        bfr[j] = fp4x8_to_bf16(w, bsc[j]);
+      for (int j = 0; j < NJ; ++j) {
+        const int n = brow[j] + lr;
+        braw[j] = *(const uint4*)(sb + n * 32 + kg * 16);
+        bsc[j] = e8m0_scale(ss[n * 4 + (kt & 1) * 2 + kg]);
       }
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int ks = 0; ks < kBK / 16; ++ks) {
+        bf16x8 af[2], bfr[NJ];
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-    }
-  };
-
-  // one K step on stage (sa, sb); the copies for step kt+2 go to (na, nb)
-  auto step = [&](int kt, const uint8_t* sa, const uint8_t* sb, const uint8_t* na, const uint8_t* nb) {
-    // this wave's copies for step kt are done once at most six (the next
-    // step's, one scale copy aside) are still in flight
-    if (kt + 1 < nk) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
-    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();  // every wave's copies for step kt are in LDS; step kt-1's reads are done
-    if (kt + 2 < nk) issue(kt + 2, na, nb);
-    compute(kt, sa, sb);
-  };
-  issue(0, s_a0, s_b0);
-  if (nk > 1) issue(1, s_a1, s_b1);
-  int kt = 0;
-  for (; kt + 3 <= nk; kt += 3) {
-    step(kt, s_a0, s_b0, s_a2, s_b2);
-    step(kt + 1, s_a1, s_b1, s_a0, s_b0);
-    step(kt + 2, s_a2, s_b2, s_a1, s_b1);
-  }
-  if (kt < nk) step(kt, s_a0, s_b0, s_a2, s_b2);
-  if (kt + 1 < nk) step(kt + 1, s_a1, s_b1, s_a0, s_b0);
-
-  // epilogue: C element r of lane: row 8*(r/4) + 4*kg + r%4, column lr
+        for (int i = 0; i < 2; ++i) af[i] = *(const bf16x8*)(sa + swz(arow0 + i * 32 + lr, 4 * kg + ks));
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = wm * 64 + i * 32 + 8 * (r >> 2) + 4 * kg + (r & 3);
-      if (row >= rows) continue;
-      if (GLU) {
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const float g = acc[i][j][r], u = acc[i][j + 2][r];
-          const float hv = g * u * __builtin_amdgcn_rcpf(1.f + __expf(-g));
-          uint32_t bits = __float_as_uint(hv);
-          bits += 0x7FFFu + ((bits >> 16) & 1u);
-          const int col = n0 + wn * 64 + j * 32 + lr;
-          a.h_out[(size_t)(pos0 + row) * a.N + col] = (uint16_t)(bits >> 16);
+        for (int j = 0; j < NJ; ++j) {
+          const uint32_t w = ks == 0 ? braw[j].x : ks == 1 ? braw[j].y : ks == 2 ? braw[j].z : braw[j].w;
+          bfr[j] = fp4x8_to_bf16(w, bsc[j]);
         }
-      } else {
-        const int pair = a.perm[pos0 + row];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int col = n0 + wn * 128 + j * 32 + lr;
-          a.p_out[(size_t)pair * a.N + col] = acc[i][j][r];
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < NJ; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+      }
+    };
+
+    // one K step on stage (sa, sb); the copies for step kt+2 go to (na, nb)
+    auto step = [&](int kt, const uint8_t* sa, const uint8_t* sb, const uint8_t* na, const uint8_t* nb) {
+      // this wave's copies for step kt are done once at most six (the next
+      // step's, one scale copy aside) are still in flight
+      if (kt + 1 < nk) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();  // every wave's copies for step kt are in LDS; step kt-1's reads are done
+      if (kt + 2 < nk) issue(kt + 2, na, nb);
+      compute(kt, sa, sb);
+    };
+    issue(0, s_a0, s_b0);
+    if (nk > 1) issue(1, s_a1, s_b1);
+    int kt = 0;
+    for (; kt + 3 <= nk; kt += 3) {
+      step(kt, s_a0, s_b0, s_a2, s_b2);
+      step(kt + 1, s_a1, s_b1, s_a0, s_b0);
+      step(kt + 2, s_a2, s_b2, s_a1, s_b1);
+    }
+    if (kt < nk) step(kt, s_a0, s_b0, s_a2, s_b2);
+    if (kt + 1 < nk) step(kt + 1, s_a1, s_b1, s_a0, s_b0);
+
+    // epilogue: C element r of lane: row 8*(r/4) + 4*kg + r%4, column lr
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = arow0 + i * 32 + 8 * (r >> 2) + 4 * kg + (r & 3);
+        if (row >= rows) continue;
+        if (GLU) {
+#pragma unroll
+          for (int j = 0; j < NJ / 2; ++j) {
+            const float g = acc[i][j][r], u = acc[i][j + NJ / 2][r];
+            const float hv = g * u * __builtin_amdgcn_rcpf(1.f + __expf(-g));
+            uint32_t bits = __float_as_uint(hv);
+            bits += 0x7FFFu + ((bits >> 16) & 1u);
+            const int col = n0 + (HALF ? wave * 32 : wn * 64 + j * 32) + lr;
+            a.h_out[(size_t)(pos0 + row) * a.N + col] = (uint16_t)(bits >> 16);
+          }
+        } else {
+          const int pair = a.perm[pos0 + row];
+#pragma unroll
+          for (int j = 0; j < NJ; ++j) {
+            const int col = n0 + brow[j] + lr;
+            a.p_out[(size_t)pair * a.N + col] = acc[i][j][r];
+          }
         }
       }
     }
-  }
+  };
+  if (half) run(std::true_type{});
+  else run(std::false_type{});
 }
 
 // y[t] = sum over ascending j of w[t][j] * P[t*k + j]
