@@ -65,6 +65,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   __shared__ int32_t s_eslot[kMaxExperts];
   __shared__ int32_t s_miss[kMaxExperts];
   __shared__ int32_t s_vic[kMaxExperts];
+  __shared__ int32_t s_vicold[kMaxExperts];  // occupant of each victim slot
+  __shared__ int32_t s_selold[kMaxExperts];
   __shared__ uint32_t s_hitbits[kMaxSlots / 32];
   __shared__ uint32_t s_hist[2048];
   __shared__ int32_t s_cnt[3][kWaves];
@@ -74,6 +76,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   __shared__ int64_t s_tick;
   __shared__ int32_t s_nuniq, s_nhit, s_m, s_q, s_keff, s_evict, s_ngpu, s_bad;
   __shared__ uint32_t s_prefix, s_pmask, s_kk;
+  __shared__ uint32_t s_kmin[kWaves], s_kmax[kWaves];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int E = a.E, Tk = a.T * a.k, n = a.n;
@@ -89,6 +92,17 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     s_tick = a.st->tick + 1;
     s_evict = 0;
     s_bad = 0;
+  }
+  // the slot table rows of this thread's slots, requested now so their
+  // latency overlaps the dedup and classification
+  // (key = tick + 1, so an empty slot's key is 0)
+  uint32_t key[SPT];
+  int32_t sid_r[SPT];
+#pragma unroll
+  for (int i = 0; i < SPT; ++i) {
+    const int s = tid * SPT + i;
+    key[i] = s < n ? (uint32_t)(a.slot_ts[s] + 1) : kSentinel;
+    sid_r[i] = s < n ? a.slot2id[s] : -1;
   }
   __syncthreads();
   const int64_t tick = s_tick;
@@ -157,29 +171,57 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   if (keff > 0) {
     // keys of this thread's contiguous slots: tick + 1 (empty = 0), hits and
     // slots past n excluded
-    uint32_t key[SPT];
     const int s0 = tid * SPT;
-    int ncand = 0;
+    uint32_t kmin = kSentinel, kmax = 0;
 #pragma unroll
     for (int i = 0; i < SPT; ++i) {
       int s = s0 + i;
-      uint32_t kv = kSentinel;
-      if (s < n && !((s_hitbits[s >> 5] >> (s & 31)) & 1u)) kv = (uint32_t)(a.slot_ts[s] + 1);
-      key[i] = kv;
+      if (s < n && !((s_hitbits[s >> 5] >> (s & 31)) & 1u)) {
+        kmin = min(kmin, key[i]);
+        kmax = max(kmax, key[i]);
+      } else {
+        key[i] = kSentinel;  // current hits and slots past n are not candidates
+      }
     }
+    // keys relative to the smallest candidate: the select then only needs
+    // the digits that the spread of ticks actually uses
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, off));
+      kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, off));
+    }
+    if (lane == 0) {
+      s_kmin[wave] = kmin;
+      s_kmax[wave] = kmax;
+    }
+    __syncthreads();
+    kmin = kSentinel;
+    kmax = 0;
+    for (int w = 0; w < kWaves; ++w) {
+      kmin = min(kmin, s_kmin[w]);
+      kmax = max(kmax, s_kmax[w]);
+    }
+#pragma unroll
+    for (int i = 0; i < SPT; ++i)
+      if (key[i] != kSentinel) key[i] -= kmin;
+    const uint32_t spread = kmax >= kmin ? kmax - kmin : 0;
+    const int bits = spread ? 32 - __builtin_clz(spread) : 0;
+    const int first_pass = bits > 21 ? 0 : bits > 10 ? 1 : 2;
     const int n_cand = n - s_nhit;
     uint32_t tau = kSentinel;  // keys < tau are all taken
     if (keff < n_cand) {
-      // radix select of the keff-th smallest key: 11 + 11 + 10 bits
+      // radix select of the keff-th smallest key: 11 + 11 + 10 bits, leading
+      // passes whose digit is zero for every candidate skipped
       if (tid == 0) {
         s_prefix = 0;
-        s_pmask = 0;
+        s_pmask = first_pass == 0 ? 0u : first_pass == 1 ? 0xFFE00000u : 0xFFFFFC00u;
         s_kk = (uint32_t)keff;
       }
       const int shifts[3] = {21, 10, 0};
       const uint32_t dmask[3] = {0x7FFu, 0x7FFu, 0x3FFu};
 #pragma unroll
       for (int pass = 0; pass < 3; ++pass) {
+        if (pass < first_pass) continue;  // uniform
         for (int i = tid; i < 2048; i += kPlanThreads) s_hist[i] = 0;
         __syncthreads();
         const uint32_t prefix = s_prefix, pmask = s_pmask;
@@ -261,9 +303,13 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
       const uint32_t kv = key[i];
       const uint64_t packed = ((uint64_t)kv << 32) | (uint32_t)(s0 + i);
       if (kv < tau) {
+        s_selold[pl] = sid_r[i];
         s_sel[pl++] = packed;
       } else if (kv == tau && kv != kSentinel) {
-        if (pe < r) s_sel[tl + pe] = packed;
+        if (pe < r) {
+          s_selold[tl + pe] = sid_r[i];
+          s_sel[tl + pe] = packed;
+        }
         ++pe;
       }
     }
@@ -274,6 +320,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
       int rank = 0;
       for (int j = 0; j < keff; ++j) rank += s_sel[j] < mine;
       s_vic[rank] = (int32_t)(mine & 0xFFFFFFFFu);
+      s_vicold[rank] = s_selold[tid];
     }
     __syncthreads();
   }
@@ -284,7 +331,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   if (tid < q) {
     const int uu = s_miss[tid];
     const int s = s_vic[tid];
-    const int old = a.slot2id[s];
+    const int old = s_vicold[tid];
     if (old >= 0) {
       a.id2slot[old] = -1;
       atomicAdd(&s_evict, 1);
