@@ -179,16 +179,18 @@ __global__ __launch_bounds__(kGemmThreads, 2) void grouped_gemm_kernel(GemmArgs 
   __shared__ int32_t s_rowsrc[kBM];  // A source row per tile row
 
   // XCD-aware mapping: consecutive workgroups go round-robin over the 8 XCDs.
-  // XCD x takes the x-th contiguous eighth of the M-tile list, N-tiles of one
-  // M-tile back to back: the N-tiles of an M-tile share its A rows, and the
-  // M-tiles of one expert (adjacent in the list) share its B slices, in that
-  // XCD's L2.
+  // XCD x takes the x-th contiguous eighth of the M-tile list: the N-tiles of
+  // an M-tile share its A rows, and the M-tiles of one expert (adjacent in
+  // the list) share its B slices, in that XCD's L2.
   const int bid = blockIdx.x;
   const int xcd = bid & 7, local = bid >> 3;
   const int n_mtiles = a.offsets[a.E + 1];
   const int per_xcd = (n_mtiles + 7) >> 3;
-  const int ml = local / a.n_ntiles;
-  const int nt = local % a.n_ntiles;
+  // within the XCD, groups of 4 M-tiles: N-tile outer, M-tile inner, so the
+  // up to 4 workgroups that read the same B slice run back to back
+  const int grp = local / (4 * a.n_ntiles), rem = local - grp * 4 * a.n_ntiles;
+  const int nt = rem >> 2;
+  const int ml = grp * 4 + (rem & 3);
   const int mt = xcd * per_xcd + ml;
   if (ml >= per_xcd || mt >= n_mtiles) return;
   const int tile = a.tiles[mt];
@@ -241,13 +243,16 @@ __global__ __launch_bounds__(kGemmThreads, 2) void grouped_gemm_kernel(GemmArgs 
     b_off[q] = (uint32_t)((mrow_base + (wave * 2 + q) * 32 + (lane >> 1)) * (K / 2) + (lane & 1) * 16);
   const uint32_t s_off = (uint32_t)((mrow_base + wave * 64 + lane) * (K / 32));
 
+  // the K offset advances the (scalar) base, the per-lane offsets stay fixed
   auto issue = [&](int kt, const uint8_t* la, const uint8_t* lb) {
     const int k0 = kt * kBK;
+    const uint8_t* ab = a_base + k0 * 2;
+    const uint8_t* bb = b_base + k0 / 2;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) dma16(a_base, a_off[q] + k0 * 2, lds_addr(la + (wave * 4 + q) * 1024));
+    for (int q = 0; q < 4; ++q) dma16(ab, a_off[q], lds_addr(la + (wave * 4 + q) * 1024));
 #pragma unroll
-    for (int q = 0; q < 2; ++q) dma16(b_base, b_off[q] + k0 / 2, lds_addr(lb + (wave * 2 + q) * 1024));
-    if ((kt & 1) == 0) dma4(s_base, s_off + k0 / 32, lds_addr(&s_sc[(kt >> 1) & 1][wave * 256]));
+    for (int q = 0; q < 2; ++q) dma16(bb, b_off[q], lds_addr(lb + (wave * 2 + q) * 1024));
+    if ((kt & 1) == 0) dma4(s_base + k0 / 32, s_off, lds_addr(&s_sc[(kt >> 1) & 1][wave * 256]));
   };
 
   const int lr = lane & 31, kg = lane >> 5;
@@ -410,7 +415,8 @@ hipError_t launch_prefill_compute(moe_ctx* ctx, int layer, const void* x, int T,
   a.tiles = pf.tiles;
   a.perm = pf.perm;
   a.max_mtiles = Tk / kBM + E;
-  const int grid_m = (a.max_mtiles + 7) / 8 * 8;
+  // M-tile slots: 8 XCDs x whole groups of 4 (see the kernel's mapping)
+  const int grid_m = (a.max_mtiles + 31) / 32 * 32;
   // GEMM1: gate/up, K = H, N = I
   a.K = H;
   a.N = I;
