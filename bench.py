@@ -19,6 +19,9 @@ oracle timed on a bounded sample of the same calls.
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -26,6 +29,76 @@ import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
+
+# Kernel sources whose counters profiles/traffic.json holds: a recorded
+# figure is used only while these files are unchanged.
+TRAFFIC_SOURCES = {
+    "decode_ffn": ["routed_expert_execution_moe_amd/csrc/ffn.h",
+                   "routed_expert_execution_moe_amd/csrc/ffn_bf16.hip"],
+    "prefill_gemm": ["routed_expert_execution_moe_amd/csrc/prefill.hip"],
+}
+TRAFFIC_KERNELS = {"decode_ffn": ["ffn_kernel"], "prefill_gemm": ["grouped_gemm_kernel"]}
+# FETCH_SIZE / WRITE_SIZE (KiB per dispatch) to bytes: what the counters read
+# for a plain kernel of known size (--copy-calibration: 1 GiB read, 1 GiB written)
+FETCH_SCALE, WRITE_SCALE = 2.0 * 1024, 1.0 * 1024
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def _sources_sha(kind):
+    h = hashlib.sha256()
+    for f in TRAFFIC_SOURCES[kind]:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(kind):
+    """HBM bytes per launch from the committed counter record, or None when
+    there is none or the kernel's source changed since it was taken."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            t = json.load(fh)[kind]
+    except (OSError, KeyError, ValueError):
+        return None
+    return t["bytes_per_launch"] if t.get("sha256") == _sources_sha(kind) else None
+
+
+def record_traffic(kind, fetch_dir, write_dir):
+    """Write profiles/traffic.json[kind] from two rocprofv3 --pmc runs (one with
+    FETCH_SIZE, one with WRITE_SIZE) of this bench: HBM bytes per dispatch of
+    each of the kind's kernels, summed over them (the decode FFN is one
+    launch per layer; the prefill GEMM is GEMM1 + GEMM2 per layer)."""
+    def per_kernel(d, counter):
+        sums = {}
+        for f in glob.glob(os.path.join(d, "*counter_collection.csv")):
+            with open(f) as fh:
+                for r in csv.DictReader(fh):
+                    if r["Counter_Name"] != counter:
+                        continue
+                    name = r["Kernel_Name"]
+                    key = next((k for k in TRAFFIC_KERNELS[kind] if k in name), None)
+                    if key is None:
+                        continue
+                    tag = name.split("(")[0]
+                    sums.setdefault(tag, []).append(float(r["Counter_Value"]))
+        return {k: sum(v) / len(v) for k, v in sums.items()}
+    fetch = per_kernel(fetch_dir, "FETCH_SIZE")
+    write = per_kernel(write_dir, "WRITE_SIZE")
+    total = sum(fetch.values()) * FETCH_SCALE + sum(write.values()) * WRITE_SCALE
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        t = {}
+    t[kind] = {"bytes_per_launch": round(total), "sha256": _sources_sha(kind),
+               "kernels": {k: {"fetch_kib": round(fetch.get(k, 0), 1),
+                               "write_kib": round(write.get(k, 0), 1)} for k in sorted(set(fetch) | set(write))},
+               "scale": {"FETCH_SIZE": FETCH_SCALE, "WRITE_SIZE": WRITE_SCALE}}
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(t, fh, indent=1, sort_keys=True)
+        fh.write("\n")
+    return t[kind]
+
 
 METRIC = "MoE-layer decode µs/layer + expert-FFN HBM GB/s (% of peak); prefill TFLOP/s"
 HBM_PEAK_GBPS = 8000.0
@@ -44,6 +117,9 @@ def parse():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--prefill-only", action="store_true",
                     help="run only the prefill leg (for profiling); prints its fields")
+    ap.add_argument("--record-traffic", nargs=3, metavar=("KIND", "FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/traffic.json[KIND] (decode_ffn | prefill_gemm) from the "
+                         "counter CSVs of a FETCH_SIZE run and a WRITE_SIZE run of this bench")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain streaming kernel of known size, whose "
                          "FETCH_SIZE / WRITE_SIZE counter readings scale those counters to bytes")
@@ -108,7 +184,8 @@ def bench_prefill():
             "prefill_roofline": {"bound": "mfma", "kernel": "grouped GEMM1 + GEMM2 (bf16 MFMA, "
                                  "MXFP4 dequantised in registers)", "achieved": round(tflops, 1),
                                  "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-                                 "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4), "traffic": None},
+                                 "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
+                                 "traffic": recorded_traffic("prefill_gemm")},
             "prefill_gemm_ms_per_layer": round(gemm_ms / wl.L, 3),
             "prefill_group_ms_per_layer": round(tm["prefill_group"]["ms"] / wl.L, 3),
             "prefill_merge_ms_per_layer": round(tm["prefill_merge"]["ms"] / wl.L, 3),
@@ -195,6 +272,10 @@ def main():
 
     if a.prefill_only:
         print(json.dumps(bench_prefill()), flush=True)
+        return
+    if a.record_traffic:
+        kind, fd, wd = a.record_traffic
+        print(json.dumps(record_traffic(kind, fd, wd)), flush=True)
         return
     if a.copy_calibration:
         print(json.dumps(copy_calibration()), flush=True)
@@ -319,7 +400,7 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(ffn_gbps / HBM_PEAK_GBPS, 4) if ffn_gbps else None,
-            "traffic": None,
+            "traffic": recorded_traffic("decode_ffn"),
         },
         "cpu_baseline": cpu,
         "breakdown_us_per_call": per,

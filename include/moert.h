@@ -74,8 +74,9 @@ typedef struct {
   int32_t n_layers;      /* L: MoE layers; flat expert id u = l*E + e        */
   int32_t n_experts;     /* E (1..1024)                                       */
   int32_t top_k;         /* k (1..min(E, 32))                                 */
-  int32_t hidden;        /* H (multiple of 256)                               */
-  int32_t inter;         /* I, expert intermediate (multiple of 256)          */
+  int32_t hidden;        /* H: multiple of 64, at most 512 sixteen-byte chunks
+                            per row (F32 2048, BF16 4096, MXFP4 16384)       */
+  int32_t inter;         /* I, expert intermediate: same rules as H           */
   int32_t w_dtype;       /* moe_dtype of expert weights: F32, BF16 or MXFP4   */
   int32_t act_dtype;     /* moe_dtype of x and y: F32 or BF16                 */
   int32_t n_slots;       /* initial device slot budget (0..max_slots)         */
@@ -183,6 +184,8 @@ moe_status moe_cache_resize(moe_ctx* ctx, int32_t new_n_slots, int32_t timeout_m
  * grouped GEMM; y[t] = sum over ascending j of w[t][j] * FFN(x[t]).
  * x (device) [T][H] act dtype; ids (device) int32 [T][k]; w (device) fp32
  * [T][k]; y (device) [T][H].  1 <= T <= max_prefill_tokens.
+ * Supported for MXFP4 experts with bf16 activations, H % 256 == 0 and
+ * I % 128 == 0 (MOE_EUNSUPPORTED otherwise).
  * MOE_ENOSPC if n_slots < 2E (the pages fall back to on-demand loading
  * instead of oversubscribing; that fallback is not provided). */
 moe_status moe_prefill_layer(moe_ctx* ctx, int32_t layer, const void* x, int32_t T,

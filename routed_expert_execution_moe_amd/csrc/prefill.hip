@@ -18,17 +18,18 @@
 //
 // GEMM tiling (gfx950, v_mfma_f32_32x32x16_bf16): a workgroup of 4 waves owns
 // a 128-row M-tile of one expert and a 256-column N-tile, the waves in a 2x2
-// grid of 64 x 128 wave tiles (2 x 4 MFMA tiles); K steps of 64 staged in LDS
-// with the 16-byte chunks of each row XOR-swizzled by (row % 8), and the next
-// K step prefetched into registers while the MFMAs run and stored into the
-// other half of a double-buffered LDS tile.  B stays MXFP4 in LDS (a quarter
-// of its bf16 size) and each lane dequantises its 8-element fragment right
-// before the MFMA with the hardware scaled FP4 -> bf16 convert.  For GEMM1 the 256
-// B-tile rows are 128 gate rows then the matching 128 up rows, so a wave's
-// gate and up accumulators share lanes and the SiLU * up epilogue needs no
-// exchange.  Workgroups are mapped so that the N-tiles of one M-tile run on
-// the same XCD (shared A rows in that XCD's L2), and each XCD takes a
-// contiguous run of M-tiles (shared B slices of one expert).
+// grid of 64 x 128 wave tiles (2 x 4 MFMA tiles); an expert's last tile of at
+// most 64 rows runs as 64 x 256 with the waves side by side.  K steps of 64
+// go through three LDS stages that direct-to-LDS copies fill two steps ahead
+// (A rows XOR-swizzled by 16-byte chunk, B as raw MXFP4 codes, a quarter of
+// its bf16 size, E8M0 scales per two steps).  Each lane dequantises its B
+// fragment right before the MFMA with the hardware scaled FP4 -> bf16
+// convert.  For GEMM1 the 256 B-tile rows are 128 gate rows then the
+// matching 128 up rows, so a wave's gate and up accumulators share lanes and
+// the SiLU * up epilogue needs no exchange.  Each XCD takes a contiguous run
+// of M-tiles, N-tile outer over groups of four M-tiles, so the N-tiles of an
+// M-tile share its A rows and the M-tiles of an expert share its B slices in
+// that XCD's L2.
 #include <type_traits>
 
 #include "internal.h"
