@@ -202,7 +202,9 @@ def bench_prefill():
 def copy_calibration():
     """Four launches of an elementwise kernel (negate) that reads 1 GiB and
     writes 1 GiB of float32: the HBM traffic counters of these launches are
-    what a counter reads for a known number of bytes."""
+    what a counter reads for a known number of bytes.  Also times (HIP
+    events) the same kernel at the decode FFN's size, 72 MB of traffic, as a
+    reference for what one short streaming launch reaches."""
     import torch
     n = 1 << 28
     a = torch.ones(n, dtype=torch.float32, device="cuda")
@@ -211,8 +213,24 @@ def copy_calibration():
         torch.neg(a, out=b)
     torch.cuda.synchronize()
     assert float(b[-1]) == -1.0
-    return {"calibration_kernel": "torch.neg float32, 2^28 elements", "bytes_read": n * 4,
-            "bytes_written": n * 4, "launches": 4}
+    out = {"calibration_kernel": "torch.neg float32, 2^28 elements", "bytes_read": n * 4,
+           "bytes_written": n * 4, "launches": 4}
+    m = 72_000_000 // 8  # elements: 36 MB read + 36 MB written
+    srcs = [torch.ones(m, dtype=torch.float32, device="cuda") for _ in range(8)]
+    dst = torch.empty(m, dtype=torch.float32, device="cuda")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ts = []
+    for it in range(200):
+        e0.record()
+        torch.neg(srcs[it % 8], out=dst)
+        e1.record()
+        torch.cuda.synchronize()
+        if it >= 20:
+            ts.append(e0.elapsed_time(e1))
+    us = sum(ts) / len(ts) * 1e3
+    out["stream_72MB_us"] = round(us, 2)
+    out["stream_72MB_gbps"] = round(2 * m * 4 / us / 1e3, 1)
+    return out
 
 
 def cpu_baseline(wl, pool_np, stride, logits, xs, steps_range, budget_s):
