@@ -142,9 +142,10 @@ moe_status moe_route_topk(moe_ctx* ctx, const float* logits, int32_t T, int32_t*
  * hits' recency, surfaces the K = min(max_tokens*k, E, n_slots[, max_fetch])
  * least-recently-used slots by (tick, slot) excluding current hits, admits the
  * first q misses into the first q of them and writes slot_map[t][j] (slot id,
- * or -1 = run on the host).  One LRU tick per call.  It then enqueues the
- * host branch for the remaining misses (launched first, on a side stream) and
- * the PCIe fill of the q admitted experts into their slots (on `stream`).
+ * or -1 = run on the host).  One LRU tick per call.  The kernel itself hands
+ * the remaining misses to the host branch (a doorbell in pinned memory that a
+ * host thread answers); the call then enqueues the PCIe fill of the q
+ * admitted experts into their slots (on `stream`).
  * ids (device) int32 [T][k]; x (device) [T][H] act dtype, read by the host
  * branch.  1 <= T <= max_tokens. */
 moe_status moe_cache_plan(moe_ctx* ctx, int32_t layer, const int32_t* ids, int32_t T,

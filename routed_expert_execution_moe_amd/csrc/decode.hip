@@ -5,6 +5,10 @@
 // then the batched copy, then grouped evaluation): the host never learns
 // which slots were chosen (the plan stays on the device), so the copy is a
 // device-pull kernel reading the pinned, device-mapped host banks over PCIe.
+// The expert FFN follows the fill on the same stream rather than running
+// beside it for the experts already resident: with megabytes of host reads in
+// flight, an HBM stream launched next to the pull ran 2-4x slower (and was
+// sometimes dispatched late), which buys little and blurs the FFN's timing.
 #include "internal.h"
 
 namespace moert {
@@ -22,7 +26,9 @@ __global__ __launch_bounds__(256) void fill_kernel(const uint8_t* __restrict__ h
   const size_t units = stride / 16;  // 16-byte units per expert
   const size_t total = (size_t)q * units;
   const size_t nthreads = (size_t)gridDim.x * blockDim.x;
-  constexpr int U = 4;
+  // 16 loads of 16 bytes in flight per lane over 64 workgroups (4 MB in
+  // flight): 54-55 GB/s from pinned host memory, a few % above wider grids
+  constexpr int U = 16;
   size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   for (; i + (U - 1) * nthreads < total; i += U * nthreads) {
     u32x4 v[U];
@@ -49,7 +55,7 @@ __global__ __launch_bounds__(256) void fill_kernel(const uint8_t* __restrict__ h
 
 hipError_t launch_fill(moe_ctx* ctx, hipStream_t s) {
   if (ctx->n_slots == 0 || ctx->cfg.mode == MOE_CPU) return hipSuccess;
-  hipLaunchKernelGGL(fill_kernel, dim3(512), dim3(256), 0, s, ctx->host_pool_dev, ctx->pool.base,
+  hipLaunchKernelGGL(fill_kernel, dim3(64), dim3(256), 0, s, ctx->host_pool_dev, ctx->pool.base,
                      ctx->stride, ctx->plan.counts, ctx->plan.fill_u, ctx->plan.fill_slot);
   return hipGetLastError();
 }

@@ -1,21 +1,48 @@
 // Router top-k and residency-table reset.
 //
 // Routing: one 64-lane wave per token.  Lane l holds logits e = l, l+64, ...
-// in registers; k rounds of a wave arg-max (larger logit first, lower expert
-// index on equal logits, NaN ranked as -inf) pick the experts, and the
-// softmax over the k selected logits gives the weights.  The pages leave the
-// router design out of scope (snackonai, "The Promise"); a softmax router is
-// the assumption.
+// in registers (all loads issued before any is used).  Each logit becomes a
+// 64-bit key, its order-preserving unsigned image above the complement of
+// its index, so one unsigned maximum ranks larger logits first and equal
+// logits by lower index (NaN counts as -inf, -0 as +0).  k rounds of a wave
+// maximum pick the experts (DPP within each row of 16 lanes, two swaps
+// across rows); the winner's key is then cleared.  The softmax over the k
+// selected logits gives the weights.  The pages leave the router design out
+// of scope (snackonai, "The Promise"); a softmax router is the assumption.
 #include "internal.h"
 
 namespace moert {
 
-constexpr int kRouteMaxPerLane = kMaxExperts / 64;  // 16
-
-__device__ inline bool better(float v, int e, float bv, int be) {
-  return v > bv || (v == bv && e < be);
+__device__ inline uint64_t route_key(float x, int e) {
+  if (x != x) x = -INFINITY;
+  if (x == 0.f) x = 0.f;  // -0 ranks with +0
+  uint32_t b = __float_as_uint(x);
+  b = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  return ((uint64_t)b << 32) | (uint32_t)(~(uint32_t)e);
 }
 
+__device__ inline float route_val(uint64_t key) {
+  uint32_t b = (uint32_t)(key >> 32);
+  b = (b & 0x80000000u) ? (b & 0x7fffffffu) : ~b;
+  return __uint_as_float(b);
+}
+
+template <int CTRL>
+__device__ inline uint64_t dpp_max(uint64_t k) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)k, CTRL, 0xF, 0xF, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(k >> 32), CTRL, 0xF, 0xF, false);
+  const uint64_t o = ((uint64_t)hi << 32) | lo;
+  return o > k ? o : k;
+}
+
+__device__ inline uint64_t xor_max(uint64_t k, int off) {
+  const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)k, off);
+  const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(k >> 32), off);
+  const uint64_t o = ((uint64_t)hi << 32) | lo;
+  return o > k ? o : k;
+}
+
+template <int PER>
 __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict__ logits, int T,
                                                          int E, int k, int32_t* __restrict__ ids,
                                                          float* __restrict__ w) {
@@ -23,57 +50,40 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
   const int t = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
   if (t >= T) return;
   const float* row = logits + (size_t)t * E;
-  float v[kRouteMaxPerLane];
-  const int per = (E + 63) >> 6;
+  float v[PER];
 #pragma unroll
-  for (int i = 0; i < kRouteMaxPerLane; ++i) {
-    int e = lane + 64 * i;
-    float x = -INFINITY;
-    if (i < per && e < E) {
-      x = row[e];
-      if (x != x) x = -INFINITY;
-    }
-    v[i] = x;
+  for (int i = 0; i < PER; ++i) v[i] = row[min(lane + 64 * i, E - 1)];
+  uint64_t key[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int e = lane + 64 * i;
+    key[i] = e < E ? route_key(v[i], e) : 0;  // 0 ranks below every logit
   }
-  uint32_t taken = 0;
-  float sel0 = 0.f, wsum = 0.f;
-  float my_val = 0.f;  // lane j keeps the j-th selected logit
-  int my_id = 0;
+  uint64_t my_key = 0;  // lane j keeps the j-th selected key
   for (int j = 0; j < k; ++j) {
-    float bv = -INFINITY;
-    int be = 0x7fffffff;
+    uint64_t b = key[0];
 #pragma unroll
-    for (int i = 0; i < kRouteMaxPerLane; ++i) {
-      int e = lane + 64 * i;
-      if (i < per && e < E && !((taken >> i) & 1u) && better(v[i], e, bv, be)) {
-        bv = v[i];
-        be = e;
-      }
-    }
+    for (int i = 1; i < PER; ++i) b = key[i] > b ? key[i] : b;
+    b = dpp_max<0xB1>(b);   // quad_perm [1,0,3,2]
+    b = dpp_max<0x4E>(b);   // quad_perm [2,3,0,1]
+    b = dpp_max<0x141>(b);  // row_half_mirror
+    b = dpp_max<0x140>(b);  // row_mirror
+    b = xor_max(b, 16);
+    b = xor_max(b, 32);
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      float ov = __shfl_xor(bv, off);
-      int oe = __shfl_xor(be, off);
-      if (better(ov, oe, bv, be)) {
-        bv = ov;
-        be = oe;
-      }
-    }
-    if ((be & 63) == lane) taken |= 1u << (be >> 6);
-    if (lane == j) {
-      my_val = bv;
-      my_id = be;
-    }
-    if (j == 0) sel0 = bv;
+    for (int i = 0; i < PER; ++i) key[i] = key[i] == b ? 0 : key[i];
+    if (lane == j) my_key = b;
   }
-  // softmax over the selected logits (lane j holds the j-th)
+  // softmax over the selected logits (lane j holds the j-th); lane 0 holds the max
+  const float my_val = route_val(my_key);
+  const float sel0 = __shfl(my_val, 0);
   float ex = 0.f;
   if (lane < k) ex = (sel0 == -INFINITY) ? 1.f : expf(my_val - sel0);
-  wsum = ex;
+  float wsum = ex;
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) wsum += __shfl_xor(wsum, off);
   if (lane < k) {
-    ids[(size_t)t * k + lane] = my_id;
+    ids[(size_t)t * k + lane] = (int32_t)~(uint32_t)my_key;
     w[(size_t)t * k + lane] = ex / wsum;
   }
 }
@@ -81,7 +91,12 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
 hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w,
                              hipStream_t s) {
   dim3 block(256), grid((T + 3) / 4);
-  hipLaunchKernelGGL(route_topk_kernel, grid, block, 0, s, logits, T, E, k, ids, w);
+  const int per = (E + 63) / 64;
+  if (per <= 1) hipLaunchKernelGGL(route_topk_kernel<1>, grid, block, 0, s, logits, T, E, k, ids, w);
+  else if (per <= 2) hipLaunchKernelGGL(route_topk_kernel<2>, grid, block, 0, s, logits, T, E, k, ids, w);
+  else if (per <= 4) hipLaunchKernelGGL(route_topk_kernel<4>, grid, block, 0, s, logits, T, E, k, ids, w);
+  else if (per <= 8) hipLaunchKernelGGL(route_topk_kernel<8>, grid, block, 0, s, logits, T, E, k, ids, w);
+  else hipLaunchKernelGGL(route_topk_kernel<16>, grid, block, 0, s, logits, T, E, k, ids, w);
   return hipGetLastError();
 }
 
