@@ -294,11 +294,17 @@ __global__ __launch_bounds__(kGemmThreads, 2) void grouped_gemm_kernel(GemmArgs 
         braw[j] = *(const uint4*)(sb + n * 32 + kg * 16);
         bsc[j] = e8m0_scale(ss[n * 4 + (kt & 1) * 2 + kg]);
       }
+      // every A fragment of the step is requested up front, so one LDS
+      // latency per step is exposed instead of one per 16-wide slice
+      bf16x8 af[kBK / 16][2];
+#pragma unroll
+      for (int ks = 0; ks < kBK / 16; ++ks)
+#pragma unroll
+        for (int i = 0; i < 2; ++i) af[ks][i] = *(const bf16x8*)(sa + swz(arow0 + i * 32 + lr, 4 * kg + ks));
+      __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the MFMAs
 #pragma unroll
       for (int ks = 0; ks < kBK / 16; ++ks) {
-        bf16x8 af[2], bfr[NJ];
-#pragma unroll
-        for (int i = 0; i < 2; ++i) af[i] = *(const bf16x8*)(sa + swz(arow0 + i * 32 + lr, 4 * kg + ks));
+        bf16x8 bfr[NJ];
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
           const uint32_t w = ks == 0 ? braw[j].x : ks == 1 ? braw[j].y : ks == 2 ? braw[j].z : braw[j].w;
@@ -308,7 +314,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void grouped_gemm_kernel(GemmArgs 
         for (int i = 0; i < 2; ++i)
 #pragma unroll
           for (int j = 0; j < NJ; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks][i], bfr[j], acc[i][j], 0, 0, 0);
       }
     };
 
