@@ -115,6 +115,8 @@ def parse():
     ap.add_argument("--cpu-baseline-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the decode run replayed from a captured HIP graph")
     ap.add_argument("--prefill-only", action="store_true",
                     help="run only the prefill leg (for profiling); prints its fields")
     ap.add_argument("--record-traffic", nargs=3, metavar=("KIND", "FETCH_DIR", "WRITE_DIR"),
@@ -368,9 +370,43 @@ def main():
             B.moe_destroy(ctx)
         return dt, tm, st0, st1
 
+    def run_graph():
+        """The same steps replayed from one captured HIP graph per step (all
+        layers): the step's logits and hidden states are copied into the
+        captured buffers, then the graph is launched; the copies are timed."""
+        ctx = B.moe_create(make_cfg(0), pool, pool_bytes)
+        try:
+            lg_s = torch.empty_like(lg_d[0])
+            x_s = torch.empty_like(x_d[0])
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                for l in range(wl.L):
+                    B.moe_route_topk(ctx, lg_s[l], wl.T, ids[l], w[l])
+                    B.moe_cache_plan(ctx, l, ids[l], wl.T, x_s[l])
+                    B.moe_expert_ffn(ctx, l, x_s[l], wl.T)
+                    B.moe_merge(ctx, w[l], wl.T, y[l])
+            torch.cuda.synchronize()
+
+            def gstep(s):
+                lg_s.copy_(lg_d[s])
+                x_s.copy_(x_d[s])
+                graph.replay()
+
+            for s in range(warmup):
+                gstep(s)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for s in range(warmup, n_run):
+                gstep(s)
+            torch.cuda.synchronize()
+            return time.perf_counter() - t0
+        finally:
+            B.moe_destroy(ctx)
+
     # the number: events off; the per-phase breakdown: a second run with events on
     dt, _, st0, st1 = run(0)
     dt_timed, tm, _, _ = run(1)
+    dt_graph = run_graph() if not a.no_graph else None
     calls = steps * wl.L
     us_per_layer = dt / calls * 1e6
     n_gpu_experts = (st1.hits - st0.hits) + (st1.fills - st0.fills)
@@ -423,6 +459,9 @@ def main():
         "cpu_baseline": cpu,
         "breakdown_us_per_call": per,
         "breakdown_run_us_per_layer": round(dt_timed / (steps * wl.L) * 1e6, 2),
+        "graph": ({"us_per_layer": round(dt_graph / (steps * wl.L) * 1e6, 2),
+                   "note": "one captured HIP graph per step (all layers), inputs copied into its "
+                           "buffers inside the timed region"} if dt_graph else None),
         "control_kernel_us": per.get("plan"),
         "ffn_us_per_layer": per.get("ffn"),
         "ffn_bytes_per_layer": round(ffn_bytes / calls),

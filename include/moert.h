@@ -158,6 +158,19 @@ moe_status moe_cache_plan(moe_ctx* ctx, int32_t layer, const int32_t* ids, int32
 moe_status moe_expert_ffn(moe_ctx* ctx, int32_t layer, const void* x, int32_t T,
                           moe_stream stream);
 
+/* Graph capture of decode calls [snackonai, "Technical Moats": a policy
+ * simple enough to run inside a captured graph; satyajit, "Residency that
+ * follows the router"]: moe_route_topk, moe_cache_plan, moe_expert_ffn and moe_merge
+ * enqueue only kernels on `stream`, and every value that changes from call to
+ * call (LRU tick, plan count, which also numbers the calls for the host
+ * branch, counts, slot lists) lives on the device.  A caller may therefore
+ * capture any sequence of whole layer calls into a HIP graph and replay it,
+ * as long as: the context was created with timing = 0; the inputs of each
+ * replay sit at the captured addresses; the last call before the capture was
+ * not a prefill layer (run one eager decode layer call after a prefill).  A
+ * resize or a prefill layer changes the slot count and buffers: capture again
+ * after either.  Replays and eager calls may be interleaved. */
+
 /* Exact merge [snackonai, "What It Actually Does"; satyajit, "Decode: the one
  * equation"]: waits for the host branch, then y[t] = sum over ascending j of
  * w[t][j] * (slot_map[t][j] >= 0 ? P_gpu[t][j] : P_cpu[t][j]) in fp32, rounded

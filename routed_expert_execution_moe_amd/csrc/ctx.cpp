@@ -542,9 +542,8 @@ extern "C" moe_status moe_cache_plan(moe_ctx* ctx, int32_t layer, const int32_t*
   if (pst != MOE_OK) return pst;
   // The control kernel hands the host branch its work first (doorbell in
   // pinned memory, answered by the poller thread); the GPU miss path follows.
-  const int64_t seq = ++ctx->call_seq;
   MOE_HIP(ctx, timing_begin(ctx, MOE_T_PLAN, s));
-  MOE_HIP(ctx, launch_plan(ctx, layer, ids, T, x, seq, s));
+  MOE_HIP(ctx, launch_plan(ctx, layer, ids, T, x, s));
   MOE_HIP(ctx, timing_end(ctx, s));
   // GPU miss path: batched copy of the admitted experts into their slots
   if (ctx->n_slots > 0 && ctx->cfg.mode != MOE_CPU) {
@@ -578,7 +577,7 @@ extern "C" moe_status moe_merge(moe_ctx* ctx, const float* w, int32_t T, void* y
     return fail(ctx, MOE_EINVAL, "moe_merge: must follow moe_expert_ffn with the same T");
   hipStream_t s = (hipStream_t)stream;
   MOE_HIP(ctx, timing_begin(ctx, MOE_T_MERGE, s));
-  MOE_HIP(ctx, launch_merge(ctx, w, T, y, ctx->call_seq, s));
+  MOE_HIP(ctx, launch_merge(ctx, w, T, y, s));
   MOE_HIP(ctx, timing_end(ctx, s));
   ctx->state = kIdle;
   return MOE_OK;

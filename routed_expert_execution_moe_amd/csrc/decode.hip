@@ -75,14 +75,15 @@ hipError_t launch_ffn(moe_ctx* ctx, const void* x, int T, hipStream_t s) {
 // host rows by the sign of slot_map (snackonai, "What It Actually Does";
 // satyajit, "Decode: the one equation").  fp32, one rounding to the output.
 // A token with host pairs first waits for the host branch to publish this
-// call's sequence number (bounded: after wait_ticks it flags an error).
+// call's sequence number, the device plan count the control kernel left
+// (bounded: after wait_ticks it flags an error).
 template <int AT>
 __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ w,
                                                     const int32_t* __restrict__ slot_map,
                                                     const float* __restrict__ pg,
                                                     const float* pc, int k, int H,
                                                     void* __restrict__ y, HostSync* sync,
-                                                    int64_t seq, uint64_t wait_ticks) {
+                                                    const DevState* st, uint64_t wait_ticks) {
   __shared__ int s_ok;
   const int t = blockIdx.y;
   bool host = false;
@@ -90,6 +91,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ w,
   if (host) {
     if (threadIdx.x == 0) {
       const uint64_t t0 = wall_clock64();
+      const int64_t seq = st->plans;
       int ok = 1;
       while (__hip_atomic_load(&sync->done, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_SYSTEM) < seq) {
         if (wall_clock64() - t0 > wait_ticks) {
@@ -122,15 +124,15 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ w,
   }
 }
 
-hipError_t launch_merge(moe_ctx* ctx, const float* w, int T, void* y, int64_t seq, hipStream_t s) {
+hipError_t launch_merge(moe_ctx* ctx, const float* w, int T, void* y, hipStream_t s) {
   const int H = ctx->cfg.hidden;
   dim3 grid((H + 255) / 256, T), block(256);
   if (ctx->cfg.act_dtype == MOE_F32)
     hipLaunchKernelGGL(merge_kernel<MOE_F32>, grid, block, 0, s, w, ctx->plan.slot_map, ctx->p_gpu,
-                       ctx->p_cpu_dev, ctx->cfg.top_k, H, y, ctx->sync_dev, seq, ctx->wait_ticks);
+                       ctx->p_cpu_dev, ctx->cfg.top_k, H, y, ctx->sync_dev, ctx->dstate, ctx->wait_ticks);
   else
     hipLaunchKernelGGL(merge_kernel<MOE_BF16>, grid, block, 0, s, w, ctx->plan.slot_map, ctx->p_gpu,
-                       ctx->p_cpu_dev, ctx->cfg.top_k, H, y, ctx->sync_dev, seq, ctx->wait_ticks);
+                       ctx->p_cpu_dev, ctx->cfg.top_k, H, y, ctx->sync_dev, ctx->dstate, ctx->wait_ticks);
   return hipGetLastError();
 }
 

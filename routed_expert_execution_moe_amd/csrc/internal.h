@@ -139,7 +139,6 @@ struct moe_ctx {
   // host branch hand-off
   moert::HostSync* sync = nullptr;        // host address
   moert::HostSync* sync_dev = nullptr;    // device address
-  int64_t call_seq = 0;                   // doorbell value of the current call
   uint64_t wait_ticks = 0;                // merge's wait limit in wall-clock ticks
   uint64_t ffn_wait_ticks = 0;            // expert FFN down items' wait limit
 
@@ -195,13 +194,13 @@ inline int dtype_bytes(int d) { return d == MOE_F32 ? 4 : 2; }
 hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w,
                              hipStream_t s);
 hipError_t launch_plan(moe_ctx* ctx, int layer, const int32_t* ids, int T, const void* x,
-                       int64_t seq, hipStream_t s);
+                       hipStream_t s);
 hipError_t launch_fill(moe_ctx* ctx, hipStream_t s);
 hipError_t launch_ffn(moe_ctx* ctx, const void* x, int T, hipStream_t s);
 hipError_t launch_ffn_f32(moe_ctx* ctx, const void* x, int T, hipStream_t s);
 hipError_t launch_ffn_bf16(moe_ctx* ctx, const void* x, int T, hipStream_t s);
 hipError_t launch_ffn_mx(moe_ctx* ctx, const void* x, int T, hipStream_t s);
-hipError_t launch_merge(moe_ctx* ctx, const float* w, int T, void* y, int64_t seq, hipStream_t s);
+hipError_t launch_merge(moe_ctx* ctx, const float* w, int T, void* y, hipStream_t s);
 hipError_t launch_prefill_admit(moe_ctx* ctx, int layer, hipStream_t s);
 hipError_t launch_prefill_compute(moe_ctx* ctx, int layer, const void* x, int T,
                                   const int32_t* ids, const float* w, void* y, hipStream_t s);

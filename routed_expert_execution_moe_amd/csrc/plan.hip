@@ -24,7 +24,6 @@ constexpr int kWaves = kPlanThreads / 64;
 constexpr uint32_t kSentinel = 0xFFFFFFFFu;
 
 struct PlanArgs {
-  int64_t seq;          // doorbell value of this call
   const int32_t* ids;
   const uint8_t* x;     // activations [T][H], act dtype
   int64_t x_bytes;      // T * H * element bytes
@@ -393,17 +392,20 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     c.K = a.K;
     c.tick_lo = (int32_t)tick;
     *pb.counts = c;
+    // the call's sequence number is the plan count after it: it lives on the
+    // device, so a replayed graph of calls numbers its calls correctly
+    DevState* st = a.st;
+    const int64_t seq = st->plans + 1;
     if (n_cpu > 0) {
       hb->c = c;
       hb->layer = a.layer;
       hb->T = a.T;
       __threadfence_system();
-      *(volatile int64_t*)&hb->seq = a.seq;  // ring the host branch
+      *(volatile int64_t*)&hb->seq = seq;  // ring the host branch
       __threadfence_system();
     }
-    DevState* st = a.st;
     st->tick = tick;
-    st->plans += 1;
+    st->plans = seq;
     st->hits += s_nhit;
     st->fills += q;
     st->cpu += mm - q;
@@ -412,9 +414,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
 }
 
 hipError_t launch_plan(moe_ctx* ctx, int layer, const int32_t* ids, int T, const void* x,
-                       int64_t seq, hipStream_t s) {
+                       hipStream_t s) {
   PlanArgs a;
-  a.seq = seq;
   a.ids = ids;
   a.x = (const uint8_t*)x;
   a.x_bytes = (int64_t)T * ctx->cfg.hidden * ctx->plan.act_bytes;
