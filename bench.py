@@ -117,6 +117,8 @@ def parse():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the decode run replayed from a captured HIP graph")
+    ap.add_argument("--no-calibrated", action="store_true",
+                    help="skip the decode run with B_P / B_H measured on this machine")
     ap.add_argument("--prefill-only", action="store_true",
                     help="run only the prefill leg (for profiling); prints its fields")
     ap.add_argument("--record-traffic", nargs=3, metavar=("KIND", "FETCH_DIR", "WRITE_DIR"),
@@ -340,9 +342,12 @@ def main():
           f"{wl.n_slots} slots, warmup {warmup} steps, timed {steps} steps", file=sys.stderr,
           flush=True)
 
-    def run(timing):
-        """Fresh context (cold cache), warmup steps, then the timed steps."""
+    def run(timing, prepare=None):
+        """Fresh context (cold cache), warmup steps, then the timed steps.
+        `prepare(ctx)` runs once on the fresh context first."""
         ctx = B.moe_create(make_cfg(timing), pool, pool_bytes)
+        if prepare is not None:
+            prepare(ctx)
 
         def step(s):
             for l in range(wl.L):
@@ -407,6 +412,24 @@ def main():
     dt, _, st0, st1 = run(0)
     dt_timed, tm, _, _ = run(1)
     dt_graph = run_graph() if not a.no_graph else None
+    # the same steps with B_P and B_H measured on this machine and the backend
+    # the pages' rule picks for them (instead of the configured numbers)
+    measured = {}
+
+    def calibrate(ctx):
+        bp, bh = B.moe_measure_bandwidth(ctx, 8, 5)
+        mode_m = B.moe_recommend_mode(bp, bh, 2.0)
+        B.moe_set_split(ctx, bp, bh, mode_m)
+        measured.update(bw_pcie_mbps=bp, bw_host_mbps=bh,
+                        recommended_mode={B.MOE_HYBRID: "hybrid", B.MOE_OFFLOAD: "offload"}[mode_m])
+
+    if not a.no_calibrated:
+        dt_m, _, sm0, sm1 = run(0, calibrate)
+        acc_m = (sm1.hits - sm0.hits) + (sm1.fills - sm0.fills) + (sm1.cpu - sm0.cpu)
+        measured.update(us_per_layer=round(dt_m / (steps * wl.L) * 1e6, 2),
+                        fills_per_layer=round((sm1.fills - sm0.fills) / (steps * wl.L), 3),
+                        cpu_experts_per_layer=round((sm1.cpu - sm0.cpu) / (steps * wl.L), 3),
+                        miss_rate=round(1 - (sm1.hits - sm0.hits) / max(acc_m, 1), 4))
     calls = steps * wl.L
     us_per_layer = dt / calls * 1e6
     n_gpu_experts = (st1.hits - st0.hits) + (st1.fills - st0.fills)
@@ -459,6 +482,7 @@ def main():
         "cpu_baseline": cpu,
         "breakdown_us_per_call": per,
         "breakdown_run_us_per_layer": round(dt_timed / (steps * wl.L) * 1e6, 2),
+        "calibrated_split": measured or None,
         "graph": ({"us_per_layer": round(dt_graph / (steps * wl.L) * 1e6, 2),
                    "note": "one captured HIP graph per step (all layers), inputs copied into its "
                            "buffers inside the timed region"} if dt_graph else None),

@@ -248,6 +248,37 @@ typedef struct {
 
 moe_status moe_ctx_stats(moe_ctx* ctx, moe_stats* out);
 
+/* Bandwidth calibration [snackonai, "The Code, Annotated": the two rates are
+ * measured once per machine on the deployed expert shapes, not taken from
+ * spec sheets; "The split policy itself": q uses exactly these two numbers].
+ * B_P: the fill kernel pulling n_experts whole experts from the pinned host
+ * banks into a scratch device buffer, reps timed launches after one untimed
+ * one (HIP events).  B_H: the host branch's own expert arithmetic on its
+ * worker pool, one token per expert, reps timed runs after one untimed one
+ * (wall clock).  Every run takes a different set of experts spread over the
+ * host pool (distinct while L*E >= n_experts*(reps+1)), so no cache serves
+ * bytes twice.  Both in MB/s of expert bytes
+ * (moe_expert_bytes without the slot padding).  Safe-point call: drains the
+ * context like moe_cache_resize (60 s limit, MOE_ETIMEDOUT), allocates and
+ * frees a scratch buffer of n_experts slots; the slot pool, the residency
+ * tables and the configured bandwidths are unchanged.  1 <= n_experts (capped
+ * at 64 and at L*E), 1 <= reps <= 1000.  Synchronous. */
+moe_status moe_measure_bandwidth(moe_ctx* ctx, int32_t n_experts, int32_t reps,
+                                 int64_t* bw_pcie_mbps, int64_t* bw_host_mbps);
+
+/* The backend rule [snackonai, "The Code, Annotated": recommend hybrid when
+ * B_H exceeds threshold x B_P, with threshold 2.0, else offload]: writes
+ * MOE_HYBRID or MOE_OFFLOAD to *out.  Pure host arithmetic, no context.
+ * MOE_EINVAL for non-positive bandwidths or threshold. */
+moe_status moe_recommend_mode(int64_t bw_pcie_mbps, int64_t bw_host_mbps, double threshold,
+                              moe_mode* out);
+
+/* Replace the bandwidths the control kernel splits misses with, and the mode
+ * (for example with measured values and the recommended backend).  Applies
+ * from the next moe_cache_plan; a graph captured earlier keeps the values it
+ * was captured with (capture again).  No layer call may be open. */
+moe_status moe_set_split(moe_ctx* ctx, int64_t bw_pcie_mbps, int64_t bw_host_mbps, moe_mode mode);
+
 /* Device time per phase, summed since creation (or the last reset), when the
  * context was created with cfg.timing = 1: each call brackets the kernels it
  * launches with a pair of HIP events on the stream they run on.  HOST is the

@@ -101,6 +101,9 @@ def lib():
             "moe_expert_ffn": ([vp, i32, vp, i32, vp], i32),
             "moe_merge": ([vp, vp, i32, vp, vp], i32),
             "moe_cache_resize": ([vp, i32, i32], i32),
+            "moe_measure_bandwidth": ([vp, i32, i32, ctypes.POINTER(i64), ctypes.POINTER(i64)], i32),
+            "moe_recommend_mode": ([i64, i64, ctypes.c_double, ctypes.POINTER(i32)], i32),
+            "moe_set_split": ([vp, i64, i64, i32], i32),
             "moe_prefill_layer": ([vp, i32, vp, i32, vp, vp, vp, vp], i32),
             "moe_plan_view_get": ([vp, ctypes.POINTER(PlanView)], i32),
             "moe_ctx_stats": ([vp, ctypes.POINTER(Stats)], i32),
@@ -196,6 +199,25 @@ def moe_merge(ctx, w, T, y, stream=None):
 
 def moe_cache_resize(ctx, new_n_slots, timeout_ms=300_000):
     _check(lib().moe_cache_resize(ctx, new_n_slots, timeout_ms), "moe_cache_resize")
+
+
+def moe_measure_bandwidth(ctx, n_experts=8, reps=5):
+    """(B_P, B_H) in MB/s, measured on the context's expert shape."""
+    bp, bh = ctypes.c_int64(), ctypes.c_int64()
+    _check(lib().moe_measure_bandwidth(ctx, n_experts, reps, ctypes.byref(bp), ctypes.byref(bh)),
+           "moe_measure_bandwidth")
+    return bp.value, bh.value
+
+
+def moe_recommend_mode(bw_pcie_mbps, bw_host_mbps, threshold=2.0):
+    m = ctypes.c_int32()
+    _check(lib().moe_recommend_mode(bw_pcie_mbps, bw_host_mbps, threshold, ctypes.byref(m)),
+           "moe_recommend_mode")
+    return m.value
+
+
+def moe_set_split(ctx, bw_pcie_mbps, bw_host_mbps, mode):
+    _check(lib().moe_set_split(ctx, bw_pcie_mbps, bw_host_mbps, mode), "moe_set_split")
 
 
 def moe_prefill_layer(ctx, layer, x, T, ids, w, y, stream=None):

@@ -303,12 +303,104 @@ bool host_branch_idle(moe_ctx* ctx) {
   return ctx->hb->last.load(std::memory_order_acquire) == *bell;
 }
 
+// The host branch's arithmetic: SwiGLU of the experts `ex` read in place from
+// the pinned host banks, on the worker pool.  Pair p takes its input from row
+// p / k of xf (fp32, MXFP4 nibble order) and writes its fp32 row to out + p*H.
+// Gate/up rows, then down rows, split evenly over the workers.
+static void host_eval(moe_ctx* ctx, const std::vector<Expert>& ex, const float* xf, int k, float* out,
+                      double* t_mid) {
+  const moe_config& c = ctx->cfg;
+  const int H = c.hidden, I = c.inter;
+  const int nex = (int)ex.size();
+  int max_pair = 0;
+  for (const Expert& X : ex)
+    for (int p : X.pairs) max_pair = std::max(max_pair, p + 1);
+  // intermediate h per pair, fp32 (MXFP4: nibble order per 32-block of I)
+  std::vector<float> hmid((size_t)max_pair * I);
+  const size_t stride = ctx->stride;
+  const uint8_t* pool = ctx->host_pool;
+  const size_t eb = c.w_dtype == MOE_F32 ? 4 : 2;
+
+  // phase 1: gate/up rows, split evenly over the workers
+  ctx->cpu->run([&](int wi, int nw) {
+    const int64_t R = (int64_t)nex * I;
+    const int64_t r0 = R * wi / nw, r1 = R * (wi + 1) / nw;
+    std::vector<const float*> xs;
+    std::vector<float> g, uu;
+    for (int64_t r = r0; r < r1; ++r) {
+      const Expert& X = ex[r / I];
+      const int row = (int)(r % I);
+      const int nt = (int)X.pairs.size();
+      xs.resize(nt);
+      g.resize(nt);
+      uu.resize(nt);
+      for (int t = 0; t < nt; ++t) xs[t] = xf + (size_t)(X.pairs[t] / k) * H;
+      const uint8_t* bank = pool + (size_t)X.u * stride;
+      if (c.w_dtype == MOE_MXFP4) {
+        const uint8_t* cg = bank + (size_t)row * (H / 2);
+        const uint8_t* cu = bank + (size_t)I * H / 2 + (size_t)row * (H / 2);
+        const uint8_t* sbase = bank + 3 * (size_t)H * I / 2;
+        dot_mx(cg, sbase + (size_t)row * (H / 32), xs.data(), nt, H, g.data());
+        dot_mx(cu, sbase + (size_t)I * H / 32 + (size_t)row * (H / 32), xs.data(), nt, H, uu.data());
+      } else if (c.w_dtype == MOE_BF16) {
+        const uint16_t* wg = (const uint16_t*)bank + (size_t)row * H;
+        const uint16_t* wu = (const uint16_t*)bank + (size_t)I * H + (size_t)row * H;
+        dot_bf16(wg, xs.data(), nt, H, g.data());
+        dot_bf16(wu, xs.data(), nt, H, uu.data());
+      } else {
+        const float* wg = (const float*)bank + (size_t)row * H;
+        const float* wu = (const float*)bank + (size_t)I * H + (size_t)row * H;
+        dot_f32(wg, xs.data(), nt, H, g.data());
+        dot_f32(wu, xs.data(), nt, H, uu.data());
+      }
+      for (int t = 0; t < nt; ++t) {
+        int col = row;
+        if (c.w_dtype == MOE_MXFP4) {  // store in nibble order for the down pass
+          const int b = row / 32, i = row % 32;
+          col = 32 * b + ((i & 1) ? 16 + i / 2 : i / 2);
+        }
+        hmid[(size_t)X.pairs[t] * I + col] = silu(g[t]) * uu[t];
+      }
+    }
+  });
+  (void)eb;
+  if (t_mid) *t_mid = now_us();
+  // phase 2: down rows
+  ctx->cpu->run([&](int wi, int nw) {
+    const int64_t R = (int64_t)nex * H;
+    const int64_t r0 = R * wi / nw, r1 = R * (wi + 1) / nw;
+    std::vector<const float*> hs;
+    std::vector<float> o;
+    for (int64_t r = r0; r < r1; ++r) {
+      const Expert& X = ex[r / H];
+      const int row = (int)(r % H);
+      const int nt = (int)X.pairs.size();
+      hs.resize(nt);
+      o.resize(nt);
+      for (int t = 0; t < nt; ++t) hs[t] = hmid.data() + (size_t)X.pairs[t] * I;
+      const uint8_t* bank = pool + (size_t)X.u * stride;
+      if (c.w_dtype == MOE_MXFP4) {
+        const uint8_t* cd = bank + (size_t)I * H + (size_t)row * (I / 2);
+        const uint8_t* sd = bank + 3 * (size_t)H * I / 2 + 2 * (size_t)I * H / 32 + (size_t)row * (I / 32);
+        dot_mx(cd, sd, hs.data(), nt, I, o.data());
+      } else if (c.w_dtype == MOE_BF16) {
+        const uint16_t* wd = (const uint16_t*)bank + 2 * (size_t)I * H + (size_t)row * I;
+        dot_bf16(wd, hs.data(), nt, I, o.data());
+      } else {
+        const float* wd = (const float*)bank + 2 * (size_t)I * H + (size_t)row * I;
+        dot_f32(wd, hs.data(), nt, I, o.data());
+      }
+      for (int t = 0; t < nt; ++t) out[(size_t)X.pairs[t] * H + row] = o[t];
+    }
+  });
+}
+
 static void cpu_branch_body(moe_ctx* ctx) {
   const moe_config& c = ctx->cfg;
   const HostBlockHeader* hb = (const HostBlockHeader*)ctx->hstage;
   const int n_cpu = hb->c.n_cpu;
   const int T = hb->T, k = c.top_k, layer = hb->layer, E = c.n_experts;
-  const int H = c.hidden, I = c.inter;
+  const int H = c.hidden;
   const int Tk = T * k;
   const int32_t* ids = (const int32_t*)(ctx->hstage + sizeof(HostBlockHeader));
   const int32_t* smap = ids + Tk;
@@ -361,84 +453,7 @@ static void cpu_branch_body(moe_ctx* ctx) {
       }
     }
   }
-  // intermediate h per pair, fp32 (MXFP4: nibble order per 32-block of I)
-  std::vector<float> hmid((size_t)Tk * I);
-  const size_t stride = ctx->stride;
-  const uint8_t* pool = ctx->host_pool;
-  const size_t eb = c.w_dtype == MOE_F32 ? 4 : 2;
-
-  // phase 1: gate/up rows, split evenly over the workers
-  ctx->cpu->run([&](int wi, int nw) {
-    const int64_t R = (int64_t)nex * I;
-    const int64_t r0 = R * wi / nw, r1 = R * (wi + 1) / nw;
-    std::vector<const float*> xs;
-    std::vector<float> g, uu;
-    for (int64_t r = r0; r < r1; ++r) {
-      const Expert& X = ex[r / I];
-      const int row = (int)(r % I);
-      const int nt = (int)X.pairs.size();
-      xs.resize(nt);
-      g.resize(nt);
-      uu.resize(nt);
-      for (int t = 0; t < nt; ++t) xs[t] = xf.data() + (size_t)(X.pairs[t] / k) * H;
-      const uint8_t* bank = pool + (size_t)X.u * stride;
-      if (c.w_dtype == MOE_MXFP4) {
-        const uint8_t* cg = bank + (size_t)row * (H / 2);
-        const uint8_t* cu = bank + (size_t)I * H / 2 + (size_t)row * (H / 2);
-        const uint8_t* sbase = bank + 3 * (size_t)H * I / 2;
-        dot_mx(cg, sbase + (size_t)row * (H / 32), xs.data(), nt, H, g.data());
-        dot_mx(cu, sbase + (size_t)I * H / 32 + (size_t)row * (H / 32), xs.data(), nt, H, uu.data());
-      } else if (c.w_dtype == MOE_BF16) {
-        const uint16_t* wg = (const uint16_t*)bank + (size_t)row * H;
-        const uint16_t* wu = (const uint16_t*)bank + (size_t)I * H + (size_t)row * H;
-        dot_bf16(wg, xs.data(), nt, H, g.data());
-        dot_bf16(wu, xs.data(), nt, H, uu.data());
-      } else {
-        const float* wg = (const float*)bank + (size_t)row * H;
-        const float* wu = (const float*)bank + (size_t)I * H + (size_t)row * H;
-        dot_f32(wg, xs.data(), nt, H, g.data());
-        dot_f32(wu, xs.data(), nt, H, uu.data());
-      }
-      for (int t = 0; t < nt; ++t) {
-        int col = row;
-        if (c.w_dtype == MOE_MXFP4) {  // store in nibble order for the down pass
-          const int b = row / 32, i = row % 32;
-          col = 32 * b + ((i & 1) ? 16 + i / 2 : i / 2);
-        }
-        hmid[(size_t)X.pairs[t] * I + col] = silu(g[t]) * uu[t];
-      }
-    }
-  });
-  (void)eb;
-  if (g_trace.on) t_p1 = now_us();
-  // phase 2: down rows
-  ctx->cpu->run([&](int wi, int nw) {
-    const int64_t R = (int64_t)nex * H;
-    const int64_t r0 = R * wi / nw, r1 = R * (wi + 1) / nw;
-    std::vector<const float*> hs;
-    std::vector<float> o;
-    for (int64_t r = r0; r < r1; ++r) {
-      const Expert& X = ex[r / H];
-      const int row = (int)(r % H);
-      const int nt = (int)X.pairs.size();
-      hs.resize(nt);
-      o.resize(nt);
-      for (int t = 0; t < nt; ++t) hs[t] = hmid.data() + (size_t)X.pairs[t] * I;
-      const uint8_t* bank = pool + (size_t)X.u * stride;
-      if (c.w_dtype == MOE_MXFP4) {
-        const uint8_t* cd = bank + (size_t)I * H + (size_t)row * (I / 2);
-        const uint8_t* sd = bank + 3 * (size_t)H * I / 2 + 2 * (size_t)I * H / 32 + (size_t)row * (I / 32);
-        dot_mx(cd, sd, hs.data(), nt, I, o.data());
-      } else if (c.w_dtype == MOE_BF16) {
-        const uint16_t* wd = (const uint16_t*)bank + 2 * (size_t)I * H + (size_t)row * I;
-        dot_bf16(wd, hs.data(), nt, I, o.data());
-      } else {
-        const float* wd = (const float*)bank + 2 * (size_t)I * H + (size_t)row * I;
-        dot_f32(wd, hs.data(), nt, I, o.data());
-      }
-      for (int t = 0; t < nt; ++t) ctx->p_cpu[(size_t)X.pairs[t] * H + row] = o[t];
-    }
-  });
+  host_eval(ctx, ex, xf.data(), k, ctx->p_cpu, g_trace.on ? &t_p1 : nullptr);
   if (g_trace.on) {
     t_p2 = now_us();
     HostTrace& tr = g_trace;
@@ -452,6 +467,30 @@ static void cpu_branch_body(moe_ctx* ctx) {
               "down %.1f us per call (%d threads)\n", (long long)tr.calls,
               (double)tr.experts / tr.calls, tr.p1 / tr.calls, tr.p2 / tr.calls, ctx->cpu_threads);
   }
+}
+
+// Seconds per evaluation of n experts (one token each, all reading the same
+// input row) by the host branch's arithmetic: set r is us[r*n .. r*n+n), set 0
+// untimed, sets 1..reps timed and averaged (distinct sets, so the host caches
+// do not serve repeated bytes).  The caller guarantees the host branch is idle.
+double host_expert_seconds(moe_ctx* ctx, const int32_t* us, int n, int reps) {
+  const int H = ctx->cfg.hidden;
+  std::vector<float> xf((size_t)H), out((size_t)n * H);
+  for (int h = 0; h < H; ++h) xf[h] = 0.01f * (float)((h * 37) % 101 - 50);
+  auto set = [&](int r) {
+    std::vector<Expert> ex;
+    for (int i = 0; i < n; ++i) ex.push_back({us[r * n + i], {i}});
+    return ex;
+  };
+  host_eval(ctx, set(0), xf.data(), n, out.data(), nullptr);
+  double total = 0.0;
+  for (int r = 1; r <= reps; ++r) {
+    const std::vector<Expert> ex = set(r);
+    const auto t0 = std::chrono::steady_clock::now();
+    host_eval(ctx, ex, xf.data(), n, out.data(), nullptr);
+    total += std::chrono::duration<double>(std::chrono::steady_clock::now() - t0).count();
+  }
+  return total / reps;
 }
 
 }  // namespace moert

@@ -5,6 +5,7 @@
 
 #include <algorithm>
 #include <chrono>
+#include <cmath>
 #include <cstdio>
 #include <cstdlib>
 #include <thread>
@@ -703,6 +704,85 @@ extern "C" moe_status moe_cache_resize(moe_ctx* ctx, int32_t new_n, int32_t time
   // resize drained the copy stream: an unconsumed prefetch is simply gone
   // (its slots were emptied above unless admitted)
   ctx->pf.buf_layer[0] = ctx->pf.buf_layer[1] = -1;
+  return MOE_OK;
+}
+
+// ------------------------------------------------------------------ bandwidths
+extern "C" moe_status moe_measure_bandwidth(moe_ctx* ctx, int32_t n_experts, int32_t reps,
+                                            int64_t* bw_pcie_mbps, int64_t* bw_host_mbps) {
+  CHECK_CTX(ctx);
+  if (!bw_pcie_mbps || !bw_host_mbps || n_experts < 1 || reps < 1 || reps > 1000)
+    return fail(ctx, MOE_EINVAL, "moe_measure_bandwidth: bad arguments");
+  if (ctx->state != kIdle) return fail(ctx, MOE_EINVAL, "moe_measure_bandwidth: a layer call is open");
+  moe_status st = drain(ctx, 60000);
+  if (st != MOE_OK) return st;
+  const int n = (int)std::min<int64_t>({(int64_t)n_experts, ctx->n_ids, 64});
+  // reps + 1 sets of n experts spread over the host pool, distinct while the
+  // pool has enough ids, so neither side re-reads bytes a cache may hold
+  const int64_t total = (int64_t)n * (reps + 1);
+  std::vector<int32_t> us(total), slots(n);
+  for (int64_t i = 0; i < total; ++i)
+    us[i] = (int32_t)(total <= ctx->n_ids ? i * ctx->n_ids / total : i % ctx->n_ids);
+  for (int i = 0; i < n; ++i) slots[i] = i;
+  const double bytes = (double)n * (double)ctx->expert_bytes;
+
+  // PCIe: the fill kernel pulling each set into a scratch device buffer (the
+  // slot pool and the tables are not touched)
+  const size_t o_cnt = (size_t)n * ctx->stride, o_fs = o_cnt + 256, o_fu = o_fs + 256;
+  uint8_t* buf = nullptr;
+  MOE_HIP(ctx, hipMalloc(&buf, o_fu + 4 * (size_t)total));
+  moe_plan_counts cnt{};
+  cnt.q = n;
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  float ms = 0.f;
+  hipError_t e = hipMemcpy(buf + o_cnt, &cnt, sizeof cnt, hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipMemcpy(buf + o_fu, us.data(), 4 * (size_t)total, hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipMemcpy(buf + o_fs, slots.data(), 4 * (size_t)n, hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipEventCreate(&e0);
+  if (e == hipSuccess) e = hipEventCreate(&e1);
+  auto pull = [&](int r) {
+    return launch_fill_lists(ctx->host_pool_dev, buf, ctx->stride, (const moe_plan_counts*)(buf + o_cnt),
+                             (const int32_t*)(buf + o_fu) + (size_t)r * n, (const int32_t*)(buf + o_fs),
+                             ctx->copy);
+  };
+  if (e == hipSuccess) e = pull(0);  // untimed
+  if (e == hipSuccess) e = hipEventRecord(e0, ctx->copy);
+  for (int r = 1; r <= reps && e == hipSuccess; ++r) e = pull(r);
+  if (e == hipSuccess) e = hipEventRecord(e1, ctx->copy);
+  if (e == hipSuccess) e = hipEventSynchronize(e1);
+  if (e == hipSuccess) e = hipEventElapsedTime(&ms, e0, e1);
+  if (e0) (void)hipEventDestroy(e0);
+  if (e1) (void)hipEventDestroy(e1);
+  (void)hipFree(buf);
+  if (e != hipSuccess) return hip_fail(ctx, e, "moe_measure_bandwidth (PCIe pull)");
+  const double pcie = bytes * reps / (ms * 1e-3) / 1e6;
+
+  // host: the host branch's expert arithmetic on its worker pool
+  const double secs = host_expert_seconds(ctx, us.data(), n, reps);
+  const double host = bytes / secs / 1e6;
+  *bw_pcie_mbps = std::max<int64_t>(1, (int64_t)std::llround(pcie));
+  *bw_host_mbps = std::max<int64_t>(1, (int64_t)std::llround(host));
+  return MOE_OK;
+}
+
+extern "C" moe_status moe_recommend_mode(int64_t bw_pcie_mbps, int64_t bw_host_mbps, double threshold,
+                                         moe_mode* out) {
+  if (!out || bw_pcie_mbps <= 0 || bw_host_mbps <= 0 || !(threshold > 0.0))
+    return fail(nullptr, MOE_EINVAL, "moe_recommend_mode: bad arguments");
+  *out = (double)bw_host_mbps > threshold * (double)bw_pcie_mbps ? MOE_HYBRID : MOE_OFFLOAD;
+  return MOE_OK;
+}
+
+extern "C" moe_status moe_set_split(moe_ctx* ctx, int64_t bw_pcie_mbps, int64_t bw_host_mbps,
+                                    moe_mode mode) {
+  CHECK_CTX(ctx);
+  if (bw_pcie_mbps <= 0 || bw_host_mbps <= 0 || bw_pcie_mbps > (int64_t)1 << 40 ||
+      bw_host_mbps > (int64_t)1 << 40 || mode < MOE_HYBRID || mode > MOE_CPU)
+    return fail(ctx, MOE_EINVAL, "moe_set_split: bad arguments");
+  if (ctx->state != kIdle) return fail(ctx, MOE_EINVAL, "moe_set_split: a layer call is open");
+  ctx->cfg.bw_pcie_mbps = bw_pcie_mbps;
+  ctx->cfg.bw_host_mbps = bw_host_mbps;
+  ctx->cfg.mode = mode;
   return MOE_OK;
 }
 

@@ -53,11 +53,18 @@ __global__ __launch_bounds__(256) void fill_kernel(const uint8_t* __restrict__ h
   }
 }
 
+hipError_t launch_fill_lists(const uint8_t* host_dev, uint8_t* dst, size_t stride,
+                             const moe_plan_counts* counts, const int32_t* fill_u,
+                             const int32_t* fill_slot, hipStream_t s) {
+  hipLaunchKernelGGL(fill_kernel, dim3(64), dim3(256), 0, s, host_dev, dst, stride, counts, fill_u,
+                     fill_slot);
+  return hipGetLastError();
+}
+
 hipError_t launch_fill(moe_ctx* ctx, hipStream_t s) {
   if (ctx->n_slots == 0 || ctx->cfg.mode == MOE_CPU) return hipSuccess;
-  hipLaunchKernelGGL(fill_kernel, dim3(64), dim3(256), 0, s, ctx->host_pool_dev, ctx->pool.base,
-                     ctx->stride, ctx->plan.counts, ctx->plan.fill_u, ctx->plan.fill_slot);
-  return hipGetLastError();
+  return launch_fill_lists(ctx->host_pool_dev, ctx->pool.base, ctx->stride, ctx->plan.counts,
+                           ctx->plan.fill_u, ctx->plan.fill_slot, s);
 }
 
 // ------------------------------------------------------------------ expert FFN

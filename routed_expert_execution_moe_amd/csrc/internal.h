@@ -196,6 +196,12 @@ hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* 
 hipError_t launch_plan(moe_ctx* ctx, int layer, const int32_t* ids, int T, const void* x,
                        hipStream_t s);
 hipError_t launch_fill(moe_ctx* ctx, hipStream_t s);
+// the fill kernel on explicit lists: q = counts->q experts fill_u[i] of the
+// mapped host banks to dst + fill_slot[i] * stride
+hipError_t launch_fill_lists(const uint8_t* host_dev, uint8_t* dst, size_t stride,
+                             const moe_plan_counts* counts, const int32_t* fill_u,
+                             const int32_t* fill_slot, hipStream_t s);
+double host_expert_seconds(moe_ctx* ctx, const int32_t* us, int n, int reps);
 hipError_t launch_ffn(moe_ctx* ctx, const void* x, int T, hipStream_t s);
 hipError_t launch_ffn_f32(moe_ctx* ctx, const void* x, int T, hipStream_t s);
 hipError_t launch_ffn_bf16(moe_ctx* ctx, const void* x, int T, hipStream_t s);

@@ -71,3 +71,35 @@ def test_strerror(lib):
     for s in range(0, -8, -1):
         assert lib.moe_strerror(s)
     assert b"unknown" in lib.moe_strerror(-99)
+
+
+def test_recommend_mode_matches_the_pages_rule(lib, golden_dir):
+    """moe_recommend_mode (host arithmetic, no GPU) against the oracle's rule,
+    which is pinned to the six machines of the pages' calibration table: the
+    six rows, ties (B_H exactly 2 B_P stays offload), random pairs, bad input."""
+    import json
+    import random
+    from oracle import costmodel
+    f = lib.moe_recommend_mode
+    f.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_double, ctypes.POINTER(ctypes.c_int32)]
+    f.restype = ctypes.c_int32
+    HYBRID, OFFLOAD = 0, 1
+
+    def rec(bp, bh, th=2.0):
+        out = ctypes.c_int32(-1)
+        assert f(bp, bh, th, ctypes.byref(out)) == 0
+        return out.value
+
+    g = json.load(open(os.path.join(golden_dir, "split_policy.json")))
+    for row in g["bw_table"]:
+        bp, bh = int(round(row["bp"] * 1000)), int(round(row["bh"] * 1000))
+        assert rec(bp, bh, g["threshold"]) == (HYBRID if row["backend"] == "hybrid" else OFFLOAD), row
+    assert rec(25_000, 50_000) == OFFLOAD and rec(25_000, 50_001) == HYBRID
+    r = random.Random(7)
+    for _ in range(2000):
+        bp, bh, th = r.randint(1, 200_000), r.randint(1, 400_000), r.choice([1.0, 1.5, 2.0, 3.0])
+        want = HYBRID if costmodel.recommend_hybrid(bp, bh, th) else OFFLOAD
+        assert rec(bp, bh, th) == want, (bp, bh, th)
+    out = ctypes.c_int32()
+    for bad in ((0, 1, 2.0), (1, 0, 2.0), (1, 1, 0.0), (1, 1, -1.0)):
+        assert f(*bad, ctypes.byref(out)) == -1
