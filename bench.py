@@ -52,18 +52,21 @@ def _sources_sha(kind):
     return h.hexdigest()
 
 
-def recorded_traffic(kind):
+def recorded_traffic(kind, workload):
     """HBM bytes per launch from the committed counter record, or None when
-    there is none or the kernel's source changed since it was taken."""
+    there is none, it was taken on another workload, or the kernel's source
+    changed since it was taken."""
     try:
         with open(TRAFFIC_FILE) as fh:
             t = json.load(fh)[kind]
     except (OSError, KeyError, ValueError):
         return None
-    return t["bytes_per_launch"] if t.get("sha256") == _sources_sha(kind) else None
+    if t.get("workload") != workload or t.get("sha256") != _sources_sha(kind):
+        return None
+    return t["bytes_per_launch"]
 
 
-def record_traffic(kind, fetch_dir, write_dir):
+def record_traffic(kind, workload, fetch_dir, write_dir):
     """Write profiles/traffic.json[kind] from two rocprofv3 --pmc runs (one with
     FETCH_SIZE, one with WRITE_SIZE) of this bench: HBM bytes per dispatch of
     each of the kind's kernels, summed over them (the decode FFN is one
@@ -90,7 +93,7 @@ def record_traffic(kind, fetch_dir, write_dir):
             t = json.load(fh)
     except (OSError, ValueError):
         t = {}
-    t[kind] = {"bytes_per_launch": round(total), "sha256": _sources_sha(kind),
+    t[kind] = {"bytes_per_launch": round(total), "sha256": _sources_sha(kind), "workload": workload,
                "kernels": {k: {"fetch_kib": round(fetch.get(k, 0), 1),
                                "write_kib": round(write.get(k, 0), 1)} for k in sorted(set(fetch) | set(write))},
                "scale": {"FETCH_SIZE": FETCH_SCALE, "WRITE_SIZE": WRITE_SCALE}}
@@ -119,11 +122,15 @@ def parse():
                     help="skip the decode run replayed from a captured HIP graph")
     ap.add_argument("--no-calibrated", action="store_true",
                     help="skip the decode run with B_P / B_H measured on this machine")
+    ap.add_argument("--bw-profile", default=None, metavar="PATH",
+                    help="also store the measured bandwidths in this JSON profile (keyed on "
+                         "expert format + GPU name)")
     ap.add_argument("--prefill-only", action="store_true",
                     help="run only the prefill leg (for profiling); prints its fields")
     ap.add_argument("--record-traffic", nargs=3, metavar=("KIND", "FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/traffic.json[KIND] (decode_ffn | prefill_gemm) from the "
-                         "counter CSVs of a FETCH_SIZE run and a WRITE_SIZE run of this bench")
+                         "counter CSVs of a FETCH_SIZE run and a WRITE_SIZE run of this bench "
+                         "(decode: on --workload; prefill: its prefill workload)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain streaming kernel of known size, whose "
                          "FETCH_SIZE / WRITE_SIZE counter readings scale those counters to bytes")
@@ -189,7 +196,7 @@ def bench_prefill():
                                  "MXFP4 dequantised in registers)", "achieved": round(tflops, 1),
                                  "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                                  "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
-                                 "traffic": recorded_traffic("prefill_gemm")},
+                                 "traffic": recorded_traffic("prefill_gemm", wl.name)},
             "prefill_gemm_ms_per_layer": round(gemm_ms / wl.L, 3),
             "prefill_group_ms_per_layer": round(tm["prefill_group"]["ms"] / wl.L, 3),
             "prefill_merge_ms_per_layer": round(tm["prefill_merge"]["ms"] / wl.L, 3),
@@ -297,7 +304,10 @@ def main():
         return
     if a.record_traffic:
         kind, fd, wd = a.record_traffic
-        print(json.dumps(record_traffic(kind, fd, wd)), flush=True)
+        # the counter runs were of the default bench: the decode workload the
+        # default run times, or the prefill workload of its prefill leg
+        wname = W.DSV4_PREFILL.name if kind == "prefill_gemm" else a.workload
+        print(json.dumps(record_traffic(kind, wname, fd, wd)), flush=True)
         return
     if a.copy_calibration:
         print(json.dumps(copy_calibration()), flush=True)
@@ -417,11 +427,14 @@ def main():
     measured = {}
 
     def calibrate(ctx):
-        bp, bh = B.moe_measure_bandwidth(ctx, 8, 5)
-        mode_m = B.moe_recommend_mode(bp, bh, 2.0)
-        B.moe_set_split(ctx, bp, bh, mode_m)
-        measured.update(bw_pcie_mbps=bp, bw_host_mbps=bh,
-                        recommended_mode={B.MOE_HYBRID: "hybrid", B.MOE_OFFLOAD: "offload"}[mode_m])
+        from routed_expert_execution_moe_amd import bw_profile
+        prof = bw_profile.measure(ctx, wl.w_dtype, torch.cuda.get_device_name(0), 8, 5, 2.0)
+        if a.bw_profile:
+            bw_profile.save(a.bw_profile, prof)
+        mode_m = B.MOE_HYBRID if prof["backend"] == "hybrid" else B.MOE_OFFLOAD
+        B.moe_set_split(ctx, prof["bw_pcie_mbps"], prof["bw_host_mbps"], mode_m)
+        measured.update(bw_pcie_mbps=prof["bw_pcie_mbps"], bw_host_mbps=prof["bw_host_mbps"],
+                        bw_h2d_mbps=prof["bw_h2d_mbps"], recommended_mode=prof["backend"])
 
     if not a.no_calibrated:
         dt_m, _, sm0, sm1 = run(0, calibrate)
@@ -477,7 +490,7 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(ffn_gbps / HBM_PEAK_GBPS, 4) if ffn_gbps else None,
-            "traffic": recorded_traffic("decode_ffn"),
+            "traffic": recorded_traffic("decode_ffn", wl.name),
         },
         "cpu_baseline": cpu,
         "breakdown_us_per_call": per,

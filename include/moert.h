@@ -257,14 +257,16 @@ moe_status moe_ctx_stats(moe_ctx* ctx, moe_stats* out);
  * worker pool, one token per expert, reps timed runs after one untimed one
  * (wall clock).  Every run takes a different set of experts spread over the
  * host pool (distinct while L*E >= n_experts*(reps+1)), so no cache serves
- * bytes twice.  Both in MB/s of expert bytes
- * (moe_expert_bytes without the slot padding).  Safe-point call: drains the
+ * bytes twice.  If bw_h2d_mbps is not NULL, the same sets are also copied
+ * with pinned host-to-device copies (the copy engines, one per expert) and
+ * that rate is written there too (the fill itself uses the pull).  All in
+ * MB/s of expert bytes (moe_expert_bytes without the slot padding).  Safe-point call: drains the
  * context like moe_cache_resize (60 s limit, MOE_ETIMEDOUT), allocates and
  * frees a scratch buffer of n_experts slots; the slot pool, the residency
  * tables and the configured bandwidths are unchanged.  1 <= n_experts (capped
  * at 64 and at L*E), 1 <= reps <= 1000.  Synchronous. */
 moe_status moe_measure_bandwidth(moe_ctx* ctx, int32_t n_experts, int32_t reps,
-                                 int64_t* bw_pcie_mbps, int64_t* bw_host_mbps);
+                                 int64_t* bw_pcie_mbps, int64_t* bw_host_mbps, int64_t* bw_h2d_mbps);
 
 /* The backend rule [snackonai, "The Code, Annotated": recommend hybrid when
  * B_H exceeds threshold x B_P, with threshold 2.0, else offload]: writes

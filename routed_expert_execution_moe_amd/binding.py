@@ -101,7 +101,8 @@ def lib():
             "moe_expert_ffn": ([vp, i32, vp, i32, vp], i32),
             "moe_merge": ([vp, vp, i32, vp, vp], i32),
             "moe_cache_resize": ([vp, i32, i32], i32),
-            "moe_measure_bandwidth": ([vp, i32, i32, ctypes.POINTER(i64), ctypes.POINTER(i64)], i32),
+            "moe_measure_bandwidth": ([vp, i32, i32, ctypes.POINTER(i64), ctypes.POINTER(i64),
+                                      ctypes.POINTER(i64)], i32),
             "moe_recommend_mode": ([i64, i64, ctypes.c_double, ctypes.POINTER(i32)], i32),
             "moe_set_split": ([vp, i64, i64, i32], i32),
             "moe_prefill_layer": ([vp, i32, vp, i32, vp, vp, vp, vp], i32),
@@ -201,12 +202,13 @@ def moe_cache_resize(ctx, new_n_slots, timeout_ms=300_000):
     _check(lib().moe_cache_resize(ctx, new_n_slots, timeout_ms), "moe_cache_resize")
 
 
-def moe_measure_bandwidth(ctx, n_experts=8, reps=5):
-    """(B_P, B_H) in MB/s, measured on the context's expert shape."""
-    bp, bh = ctypes.c_int64(), ctypes.c_int64()
-    _check(lib().moe_measure_bandwidth(ctx, n_experts, reps, ctypes.byref(bp), ctypes.byref(bh)),
-           "moe_measure_bandwidth")
-    return bp.value, bh.value
+def moe_measure_bandwidth(ctx, n_experts=8, reps=5, h2d=False):
+    """(B_P, B_H) in MB/s, measured on the context's expert shape; with
+    h2d=True also the pinned host-to-device copy rate: (B_P, B_H, B_H2D)."""
+    bp, bh, bc = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+    _check(lib().moe_measure_bandwidth(ctx, n_experts, reps, ctypes.byref(bp), ctypes.byref(bh),
+                                       ctypes.byref(bc) if h2d else None), "moe_measure_bandwidth")
+    return (bp.value, bh.value, bc.value) if h2d else (bp.value, bh.value)
 
 
 def moe_recommend_mode(bw_pcie_mbps, bw_host_mbps, threshold=2.0):

@@ -709,7 +709,8 @@ extern "C" moe_status moe_cache_resize(moe_ctx* ctx, int32_t new_n, int32_t time
 
 // ------------------------------------------------------------------ bandwidths
 extern "C" moe_status moe_measure_bandwidth(moe_ctx* ctx, int32_t n_experts, int32_t reps,
-                                            int64_t* bw_pcie_mbps, int64_t* bw_host_mbps) {
+                                            int64_t* bw_pcie_mbps, int64_t* bw_host_mbps,
+                                            int64_t* bw_h2d_mbps) {
   CHECK_CTX(ctx);
   if (!bw_pcie_mbps || !bw_host_mbps || n_experts < 1 || reps < 1 || reps > 1000)
     return fail(ctx, MOE_EINVAL, "moe_measure_bandwidth: bad arguments");
@@ -751,6 +752,24 @@ extern "C" moe_status moe_measure_bandwidth(moe_ctx* ctx, int32_t n_experts, int
   if (e == hipSuccess) e = hipEventRecord(e1, ctx->copy);
   if (e == hipSuccess) e = hipEventSynchronize(e1);
   if (e == hipSuccess) e = hipEventElapsedTime(&ms, e0, e1);
+  // the same sets as pinned host-to-device copies (the copy engines), one per expert
+  float ms_h2d = 0.f;
+  if (bw_h2d_mbps) {
+    auto copy_set = [&](int r) {
+      hipError_t ce = hipSuccess;
+      for (int i = 0; i < n && ce == hipSuccess; ++i)
+        ce = hipMemcpyAsync(buf + (size_t)i * ctx->stride,
+                            ctx->host_pool + (size_t)us[(size_t)r * n + i] * ctx->stride, ctx->expert_bytes,
+                            hipMemcpyHostToDevice, ctx->copy);
+      return ce;
+    };
+    if (e == hipSuccess) e = copy_set(0);
+    if (e == hipSuccess) e = hipEventRecord(e0, ctx->copy);
+    for (int r = 1; r <= reps && e == hipSuccess; ++r) e = copy_set(r);
+    if (e == hipSuccess) e = hipEventRecord(e1, ctx->copy);
+    if (e == hipSuccess) e = hipEventSynchronize(e1);
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms_h2d, e0, e1);
+  }
   if (e0) (void)hipEventDestroy(e0);
   if (e1) (void)hipEventDestroy(e1);
   (void)hipFree(buf);
@@ -761,6 +780,7 @@ extern "C" moe_status moe_measure_bandwidth(moe_ctx* ctx, int32_t n_experts, int
   const double secs = host_expert_seconds(ctx, us.data(), n, reps);
   const double host = bytes / secs / 1e6;
   *bw_pcie_mbps = std::max<int64_t>(1, (int64_t)std::llround(pcie));
+  if (bw_h2d_mbps) *bw_h2d_mbps = std::max<int64_t>(1, (int64_t)std::llround(bytes * reps / (ms_h2d * 1e-3) / 1e6));
   *bw_host_mbps = std::max<int64_t>(1, (int64_t)std::llround(host));
   return MOE_OK;
 }
