@@ -140,9 +140,10 @@ def parse():
 def bench_prefill():
     """One untimed pass and one timed pass of the DeepSeek-shaped MXFP4
     prefill chunk (8 layers x 8,192 tokens, two full-layer buffers of 256
-    experts, the next layer's slab streamed while the current one computes).
-    Returns the grouped-GEMM TFLOP/s (HIP events around the two GEMM kernels),
-    the wall time per layer and the slab copy rate."""
+    experts, the next layer's slab streamed while the current one computes),
+    then one timed pass with one buffer.  Returns the grouped-GEMM TFLOP/s
+    (HIP events around the two GEMM kernels), the wall time per layer, the
+    slab copy rate and the one-buffer wall time."""
     import ctypes  # noqa: F401
 
     import numpy as np
@@ -183,6 +184,15 @@ def bench_prefill():
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
         tm = B.moe_ctx_timing(ctx)
+        # the ablation with the second full-layer buffer disabled: each
+        # layer's slab copy waits for the previous layer's compute
+        B.moe_prefill_set_buffers(ctx, 1)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        one_pass()
+        torch.cuda.synchronize()
+        wall1 = time.perf_counter() - t0
+        B.moe_prefill_set_buffers(ctx, 2)
         flops = wl.L * 6.0 * wl.H * wl.I * wl.T * wl.k
         gemm_ms = tm["prefill_gemm"]["ms"]
         tflops = flops / (gemm_ms * 1e-3) / 1e12
@@ -203,6 +213,8 @@ def bench_prefill():
             "prefill_layer_ms": round(wall / wl.L * 1e3, 3),
             "prefill_chunk_tok_s": round(wl.T / wall, 1),
             "prefill_copy_gbps": round(slab * copies / (copy_ms * 1e-3) / 1e9, 1) if copy_ms else None,
+            "prefill_single_buffer": {"layer_ms": round(wall1 / wl.L * 1e3, 3),
+                                      "penalty_pct": round((wall1 / wall - 1.0) * 100, 1)},
         }
     finally:
         if ctx:

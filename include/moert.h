@@ -189,10 +189,12 @@ moe_status moe_merge(moe_ctx* ctx, const float* w, int32_t T, void* y, moe_strea
 moe_status moe_cache_resize(moe_ctx* ctx, int32_t new_n_slots, int32_t timeout_ms);
 
 /* One prefill chunk of MoE layer `layer` [satyajit, "Prefill: hide the pool
- * behind the wire"; son]: two full-layer buffers are slots [0,E) and [E,2E)
- * of the shared pool; layer l runs out of buffer l%2 while a copy stream
- * streams every expert of layer l+1 into the other buffer with one
- * hipMemcpyAsync from the pinned host pool.  The residency tables record the
+ * behind the wire"; snackonai, "It In Action"]: two full-layer buffers are
+ * slots [0,E) and [E,2E) of the shared pool; layer l runs out of buffer l%2
+ * while a copy stream streams every expert of layer l+1 into the other
+ * buffer with one hipMemcpyAsync from the pinned host pool (with one buffer,
+ * see moe_prefill_set_buffers, every layer uses slots [0,E) and its copy
+ * starts after the previous layer's compute).  The residency tables record the
  * buffer's experts as ordinary slots (one tick per layer), so what survives
  * seeds decode.  Tokens are grouped by expert and evaluated with an MFMA
  * grouped GEMM; y[t] = sum over ascending j of w[t][j] * FFN(x[t]).
@@ -200,10 +202,18 @@ moe_status moe_cache_resize(moe_ctx* ctx, int32_t new_n_slots, int32_t timeout_m
  * [T][k]; y (device) [T][H].  1 <= T <= max_prefill_tokens.
  * Supported for MXFP4 experts with bf16 activations, H % 256 == 0 and
  * I % 128 == 0 (MOE_EUNSUPPORTED otherwise).
- * MOE_ENOSPC if n_slots < 2E (the pages fall back to on-demand loading
- * instead of oversubscribing; that fallback is not provided). */
+ * MOE_ENOSPC if n_slots < buffers x E (the pages fall back to on-demand
+ * loading instead of oversubscribing; that fallback is not provided). */
 moe_status moe_prefill_layer(moe_ctx* ctx, int32_t layer, const void* x, int32_t T,
                              const int32_t* ids, const float* w, void* y, moe_stream stream);
+
+/* Full-layer buffers for prefill: 2 (default; the next layer streams while
+ * this one computes) or 1 (the ablation the pages measure by disabling the
+ * second buffer [snackonai, "It In Action"]: each layer's copy waits for the
+ * previous layer's compute, and n_slots >= E suffices).  MOE_EBUSY while a
+ * prefetched slab is pending (between two prefill layers of a chunk); call it
+ * before a chunk's first layer or after a decode call. */
+moe_status moe_prefill_set_buffers(moe_ctx* ctx, int32_t n_buffers);
 
 /* Device addresses of the last plan's fixed-shape outputs and of the
  * residency tables (for inspection and tests; reading them requires the

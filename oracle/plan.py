@@ -196,19 +196,21 @@ def resize(st: Residency, n_new: int):
     return moves
 
 
-def prefill_admit(st: Residency, layer: int, E: int):
+def prefill_admit(st: Residency, layer: int, E: int, buffers: int = 2):
     """Full-layer buffer admission for prefill (satyajit, "Prefill: hide the
     pool behind the wire"; signalovernoise essay).  Two full-layer buffers
     come out of the shared pool; reading: they are slots [0, E) and [E, 2E),
     layer l uses buffer l mod 2, expert e of layer l sits in slot b*E + e with
     one tick per prefill layer; the buffer's previous occupants are evicted
     and any other slot still holding an expert of layer l is emptied.  What
-    survives seeds decode.  Returns the buffer index b."""
+    survives seeds decode.  With the second buffer disabled (snackonai, "It
+    In Action") every layer uses buffer 0.  Returns the buffer index b."""
+    assert buffers in (1, 2)
     n = st.n_slots
-    if n < 2 * E:
-        raise ValueError("two full-layer buffers do not fit in the slot pool")
+    if n < buffers * E:
+        raise ValueError("the full-layer buffers do not fit in the slot pool")
     st.tick += 1
-    b = layer % 2
+    b = layer % buffers
     for e in range(E):
         s = b * E + e
         old = st.slot2id[s]

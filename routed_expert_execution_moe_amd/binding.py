@@ -105,6 +105,7 @@ def lib():
                                       ctypes.POINTER(i64)], i32),
             "moe_recommend_mode": ([i64, i64, ctypes.c_double, ctypes.POINTER(i32)], i32),
             "moe_set_split": ([vp, i64, i64, i32], i32),
+            "moe_prefill_set_buffers": ([vp, i32], i32),
             "moe_prefill_layer": ([vp, i32, vp, i32, vp, vp, vp, vp], i32),
             "moe_plan_view_get": ([vp, ctypes.POINTER(PlanView)], i32),
             "moe_ctx_stats": ([vp, ctypes.POINTER(Stats)], i32),
@@ -220,6 +221,10 @@ def moe_recommend_mode(bw_pcie_mbps, bw_host_mbps, threshold=2.0):
 
 def moe_set_split(ctx, bw_pcie_mbps, bw_host_mbps, mode):
     _check(lib().moe_set_split(ctx, bw_pcie_mbps, bw_host_mbps, mode), "moe_set_split")
+
+
+def moe_prefill_set_buffers(ctx, n_buffers):
+    _check(lib().moe_prefill_set_buffers(ctx, n_buffers), "moe_prefill_set_buffers")
 
 
 def moe_prefill_layer(ctx, layer, x, T, ids, w, y, stream=None):

@@ -827,12 +827,12 @@ static moe_status prefill_setup(moe_ctx* ctx) {
   return MOE_OK;
 }
 
-// Issue the slab copy of `layer` into buffer layer % 2 on the copy stream.
+// Issue the slab copy of `layer` into its buffer on the copy stream.
 // It waits for everything enqueued on the caller's stream before this call
 // (ev_start): earlier readers of that buffer, decode work on those slots.
 static moe_status prefill_issue(moe_ctx* ctx, int32_t layer) {
   auto& pf = ctx->pf;
-  int b = layer % 2;
+  const int b = prefill_buffer(ctx, layer);
   const int E = ctx->cfg.n_experts;
   MOE_HIP(ctx, hipStreamWaitEvent(ctx->copy, pf.ev_start, 0));
   MOE_HIP(ctx, timing_begin(ctx, MOE_T_PREFILL_COPY, ctx->copy));
@@ -854,10 +854,27 @@ moe_status moert::prefill_settle(moe_ctx* ctx, hipStream_t s) {
   for (int b = 0; b < 2; ++b) {
     if (pf.buf_layer[b] >= 0 && !pf.admitted[b]) {
       MOE_HIP(ctx, hipStreamWaitEvent(s, pf.ev_copied[b], 0));
-      MOE_HIP(ctx, launch_prefill_admit(ctx, pf.buf_layer[b], s));
+      MOE_HIP(ctx, launch_prefill_admit(ctx, pf.buf_layer[b], b, s));
       pf.admitted[b] = true;
     }
     pf.buf_layer[b] = -1;  // decode fills may overwrite the buffer from here on
+  }
+  return MOE_OK;
+}
+
+extern "C" moe_status moe_prefill_set_buffers(moe_ctx* ctx, int32_t n_buffers) {
+  CHECK_CTX(ctx);
+  if (n_buffers != 1 && n_buffers != 2)
+    return fail(ctx, MOE_EINVAL, "moe_prefill_set_buffers: n_buffers must be 1 or 2");
+  if (ctx->state != kIdle) return fail(ctx, MOE_EINVAL, "moe_prefill_set_buffers: a layer call is open");
+  auto& pf = ctx->pf;
+  for (int b = 0; b < 2; ++b)
+    if (pf.buf_layer[b] >= 0 && !pf.admitted[b])
+      return fail(ctx, MOE_EBUSY, "moe_prefill_set_buffers: a prefetched slab is pending");
+  if (pf.buffers != n_buffers) {
+    // a slab issued under the other mapping no longer names its buffer
+    pf.buf_layer[0] = pf.buf_layer[1] = -1;
+    pf.buffers = n_buffers;
   }
   return MOE_OK;
 }
@@ -876,22 +893,23 @@ extern "C" moe_status moe_prefill_layer(moe_ctx* ctx, int32_t layer, const void*
                 "hidden % 256 == 0 and inter % 128 == 0");
   if (((uintptr_t)x & 15) || ((uintptr_t)ids & 3) || ((uintptr_t)w & 3) || ((uintptr_t)y & 3))
     return fail(ctx, MOE_EINVAL, "moe_prefill_layer: x must be 16-byte aligned");
-  if (ctx->n_slots < 2 * c.n_experts)
-    return fail(ctx, MOE_ENOSPC, "moe_prefill_layer: two full-layer buffers do not fit in the slot pool");
+  auto& pf = ctx->pf;
+  if (ctx->n_slots < pf.buffers * c.n_experts)
+    return fail(ctx, MOE_ENOSPC, "moe_prefill_layer: the full-layer buffers do not fit in the slot pool");
   moe_status st = prefill_setup(ctx);
   if (st != MOE_OK) return st;
-  auto& pf = ctx->pf;
   hipStream_t s = (hipStream_t)stream;
-  const int b = layer % 2;
+  const int b = prefill_buffer(ctx, layer);
   MOE_HIP(ctx, hipEventRecord(pf.ev_start, s));
   if (pf.buf_layer[b] != layer && (st = prefill_issue(ctx, layer)) != MOE_OK) return st;
-  // stream the next layer into the other buffer while this one computes
-  if (layer + 1 < c.n_layers && pf.buf_layer[1 - b] != layer + 1 &&
+  // with two buffers, stream the next layer into the other one while this
+  // one computes; with one, the next layer's copy waits for this compute
+  if (pf.buffers == 2 && layer + 1 < c.n_layers && pf.buf_layer[1 - b] != layer + 1 &&
       (st = prefill_issue(ctx, layer + 1)) != MOE_OK)
     return st;
   MOE_HIP(ctx, hipStreamWaitEvent(s, pf.ev_copied[b], 0));
   if (!pf.admitted[b]) {
-    MOE_HIP(ctx, launch_prefill_admit(ctx, layer, s));
+    MOE_HIP(ctx, launch_prefill_admit(ctx, layer, b, s));
     pf.admitted[b] = true;
   }
   MOE_HIP(ctx, launch_prefill_compute(ctx, layer, x, T, ids, w, y, s));

@@ -154,6 +154,7 @@ struct moe_ctx {
   // prefill (allocated lazily on the first prefill call)
   struct Prefill {
     bool ready = false;
+    int32_t buffers = 2;                   // full-layer buffers in use (1: no prefetch)
     int32_t buf_layer[2] = {-1, -1};      // layer whose slab was issued into buffer b
     bool admitted[2] = {false, false};     // tables already describe buffer b
     hipEvent_t ev_copied[2] = {nullptr, nullptr};
@@ -207,7 +208,9 @@ hipError_t launch_ffn_f32(moe_ctx* ctx, const void* x, int T, hipStream_t s);
 hipError_t launch_ffn_bf16(moe_ctx* ctx, const void* x, int T, hipStream_t s);
 hipError_t launch_ffn_mx(moe_ctx* ctx, const void* x, int T, hipStream_t s);
 hipError_t launch_merge(moe_ctx* ctx, const float* w, int T, void* y, hipStream_t s);
-hipError_t launch_prefill_admit(moe_ctx* ctx, int layer, hipStream_t s);
+hipError_t launch_prefill_admit(moe_ctx* ctx, int layer, int b, hipStream_t s);
+// the full-layer buffer of a prefill layer: layer % 2 with two buffers, else 0
+inline int prefill_buffer(const moe_ctx* ctx, int layer);
 hipError_t launch_prefill_compute(moe_ctx* ctx, int layer, const void* x, int T,
                                   const int32_t* ids, const float* w, void* y, hipStream_t s);
 hipError_t launch_table_reset(moe_ctx* ctx, hipStream_t s);
@@ -227,3 +230,7 @@ void host_branch_stop(moe_ctx* ctx);
 bool host_branch_idle(moe_ctx* ctx);
 
 }  // namespace moert
+
+inline int moert::prefill_buffer(const moe_ctx* ctx, int layer) {
+  return ctx->pf.buffers == 2 ? (layer & 1) : 0;
+}

@@ -450,16 +450,16 @@ hipError_t launch_plan(moe_ctx* ctx, int layer, const int32_t* ids, int T, const
 }
 
 // ---------------------------------------------------------------- prefill admission
-// Buffer b = layer % 2 is slots [b*E, (b+1)*E); expert e of the layer sits in
+// Buffer b (layer % 2 with two buffers, 0 with one) is slots [b*E, (b+1)*E);
+// expert e of the layer sits in
 // slot b*E + e with one tick for the layer.  The buffer's previous occupants
 // are evicted and any other slot still holding an expert of this layer is
 // emptied (satyajit, "Prefill: hide the pool behind the wire").
-__global__ __launch_bounds__(kMaxExperts) void prefill_admit_kernel(int layer, int E, int32_t* id2slot,
+__global__ __launch_bounds__(kMaxExperts) void prefill_admit_kernel(int layer, int b, int E, int32_t* id2slot,
                                                                     int32_t* slot2id, int64_t* slot_ts,
                                                                     DevState* st) {
   __shared__ int64_t s_tick;
   const int e = threadIdx.x;
-  const int b = layer & 1;
   if (e == 0) s_tick = st->tick + 1;
   // other slots holding this layer's experts (outside the buffer) are emptied
   if (e < E) {
@@ -490,8 +490,8 @@ __global__ __launch_bounds__(kMaxExperts) void prefill_admit_kernel(int layer, i
   }
 }
 
-hipError_t launch_prefill_admit(moe_ctx* ctx, int layer, hipStream_t s) {
-  hipLaunchKernelGGL(prefill_admit_kernel, dim3(1), dim3(kMaxExperts), 0, s, layer,
+hipError_t launch_prefill_admit(moe_ctx* ctx, int layer, int b, hipStream_t s) {
+  hipLaunchKernelGGL(prefill_admit_kernel, dim3(1), dim3(kMaxExperts), 0, s, layer, b,
                      ctx->cfg.n_experts, ctx->id2slot, ctx->slot2id, ctx->slot_ts, ctx->dstate);
   return hipGetLastError();
 }

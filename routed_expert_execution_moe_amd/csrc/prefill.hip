@@ -1,5 +1,6 @@
 // Prefill compute for one chunk of T tokens of one MoE layer whose E experts
-// sit in the full-layer buffer b = layer % 2, slots [b*E, (b+1)*E)
+// sit in the full-layer buffer b (layer % 2, or 0 when the context runs one
+// buffer), slots [b*E, (b+1)*E)
 // (satyajit, "Prefill: hide the pool behind the wire").
 //
 //   1. group    per-expert counts of the T*k routed pairs, offsets, the list
@@ -415,7 +416,7 @@ hipError_t launch_prefill_compute(moe_ctx* ctx, int layer, const void* x, int T,
   GemmArgs a{};
   a.slot_base = ctx->pool.base;
   a.stride = ctx->stride;
-  a.slot0 = (layer & 1) * E;
+  a.slot0 = prefill_buffer(ctx, layer) * E;
   a.E = E;
   a.k = k;
   a.offsets = pf.offsets;

@@ -22,10 +22,12 @@ pytestmark = pytest.mark.gpu
 TOL = 2e-2
 
 
-def run_prefill(wl, sample_tokens=None, check_bytes=True, decode_after=False):
+def run_prefill(wl, sample_tokens=None, check_bytes=True, decode_after=False, buffers=2):
     import torch
     g = GpuRun(wl, n_slots=wl.n_slots, max_tokens=8, max_prefill_tokens=wl.T)
     try:
+        if buffers != 2:
+            g.B.moe_prefill_set_buffers(g.ctx, buffers)
         o = OracleRun(wl, g.bank, n_slots=wl.n_slots, max_tokens=8)
         dev = g.dev
         ids = torch.empty((wl.T, wl.k), dtype=torch.int32, device=dev)
@@ -42,7 +44,7 @@ def run_prefill(wl, sample_tokens=None, check_bytes=True, decode_after=False):
             torch.cuda.synchronize()
             ids_o, w_o = o.route(lg)
             assert np.array_equal(ids.cpu().numpy(), ids_o), l
-            b = OP.prefill_admit(o.st, l, wl.E)
+            b = OP.prefill_admit(o.st, l, wl.E, buffers)
             i2s, s2i, ts, tick = g.tables()
             assert i2s == o.st.id2slot and s2i == o.st.slot2id and ts == o.st.slot_ts, l
             assert tick == o.st.tick
@@ -89,6 +91,14 @@ def test_prefill_mini_every_token():
     wl = dataclasses.replace(W.DSV4_PREFILL, L=3, E=16, k=4, H=512, I=512, T=333, n_slots=40)
     log("prefill mini: L=3 E=16 k=4 H=512 I=512 T=333 n=40")
     run_prefill(wl, decode_after=True)
+
+
+def test_prefill_mini_single_buffer():
+    """The second buffer disabled: every layer in slots [0, E), n < 2E, and
+    decode continuing from what is left."""
+    wl = dataclasses.replace(W.DSV4_PREFILL, L=3, E=16, k=4, H=512, I=512, T=333, n_slots=24)
+    log("prefill mini, one buffer: L=3 E=16 k=4 H=512 I=512 T=333 n=24")
+    run_prefill(wl, decode_after=True, buffers=1)
 
 
 def test_prefill_mini_large_tiles():

@@ -275,3 +275,31 @@ def test_prefill_admit_buffers():
                 assert st.id2slot[u] == s
     with pytest.raises(ValueError):
         P.prefill_admit(P.Residency(L * E, 2 * E - 1), 0, E)
+
+
+def test_prefill_admit_single_buffer():
+    """With the second buffer disabled every layer lands in slots [0, E): the
+    previous layer's experts there are evicted, a decode-resident expert of
+    the new layer outside the buffer is emptied, slots past the buffer that
+    hold other layers' experts keep them, and n = E suffices."""
+    L, E = 3, 4
+    st = P.Residency(L * E, E + 2)
+    # decode leaves layer 1's expert 2 and layer 2's expert 0 in the extra slots
+    st.tick = 5
+    for s, u in ((E, 1 * E + 2), (E + 1, 2 * E + 0)):
+        st.slot2id[s], st.id2slot[u], st.slot_ts[s] = u, s, 5
+    assert P.prefill_admit(st, 0, E, buffers=1) == 0
+    assert st.slot2id[:E] == [0, 1, 2, 3] and st.tick == 6
+    assert st.slot2id[E:] == [E + 2, 2 * E]          # other layers' experts stay
+    assert P.prefill_admit(st, 1, E, buffers=1) == 0
+    assert st.slot2id[:E] == [E, E + 1, E + 2, E + 3]
+    assert st.slot2id[E] == -1 and st.slot_ts[E] == -1  # its copy outside the buffer is emptied
+    assert st.id2slot[E + 2] == 2
+    assert all(st.id2slot[u] == -1 for u in range(E))    # layer 0 was evicted
+    assert st.slot2id[E + 1] == 2 * E and st.slot_ts[E + 1] == 5
+    for s, u in enumerate(st.slot2id):
+        if u >= 0:
+            assert st.id2slot[u] == s
+    P.prefill_admit(P.Residency(L * E, E), 2, E, buffers=1)  # one buffer fits in n = E
+    with pytest.raises(ValueError):
+        P.prefill_admit(P.Residency(L * E, E - 1), 0, E, buffers=1)
