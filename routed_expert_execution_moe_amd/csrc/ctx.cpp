@@ -430,9 +430,11 @@ static moe_status timing_create(moe_ctx* ctx) {
   T.a.resize(Timing::kRing);
   T.b.resize(Timing::kRing);
   T.phase.resize(Timing::kRing);
+  // timing-only events: no system-scope fence (cache write-back and
+  // invalidate) on record, which would also slow the work that follows
   for (int i = 0; i < Timing::kRing; ++i) {
-    MOE_HIP(ctx, hipEventCreate(&T.a[i]));
-    MOE_HIP(ctx, hipEventCreate(&T.b[i]));
+    MOE_HIP(ctx, hipEventCreateWithFlags(&T.a[i], hipEventDisableSystemFence));
+    MOE_HIP(ctx, hipEventCreateWithFlags(&T.b[i], hipEventDisableSystemFence));
   }
   return MOE_OK;
 }
