@@ -285,6 +285,16 @@ moe_status moe_measure_bandwidth(moe_ctx* ctx, int32_t n_experts, int32_t reps,
 moe_status moe_recommend_mode(int64_t bw_pcie_mbps, int64_t bw_host_mbps, double threshold,
                               moe_mode* out);
 
+/* Per-layer host decode [satyajit, "Four backends, and the one that has to be
+ * measured": a flag names the MoE layers that decode on the CPU]: flags
+ * (host) [n_layers], nonzero = that layer's calls run with mode CPU (q = 0:
+ * no fills and no admissions; experts of the layer still resident from
+ * before stay hits on the GPU until evicted).  NULL clears.  n_layers must
+ * equal cfg.n_layers.  Applies from the next moe_cache_plan; a graph
+ * captured earlier keeps the modes it was captured with.  No layer call may
+ * be open. */
+moe_status moe_set_cpu_layers(moe_ctx* ctx, const uint8_t* flags, int32_t n_layers);
+
 /* Replace the bandwidths the control kernel splits misses with, and the mode
  * (for example with measured values and the recommended backend).  Applies
  * from the next moe_cache_plan; a graph captured earlier keeps the values it

@@ -106,6 +106,7 @@ def lib():
             "moe_recommend_mode": ([i64, i64, ctypes.c_double, ctypes.POINTER(i32)], i32),
             "moe_set_split": ([vp, i64, i64, i32], i32),
             "moe_prefill_set_buffers": ([vp, i32], i32),
+            "moe_set_cpu_layers": ([vp, ctypes.POINTER(ctypes.c_uint8), i32], i32),
             "moe_prefill_layer": ([vp, i32, vp, i32, vp, vp, vp, vp], i32),
             "moe_plan_view_get": ([vp, ctypes.POINTER(PlanView)], i32),
             "moe_ctx_stats": ([vp, ctypes.POINTER(Stats)], i32),
@@ -217,6 +218,15 @@ def moe_recommend_mode(bw_pcie_mbps, bw_host_mbps, threshold=2.0):
     _check(lib().moe_recommend_mode(bw_pcie_mbps, bw_host_mbps, threshold, ctypes.byref(m)),
            "moe_recommend_mode")
     return m.value
+
+
+def moe_set_cpu_layers(ctx, flags):
+    """flags: sequence of L truthy values (layers that decode on the host), or None."""
+    if flags is None:
+        _check(lib().moe_set_cpu_layers(ctx, None, 0), "moe_set_cpu_layers")
+        return
+    arr = (ctypes.c_uint8 * len(flags))(*[1 if f else 0 for f in flags])
+    _check(lib().moe_set_cpu_layers(ctx, arr, len(flags)), "moe_set_cpu_layers")
 
 
 def moe_set_split(ctx, bw_pcie_mbps, bw_host_mbps, mode):

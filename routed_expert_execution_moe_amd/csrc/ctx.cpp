@@ -795,6 +795,16 @@ extern "C" moe_status moe_recommend_mode(int64_t bw_pcie_mbps, int64_t bw_host_m
   return MOE_OK;
 }
 
+extern "C" moe_status moe_set_cpu_layers(moe_ctx* ctx, const uint8_t* flags, int32_t n_layers) {
+  CHECK_CTX(ctx);
+  if (flags && n_layers != ctx->cfg.n_layers)
+    return fail(ctx, MOE_EINVAL, "moe_set_cpu_layers: n_layers must equal the context's layer count");
+  if (ctx->state != kIdle) return fail(ctx, MOE_EINVAL, "moe_set_cpu_layers: a layer call is open");
+  if (!flags) ctx->cpu_layers.clear();
+  else ctx->cpu_layers.assign(flags, flags + n_layers);
+  return MOE_OK;
+}
+
 extern "C" moe_status moe_set_split(moe_ctx* ctx, int64_t bw_pcie_mbps, int64_t bw_host_mbps,
                                     moe_mode mode) {
   CHECK_CTX(ctx);

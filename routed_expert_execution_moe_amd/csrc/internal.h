@@ -143,6 +143,7 @@ struct moe_ctx {
   uint64_t ffn_wait_ticks = 0;            // expert FFN down items' wait limit
 
   hipStream_t copy = nullptr;  // prefill transfers
+  std::vector<uint8_t> cpu_layers;  // [L] nonzero: the layer decodes its misses on the host, never fills
 
   moert::CpuPool* cpu = nullptr;
   moert::HostBranch* hb = nullptr;

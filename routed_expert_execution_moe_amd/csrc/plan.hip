@@ -429,7 +429,7 @@ hipError_t launch_plan(moe_ctx* ctx, int layer, const int32_t* ids, int T, const
   if (ctx->cfg.max_fetch > 0) K = std::min<int64_t>(K, ctx->cfg.max_fetch);
   a.K = (int32_t)K;
   a.umax = ctx->umax;
-  a.mode = ctx->cfg.mode;
+  a.mode = (!ctx->cpu_layers.empty() && ctx->cpu_layers[layer]) ? MOE_CPU : ctx->cfg.mode;
   a.max_fetch = ctx->cfg.max_fetch;
   a.bwp = ctx->cfg.bw_pcie_mbps;
   a.bwh = ctx->cfg.bw_host_mbps;

@@ -134,3 +134,45 @@ def test_qwen_elastic_full():
     worst, n, st = run_decode(
         wl, check_output=lambda s, l: (s % 64 == 0 and l < 2) or s in (127, 128, 255, 256, 383, 384, 511) and l < 2)
     log(f"qwen elastic full: worst {worst:.3e} over {n} outputs {st}")
+
+
+def test_cpu_layers_bf16():
+    """Layers 1 and 3 decode on the host (mode CPU for their calls), the others
+    hybrid: every plan bit-exact against the oracle run with the same
+    per-layer modes, outputs within tolerance, and no expert of a host layer
+    ever admitted.  Switching the flags off mid-run lets those layers fill."""
+    wl = mini(W.QWEN_BF16, L=4, steps=12, n_slots=189)
+    g = GpuRun(wl)
+    try:
+        o = OracleRun(wl, g.bank)
+        logits = W.router_logits(wl)
+        cpu = [False, True, False, True]
+        g.B.moe_set_cpu_layers(g.ctx, cpu)
+        worst = 0.0
+        for s in range(wl.steps):
+            if s == 8:
+                g.B.moe_set_cpu_layers(g.ctx, None)
+                cpu = [False] * wl.L
+            for l in range(wl.L):
+                x = W.hidden(wl, s, l)
+                ids_g, w_g = g.decode_call(l, logits[s, l], x)
+                ids_o, w_o = o.route(logits[s, l])
+                assert np.array_equal(ids_g, ids_o), (s, l)
+                o.mode = 2 if cpu[l] else 0
+                op = o.plan(l, ids_o)
+                compare_plan(g.plan_view(wl.T), op, wl.T)
+                if cpu[l]:
+                    assert op.q == 0 and not op.hits, (s, l)
+                err, _ = rel_err(g.y_f64(), o.output(l, x_f64(wl, x), ids_o, w_o))
+                worst = max(worst, err)
+                assert err <= TOL[wl.w_dtype], (s, l, err)
+            if s == 7:
+                i2s, _, _, _ = g.tables()
+                for l in (1, 3):
+                    assert all(i2s[l * wl.E + e] == -1 for e in range(wl.E)), l
+        i2s, s2i, ts, tick = g.tables()
+        assert i2s == o.st.id2slot and s2i == o.st.slot2id and ts == o.st.slot_ts
+        assert any(i2s[1 * wl.E + e] >= 0 for e in range(wl.E))  # filled once released
+        log(f"  host layers 1, 3 then none: worst rel err {worst:.3e}")
+    finally:
+        g.close()
