@@ -30,7 +30,10 @@
 // the SiLU * up epilogue needs no exchange.  Each XCD takes a contiguous run
 // of M-tiles, N-tile outer over groups of four M-tiles, so the N-tiles of an
 // M-tile share its A rows and the M-tiles of an expert share its B slices in
-// that XCD's L2.
+// that XCD's L2.  The down GEMM's fp32 output rows leave through the stage
+// buffer (written per wave, read back as 16-byte row pieces), so each lane
+// stores 16 bytes at a time; the pair index of each tile row is read once
+// into LDS at the start.
 #include <type_traits>
 
 #include "internal.h"
@@ -175,10 +178,18 @@ __device__ inline uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t
 
 template <bool GLU>
 __global__ __launch_bounds__(kGemmThreads, 2) void grouped_gemm_kernel(GemmArgs a) {
-  __shared__ __attribute__((aligned(1024))) uint8_t s_a0[kStageA], s_a1[kStageA], s_a2[kStageA];
-  __shared__ __attribute__((aligned(1024))) uint8_t s_b0[kStageB], s_b1[kStageB], s_b2[kStageB];
+  // three A and three B stages in one buffer: after the K loop the down
+  // GEMM reuses it to stage its output rows
+  __shared__ __attribute__((aligned(1024))) uint8_t s_stage[3 * kStageA + 3 * kStageB];
+  uint8_t* const s_a0 = s_stage;
+  uint8_t* const s_a1 = s_stage + kStageA;
+  uint8_t* const s_a2 = s_stage + 2 * kStageA;
+  uint8_t* const s_b0 = s_stage + 3 * kStageA;
+  uint8_t* const s_b1 = s_stage + 3 * kStageA + kStageB;
+  uint8_t* const s_b2 = s_stage + 3 * kStageA + 2 * kStageB;
   __shared__ __attribute__((aligned(1024))) uint8_t s_sc[2][kStageS];
   __shared__ int32_t s_rowsrc[kBM];  // A source row per tile row
+  __shared__ int32_t s_pair[kBM];    // down: the pair (output row) of each tile row
 
   // XCD-aware mapping: consecutive workgroups go round-robin over the 8 XCDs.
   // XCD x takes the x-th contiguous eighth of the M-tile list: the N-tiles of
@@ -208,7 +219,9 @@ __global__ __launch_bounds__(kGemmThreads, 2) void grouped_gemm_kernel(GemmArgs 
   // first row: no masked loads, and their results are never written
   if (tid < kBM) {
     const int r = tid < rows ? tid : 0;
-    s_rowsrc[tid] = GLU ? a.perm[pos0 + r] / a.k : pos0 + r;
+    const int p = a.perm[pos0 + r];
+    s_rowsrc[tid] = GLU ? p / a.k : pos0 + r;
+    s_pair[tid] = p;
   }
   __syncthreads();
 
@@ -340,14 +353,44 @@ __global__ __launch_bounds__(kGemmThreads, 2) void grouped_gemm_kernel(GemmArgs 
     if (kt < nk) step(kt, s_a0, s_b0, s_a2, s_b2);
     if (kt + 1 < nk) step(kt + 1, s_a1, s_b1, s_a0, s_b0);
 
-    // epilogue: C element r of lane: row 8*(r/4) + 4*kg + r%4, column lr
+    // C element r of lane: row 8*(r/4) + 4*kg + r%4, column lr.
+    // Down epilogue: each wave writes 32 of its rows (its NJ*32 columns) to
+    // the stage buffer, reads them back as 16-byte row pieces and stores
+    // those to the pair's fp32 row, twice (row blocks i = 0, 1).
+    if constexpr (!GLU) {
+      constexpr int CW = NJ * 32, CS = CW + 4;  // row stride padded by 4 floats
+      constexpr int LPR = CW / 4;               // lanes per row
+      constexpr int RPI = 64 / LPR;             // rows per read
+      static_assert(4 * 32 * CS * 4 <= 3 * kStageA + 3 * kStageB, "staging fits the stage buffer");
+      __syncthreads();  // every wave is done reading the stages
+      float* cbuf = (float*)s_stage + wave * (32 * CS);
+      const int c4 = lane % LPR, rsub = lane / LPR;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) cbuf[(8 * (r >> 2) + 4 * kg + (r & 3)) * CS + j * 32 + lr] = acc[i][j][r];
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's rows are in LDS
+#pragma unroll
+        for (int q = 0; q < 32 / RPI; ++q) {
+          const int rl = q * RPI + rsub;
+          const float4 v = *(const float4*)&cbuf[rl * CS + c4 * 4];
+          const int row = arow0 + i * 32 + rl;
+          if (row < rows) *(float4*)&a.p_out[(size_t)s_pair[row] * a.N + n0 + brow[0] + c4 * 4] = v;
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads done before the next block's writes
+      }
+      return;
+    }
+    // gate/up epilogue: h = silu(g) * u rounded to bf16, rows in pos order
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int row = arow0 + i * 32 + 8 * (r >> 2) + 4 * kg + (r & 3);
         if (row >= rows) continue;
-        if (GLU) {
+        if constexpr (GLU) {
 #pragma unroll
           for (int j = 0; j < NJ / 2; ++j) {
             const float g = acc[i][j][r], u = acc[i][j + NJ / 2][r];
@@ -356,13 +399,6 @@ __global__ __launch_bounds__(kGemmThreads, 2) void grouped_gemm_kernel(GemmArgs 
             bits += 0x7FFFu + ((bits >> 16) & 1u);
             const int col = n0 + (HALF ? wave * 32 : wn * 64 + j * 32) + lr;
             a.h_out[(size_t)(pos0 + row) * a.N + col] = (uint16_t)(bits >> 16);
-          }
-        } else {
-          const int pair = a.perm[pos0 + row];
-#pragma unroll
-          for (int j = 0; j < NJ; ++j) {
-            const int col = n0 + brow[j] + lr;
-            a.p_out[(size_t)pair * a.N + col] = acc[i][j][r];
           }
         }
       }
