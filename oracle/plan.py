@@ -231,3 +231,44 @@ def prefill_admit(st: Residency, layer: int, E: int, buffers: int = 2):
         st.id2slot[u] = s
         st.slot_ts[s] = st.tick
     return b
+
+
+def prefill_on_demand(st: Residency, layer: int, routed, E: int):
+    """On-demand prefill when the pool cannot hold the full-layer buffers
+    (signalovernoise essay: it falls back to on-demand rather than
+    oversubscribe; snackonai, "The Architecture, Unpacked", second decision:
+    it degrades to on-demand loading instead of oversubscribing VRAM).
+
+    Reading: only the experts of `layer` that the chunk routes to are loaded,
+    after routing is known, in ascending expert order and in passes of at
+    most n (the slot count) experts.  A pass behaves like a small full-layer
+    buffer: one tick; slots [0, P) evict their occupants; any other slot
+    holding one of the pass's IDs is emptied; expert i of the pass goes to
+    slot i with the pass's tick.  Every routed expert of a pass is loaded
+    from its host bank even if it was resident elsewhere.  Returns the passes
+    (lists of expert indices)."""
+    n = st.n_slots
+    if n < 1:
+        raise ValueError("on-demand prefill needs at least one slot")
+    experts = sorted({int(e) for e in routed if 0 <= int(e) < E})
+    passes = [experts[i:i + n] for i in range(0, len(experts), n)]
+    for part in passes:
+        st.tick += 1
+        ids = [layer * E + e for e in part]
+        for i in range(len(part)):
+            old = st.slot2id[i]
+            if old >= 0:
+                st.id2slot[old] = -1
+            st.slot2id[i] = -1
+            st.slot_ts[i] = -1
+        for u in ids:
+            s = st.id2slot[u]
+            if s >= 0:
+                st.slot2id[s] = -1
+                st.slot_ts[s] = -1
+                st.id2slot[u] = -1
+        for i, u in enumerate(ids):
+            st.slot2id[i] = u
+            st.id2slot[u] = i
+            st.slot_ts[i] = st.tick
+    return passes

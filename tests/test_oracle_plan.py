@@ -303,3 +303,86 @@ def test_prefill_admit_single_buffer():
     P.prefill_admit(P.Residency(L * E, E), 2, E, buffers=1)  # one buffer fits in n = E
     with pytest.raises(ValueError):
         P.prefill_admit(P.Residency(L * E, E - 1), 0, E, buffers=1)
+
+
+def _warm(L, E, n, steps, seed):
+    """A residency state left by offload decode over random routing."""
+    rng = random.Random(seed)
+    st = P.Residency(L * E, n)
+    K = P.victim_bound(1, 2, E, n)
+    for _ in range(steps):
+        P.plan(st, rng.randrange(L), [rng.sample(range(E), 2)], E, K, 1, 1, P.OFFLOAD)
+    return st
+
+
+def test_prefill_on_demand_one_pass_is_single_buffer():
+    """With every expert routed and n >= E, on-demand is one pass over all E
+    experts into slots [0, E): the same tables as the one-buffer admission,
+    pinned above, from the same decode-warmed state."""
+    L, E = 3, 6
+    for n in (E, E + 1, 2 * E - 1):
+        for layer in range(L):
+            a = _warm(L, E, n, 30, 100 * n + layer)
+            b = a.copy()
+            passes = P.prefill_on_demand(a, layer, list(range(E)) * 2, E)
+            P.prefill_admit(b, layer, E, buffers=1)
+            assert passes == [list(range(E))]
+            assert (a.id2slot, a.slot2id, a.slot_ts, a.tick) == (b.id2slot, b.slot2id, b.slot_ts, b.tick)
+
+
+def test_prefill_on_demand_passes_worked_example():
+    """L = 2, E = 6, n = 2; decode left layer 1 expert 3 in slot 1 (tick 4)
+    and layer 0 expert 5 in slot 0 (tick 3).  A layer-1 chunk that routes to
+    experts {4, 1, 3, 1} runs passes [1, 3] and [4]: pass one (tick 5) puts
+    u = 7 in slot 0 (evicting u = 5) and u = 9 in slot 1 (its own old slot,
+    refreshed); pass two (tick 6) puts u = 10 in slot 0 (evicting u = 7);
+    slot 1 keeps u = 9 with tick 5."""
+    E = 6
+    st = P.Residency(2 * E, 2)
+    st.slot2id, st.slot_ts, st.tick = [5, 9], [3, 4], 4
+    st.id2slot[5], st.id2slot[9] = 0, 1
+    passes = P.prefill_on_demand(st, 1, [4, 1, 3, 1, -1, 6], E)
+    assert passes == [[1, 3], [4]]
+    assert st.tick == 6
+    assert st.slot2id == [10, 9] and st.slot_ts == [6, 5]
+    assert [u for u in range(2 * E) if st.id2slot[u] >= 0] == [9, 10]
+    with pytest.raises(ValueError):
+        P.prefill_on_demand(P.Residency(2 * E, 0), 0, [0], E)
+
+
+def test_prefill_on_demand_invariants():
+    """Random decode-warmed states and routed sets: the passes cover the
+    routed experts in ascending order with at most n each, one tick per pass;
+    the last pass's experts sit in slots [0, P) with the final tick; the
+    other experts of the chunk are resident at most once, each with its pass's
+    tick; slots past the first (largest) pass that held IDs outside the chunk
+    keep them, and slots below it hold only the chunk's experts."""
+    rng = random.Random(5)
+    L, E = 3, 10
+    for trial in range(200):
+        n = rng.randrange(1, 2 * E)
+        st = _warm(L, E, n, rng.randrange(0, 40), trial)
+        before = st.copy()
+        layer = rng.randrange(L)
+        routed = [rng.randrange(E) for _ in range(rng.randrange(1, 3 * E))]
+        passes = P.prefill_on_demand(st, layer, routed, E)
+        flat = [e for p in passes for e in p]
+        assert flat == sorted(set(routed))
+        assert all(1 <= len(p) <= n for p in passes) and all(len(p) == n for p in passes[:-1])
+        assert st.tick == before.tick + len(passes)
+        last = passes[-1]
+        assert st.slot2id[:len(last)] == [layer * E + e for e in last]
+        assert st.slot_ts[:len(last)] == [st.tick] * len(last)
+        chunk = {layer * E + e for e in flat}
+        for s, u in enumerate(st.slot2id):
+            if u >= 0:
+                assert st.id2slot[u] == s
+            if s >= len(passes[0]) and before.slot2id[s] not in chunk:
+                assert (u, st.slot_ts[s]) == (before.slot2id[s], before.slot_ts[s])
+            if s < len(passes[0]):
+                assert u in chunk
+        for u in chunk:
+            s = st.id2slot[u]
+            if s >= 0:
+                pi = next(i for i, p in enumerate(passes) if u - layer * E in p)
+                assert st.slot_ts[s] == before.tick + pi + 1
