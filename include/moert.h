@@ -32,7 +32,9 @@
  *     that context returns MOE_EHIP (moe_last_error() has the text).
  *   - route / plan / ffn / merge / prefill enqueue work on `stream` and never
  *     synchronise the host; plans stay on the device (the host never reads
- *     them on this path) [snackonai, "The Architecture, Unpacked"].
+ *     them on this path) [snackonai, "The Architecture, Unpacked"].  The one
+ *     exception is on-demand prefill (see moe_prefill_layer), which must read
+ *     a layer's routed experts before it can fetch them.
  *   - One context is driven by one host thread, and its decode calls for a
  *     layer are issued in the order plan → ffn → merge on one stream; a call
  *     out of that order returns MOE_EINVAL.
@@ -56,7 +58,7 @@ typedef enum {
   MOE_OK = 0,
   MOE_EINVAL = -1,       /* bad argument or call order; nothing enqueued      */
   MOE_ENOMEM = -2,       /* device or pinned host allocation failed           */
-  MOE_ENOSPC = -3,       /* two full-layer buffers do not fit (prefill)       */
+  MOE_ENOSPC = -3,       /* prefill with an empty slot pool                   */
   MOE_EHIP = -4,         /* HIP runtime error (latched)                       */
   MOE_EBUSY = -5,        /* work still in flight where a safe point is needed */
   MOE_ETIMEDOUT = -6,    /* resize could not drain within timeout_ms          */
@@ -202,8 +204,14 @@ moe_status moe_cache_resize(moe_ctx* ctx, int32_t new_n_slots, int32_t timeout_m
  * [T][k]; y (device) [T][H].  1 <= T <= max_prefill_tokens.
  * Supported for MXFP4 experts with bf16 activations, H % 256 == 0 and
  * I % 128 == 0 (MOE_EUNSUPPORTED otherwise).
- * MOE_ENOSPC if n_slots < buffers x E (the pages fall back to on-demand
- * loading instead of oversubscribing; that fallback is not provided). */
+ * When n_slots < buffers x E the buffers do not fit, and the call falls back
+ * to on-demand loading instead of oversubscribing [signalovernoise essay;
+ * snackonai, "The Architecture, Unpacked"]: it synchronises `stream` once to
+ * read which experts the chunk routes to, then loads them in ascending order,
+ * at most n_slots per pass, into slots [0, P) (one tick per pass; occupants
+ * evicted, a pass expert resident elsewhere emptied there), and runs the
+ * grouped GEMM over each pass's experts on `stream`; nothing is prefetched.
+ * MOE_ENOSPC if n_slots == 0. */
 moe_status moe_prefill_layer(moe_ctx* ctx, int32_t layer, const void* x, int32_t T,
                              const int32_t* ids, const float* w, void* y, moe_stream stream);
 

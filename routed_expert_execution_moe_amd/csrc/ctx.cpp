@@ -96,7 +96,7 @@ extern "C" const char* moe_strerror(moe_status s) {
     case MOE_OK: return "ok";
     case MOE_EINVAL: return "invalid argument or call order";
     case MOE_ENOMEM: return "out of memory";
-    case MOE_ENOSPC: return "two full-layer buffers do not fit in the slot pool";
+    case MOE_ENOSPC: return "prefill needs at least one slot";
     case MOE_EHIP: return "HIP runtime error";
     case MOE_EBUSY: return "busy";
     case MOE_ETIMEDOUT: return "timed out";
@@ -404,6 +404,8 @@ static void free_all(moe_ctx* ctx) {
   F(ctx->p_gpu); F(ctx->h_mid); F(ctx->plan_alloc);
   auto& pf = ctx->pf;
   F(pf.counts); F(pf.offsets); F(pf.cursor); F(pf.perm); F(pf.hmid); F(pf.prow); F(pf.tiles);
+  F(pf.slot_of);
+  if (pf.counts_host) (void)hipHostFree(pf.counts_host);
   for (int b = 0; b < 2; ++b)
     if (pf.ev_copied[b]) (void)hipEventDestroy(pf.ev_copied[b]);
   if (pf.ev_start) (void)hipEventDestroy(pf.ev_start);
@@ -832,6 +834,8 @@ static moe_status prefill_setup(moe_ctx* ctx) {
   MOE_HIP(ctx, hipMalloc((void**)&pf.perm, 4 * Tk));
   MOE_HIP(ctx, hipMalloc((void**)&pf.hmid, 2 * Tk * c.inter));
   MOE_HIP(ctx, hipMalloc((void**)&pf.prow, 4 * Tk * c.hidden));
+  MOE_HIP(ctx, hipMalloc((void**)&pf.slot_of, 4 * (size_t)c.n_experts));
+  MOE_HIP(ctx, hipHostMalloc((void**)&pf.counts_host, 4 * (size_t)c.n_experts, hipHostMallocDefault));
   for (int b = 0; b < 2; ++b)
     MOE_HIP(ctx, hipEventCreateWithFlags(&pf.ev_copied[b], hipEventDisableTiming));
   MOE_HIP(ctx, hipEventCreateWithFlags(&pf.ev_start, hipEventDisableTiming));
@@ -874,6 +878,46 @@ moe_status moert::prefill_settle(moe_ctx* ctx, hipStream_t s) {
   return MOE_OK;
 }
 
+// On-demand prefill, used when the pool cannot hold the full-layer buffers
+// (signalovernoise essay; snackonai, "The Architecture, Unpacked"): the
+// layer's routed experts are known only after routing, so the host reads the
+// per-expert counts (one stream synchronisation per layer), then loads the
+// routed experts in ascending order, at most n_slots per pass, into slots
+// [0, P) with one copy per run of consecutive experts, and runs the grouped
+// GEMM over that pass's experts only.  Each pass writes the partial rows of
+// its own pairs, so one merge after the last pass sees every pair once.
+static moe_status prefill_on_demand(moe_ctx* ctx, int32_t layer, const void* x, int32_t T,
+                                    const int32_t* ids, const float* w, void* y, hipStream_t s) {
+  auto& pf = ctx->pf;
+  const int E = ctx->cfg.n_experts;
+  moe_status st = prefill_settle(ctx, s);
+  if (st != MOE_OK) return st;
+  MOE_HIP(ctx, launch_prefill_group(ctx, ids, T, s));
+  MOE_HIP(ctx, hipMemcpyAsync(pf.counts_host, pf.counts, 4 * (size_t)E, hipMemcpyDeviceToHost, s));
+  MOE_HIP(ctx, hipStreamSynchronize(s));
+  std::vector<int32_t> routed;
+  for (int e = 0; e < E; ++e)
+    if (pf.counts_host[e] > 0) routed.push_back(e);
+  const int n = ctx->n_slots, nu = (int)routed.size();
+  for (int p0 = 0; p0 < nu; p0 += n) {
+    const int P = std::min(n, nu - p0);
+    MOE_HIP(ctx, launch_prefill_pass_admit(ctx, layer, p0, P, s));
+    MOE_HIP(ctx, timing_begin(ctx, MOE_T_PREFILL_COPY, s));
+    for (int i = 0; i < P;) {
+      int j = i + 1;
+      while (j < P && routed[p0 + j] == routed[p0 + j - 1] + 1) ++j;
+      MOE_HIP(ctx, hipMemcpyAsync(ctx->pool.base + (size_t)i * ctx->stride,
+                                  ctx->host_pool + ((size_t)layer * E + routed[p0 + i]) * ctx->stride,
+                                  (size_t)(j - i) * ctx->stride, hipMemcpyHostToDevice, s));
+      i = j;
+    }
+    MOE_HIP(ctx, timing_end(ctx, s));
+    MOE_HIP(ctx, launch_prefill_gemm(ctx, layer, x, T, pf.slot_of, s));
+  }
+  MOE_HIP(ctx, launch_prefill_merge(ctx, ids, w, T, y, s));
+  return MOE_OK;
+}
+
 extern "C" moe_status moe_prefill_set_buffers(moe_ctx* ctx, int32_t n_buffers) {
   CHECK_CTX(ctx);
   if (n_buffers != 1 && n_buffers != 2)
@@ -906,11 +950,11 @@ extern "C" moe_status moe_prefill_layer(moe_ctx* ctx, int32_t layer, const void*
   if (((uintptr_t)x & 15) || ((uintptr_t)ids & 3) || ((uintptr_t)w & 3) || ((uintptr_t)y & 3))
     return fail(ctx, MOE_EINVAL, "moe_prefill_layer: x must be 16-byte aligned");
   auto& pf = ctx->pf;
-  if (ctx->n_slots < pf.buffers * c.n_experts)
-    return fail(ctx, MOE_ENOSPC, "moe_prefill_layer: the full-layer buffers do not fit in the slot pool");
+  if (ctx->n_slots < 1) return fail(ctx, MOE_ENOSPC, "moe_prefill_layer: the slot pool is empty");
   moe_status st = prefill_setup(ctx);
   if (st != MOE_OK) return st;
   hipStream_t s = (hipStream_t)stream;
+  if (ctx->n_slots < pf.buffers * c.n_experts) return prefill_on_demand(ctx, layer, x, T, ids, w, y, s);
   const int b = prefill_buffer(ctx, layer);
   MOE_HIP(ctx, hipEventRecord(pf.ev_start, s));
   if (pf.buf_layer[b] != layer && (st = prefill_issue(ctx, layer)) != MOE_OK) return st;

@@ -169,6 +169,8 @@ struct moe_ctx {
     float* prow = nullptr;                 // [Tmax*k][H] fp32 partial rows
     int32_t* tiles = nullptr;              // GEMM tile schedule
     int32_t max_tiles = 0;
+    int32_t* slot_of = nullptr;            // [E] on-demand pass: slot of each expert, -1 outside
+    int32_t* counts_host = nullptr;        // [E] pinned copy of counts (on-demand)
   } pf;
 
   moert::Timing* timing = nullptr;
@@ -214,6 +216,15 @@ hipError_t launch_prefill_admit(moe_ctx* ctx, int layer, int b, hipStream_t s);
 inline int prefill_buffer(const moe_ctx* ctx, int layer);
 hipError_t launch_prefill_compute(moe_ctx* ctx, int layer, const void* x, int T,
                                   const int32_t* ids, const float* w, void* y, hipStream_t s);
+// the three phases of launch_prefill_compute: grouping of the routed pairs;
+// GEMM1 + GEMM2 over the experts of the layer's buffer (slot_of == nullptr)
+// or over the experts slot_of maps (others skipped); the merge
+hipError_t launch_prefill_group(moe_ctx* ctx, const int32_t* ids, int T, hipStream_t s);
+hipError_t launch_prefill_gemm(moe_ctx* ctx, int layer, const void* x, int T, const int32_t* slot_of,
+                               hipStream_t s);
+hipError_t launch_prefill_merge(moe_ctx* ctx, const int32_t* ids, const float* w, int T, void* y,
+                                hipStream_t s);
+hipError_t launch_prefill_pass_admit(moe_ctx* ctx, int layer, int p0, int P, hipStream_t s);
 hipError_t launch_table_reset(moe_ctx* ctx, hipStream_t s);
 moe_status prefill_settle(moe_ctx* ctx, hipStream_t s);
 

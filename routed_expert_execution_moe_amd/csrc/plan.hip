@@ -490,6 +490,67 @@ __global__ __launch_bounds__(kMaxExperts) void prefill_admit_kernel(int layer, i
   }
 }
 
+// One pass of on-demand prefill (the pool cannot hold the full-layer
+// buffers): the experts of `layer` with routed pairs (counts > 0), ranked in
+// ascending expert order; ranks [p0, p0 + P) form this pass and go to slots
+// [0, P) in rank order, with one tick.  The slots' occupants are evicted and
+// a pass expert resident elsewhere is emptied there.  slot_of[e] receives the
+// slot of each expert in the pass and -1 for every other expert.
+__global__ __launch_bounds__(kMaxExperts) void prefill_pass_admit_kernel(int layer, int E, int p0, int P,
+                                                                         const int32_t* counts,
+                                                                         int32_t* slot_of, int32_t* id2slot,
+                                                                         int32_t* slot2id, int64_t* slot_ts,
+                                                                         DevState* st) {
+  __shared__ int32_t s_scan[kMaxExperts];
+  __shared__ int64_t s_tick;
+  const int e = threadIdx.x;
+  const int f = (e < E && counts[e] > 0) ? 1 : 0;
+  s_scan[e] = f;
+  __syncthreads();
+  for (int off = 1; off < kMaxExperts; off <<= 1) {  // inclusive scan of the flags
+    const int v = e >= off ? s_scan[e - off] : 0;
+    __syncthreads();
+    s_scan[e] += v;
+    __syncthreads();
+  }
+  const int rank = s_scan[e] - f;
+  const int slot = (f && rank >= p0 && rank < p0 + P) ? rank - p0 : -1;
+  if (e < E) slot_of[e] = slot;
+  if (e == 0) s_tick = st->tick + 1;
+  if (e < P) {  // evict the occupants of slots [0, P)
+    const int old = slot2id[e];
+    if (old >= 0) id2slot[old] = -1;
+  }
+  __syncthreads();
+  if (slot >= 0) {  // a pass expert still resident elsewhere is emptied there
+    const int u = layer * E + e;
+    const int s = id2slot[u];
+    if (s >= 0) {
+      slot2id[s] = -1;
+      slot_ts[s] = -1;
+      id2slot[u] = -1;
+    }
+  }
+  __syncthreads();
+  if (slot >= 0) {
+    const int u = layer * E + e;
+    slot2id[slot] = u;
+    id2slot[u] = slot;
+    slot_ts[slot] = s_tick;
+  }
+  if (e == 0) {
+    st->tick = s_tick;
+    st->prefill_layers += 1;
+  }
+}
+
+hipError_t launch_prefill_pass_admit(moe_ctx* ctx, int layer, int p0, int P, hipStream_t s) {
+  hipLaunchKernelGGL(prefill_pass_admit_kernel, dim3(1), dim3(kMaxExperts), 0, s, layer,
+                     ctx->cfg.n_experts, p0, P, ctx->pf.counts, ctx->pf.slot_of, ctx->id2slot,
+                     ctx->slot2id, ctx->slot_ts, ctx->dstate);
+  return hipGetLastError();
+}
+
 hipError_t launch_prefill_admit(moe_ctx* ctx, int layer, int b, hipStream_t s) {
   hipLaunchKernelGGL(prefill_admit_kernel, dim3(1), dim3(kMaxExperts), 0, s, layer, b,
                      ctx->cfg.n_experts, ctx->id2slot, ctx->slot2id, ctx->slot_ts, ctx->dstate);

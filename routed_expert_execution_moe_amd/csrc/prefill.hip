@@ -139,6 +139,7 @@ struct GemmArgs {
   const uint8_t* slot_base;   // slot s at slot_base + s * stride
   size_t stride;
   int slot0;                  // b * E
+  const int32_t* slot_of;     // [E] slot of each expert, -1 = skip; nullptr: slot0 + e
   int E, k;
   int K;                      // contraction: H (GEMM1) or I (GEMM2)
   int N;                      // output columns per matrix: I (GEMM1) or H (GEMM2)
@@ -209,6 +210,8 @@ __global__ __launch_bounds__(kGemmThreads, 2) void grouped_gemm_kernel(GemmArgs 
   const int tile = a.tiles[mt];
   const int e = tile >> 20, m0 = ((tile >> 1) & 0x7FFFF) * 64;
   const bool half = tile & 1;  // at most 64 rows: computed as 64 x 256
+  const int eslot = a.slot_of ? a.slot_of[e] : a.slot0 + e;
+  if (eslot < 0) return;  // not in this on-demand pass
   const int pos0 = a.offsets[e] + m0;
   const int rows = min(half ? kBM / 2 : kBM, a.offsets[e + 1] - pos0);
   const int tid = threadIdx.x, lane = tid & 63;
@@ -225,7 +228,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void grouped_gemm_kernel(GemmArgs 
   }
   __syncthreads();
 
-  const uint8_t* slot = a.slot_base + (size_t)(a.slot0 + e) * a.stride;
+  const uint8_t* slot = a.slot_base + (size_t)eslot * a.stride;
   // B tile rows: GLU -> gate rows n0..n0+127 then up rows n0..n0+127 (n0 = nt*128);
   // down -> rows n0..n0+255 (n0 = nt*256)
   const int n0 = GLU ? nt * (kBN / 2) : nt * kBN;
@@ -432,12 +435,9 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(const float* __restr
   }
 }
 
-hipError_t launch_prefill_compute(moe_ctx* ctx, int layer, const void* x, int T, const int32_t* ids,
-                                  const float* w, void* y, hipStream_t s) {
+hipError_t launch_prefill_group(moe_ctx* ctx, const int32_t* ids, int T, hipStream_t s) {
   const moe_config& c = ctx->cfg;
-  if (c.w_dtype != MOE_MXFP4 || c.act_dtype != MOE_BF16) return hipErrorNotSupported;
-  const int E = c.n_experts, k = c.top_k, H = c.hidden, I = c.inter;
-  const int Tk = T * k;
+  const int E = c.n_experts, Tk = T * c.top_k;
   auto& pf = ctx->pf;
   hipError_t e = timing_begin(ctx, MOE_T_PREFILL_GROUP, s);
   if (e != hipSuccess) return e;
@@ -447,12 +447,24 @@ hipError_t launch_prefill_compute(moe_ctx* ctx, int layer, const void* x, int T,
   hipLaunchKernelGGL(group_scan_kernel, dim3(1), dim3(1024), 0, s, pf.counts, E, pf.offsets, pf.tiles);
   hipLaunchKernelGGL(group_scatter_kernel, dim3(gb), dim3(256), 0, s, ids, Tk, E, pf.offsets,
                      pf.cursor, pf.perm);
-  if ((e = timing_end(ctx, s)) != hipSuccess) return e;
-  if ((e = timing_begin(ctx, MOE_T_PREFILL_GEMM, s)) != hipSuccess) return e;
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  return timing_end(ctx, s);
+}
+
+hipError_t launch_prefill_gemm(moe_ctx* ctx, int layer, const void* x, int T, const int32_t* slot_of,
+                               hipStream_t s) {
+  const moe_config& c = ctx->cfg;
+  if (c.w_dtype != MOE_MXFP4 || c.act_dtype != MOE_BF16) return hipErrorNotSupported;
+  const int E = c.n_experts, k = c.top_k, H = c.hidden, I = c.inter;
+  const int Tk = T * k;
+  auto& pf = ctx->pf;
+  hipError_t e = timing_begin(ctx, MOE_T_PREFILL_GEMM, s);
+  if (e != hipSuccess) return e;
   GemmArgs a{};
   a.slot_base = ctx->pool.base;
   a.stride = ctx->stride;
   a.slot0 = prefill_buffer(ctx, layer) * E;
+  a.slot_of = slot_of;
   a.E = E;
   a.k = k;
   a.offsets = pf.offsets;
@@ -481,12 +493,30 @@ hipError_t launch_prefill_compute(moe_ctx* ctx, int layer, const void* x, int T,
   a.p_out = pf.prow;
   a.n_ntiles = H / kBN;
   hipLaunchKernelGGL(grouped_gemm_kernel<false>, dim3(grid_m * a.n_ntiles), dim3(kGemmThreads), 0, s, a);
-  if ((e = timing_end(ctx, s)) != hipSuccess) return e;
-  if ((e = timing_begin(ctx, MOE_T_PREFILL_MERGE, s)) != hipSuccess) return e;
-  dim3 mg((H + 255) / 256, T);
-  hipLaunchKernelGGL(prefill_merge_kernel<MOE_BF16>, mg, dim3(256), 0, s, w, ids, pf.prow, k, H, E, y);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   return timing_end(ctx, s);
+}
+
+hipError_t launch_prefill_merge(moe_ctx* ctx, const int32_t* ids, const float* w, int T, void* y,
+                                hipStream_t s) {
+  const moe_config& c = ctx->cfg;
+  const int E = c.n_experts, k = c.top_k, H = c.hidden;
+  hipError_t e = timing_begin(ctx, MOE_T_PREFILL_MERGE, s);
+  if (e != hipSuccess) return e;
+  dim3 mg((H + 255) / 256, T);
+  hipLaunchKernelGGL(prefill_merge_kernel<MOE_BF16>, mg, dim3(256), 0, s, w, ids, ctx->pf.prow, k, H, E, y);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  return timing_end(ctx, s);
+}
+
+hipError_t launch_prefill_compute(moe_ctx* ctx, int layer, const void* x, int T, const int32_t* ids,
+                                  const float* w, void* y, hipStream_t s) {
+  const moe_config& c = ctx->cfg;
+  if (c.w_dtype != MOE_MXFP4 || c.act_dtype != MOE_BF16) return hipErrorNotSupported;
+  hipError_t e = launch_prefill_group(ctx, ids, T, s);
+  if (e == hipSuccess) e = launch_prefill_gemm(ctx, layer, x, T, nullptr, s);
+  if (e == hipSuccess) e = launch_prefill_merge(ctx, ids, w, T, y, s);
+  return e;
 }
 
 }  // namespace moert

@@ -23,6 +23,8 @@ TOL = 2e-2
 
 
 def run_prefill(wl, sample_tokens=None, check_bytes=True, decode_after=False, buffers=2):
+    """buffers x E > n_slots runs the on-demand fallback (checked against the
+    oracle's on-demand admission, pass by pass through the final tables)."""
     import torch
     g = GpuRun(wl, n_slots=wl.n_slots, max_tokens=8, max_prefill_tokens=wl.T)
     try:
@@ -44,13 +46,20 @@ def run_prefill(wl, sample_tokens=None, check_bytes=True, decode_after=False, bu
             torch.cuda.synchronize()
             ids_o, w_o = o.route(lg)
             assert np.array_equal(ids.cpu().numpy(), ids_o), l
-            b = OP.prefill_admit(o.st, l, wl.E, buffers)
+            on_demand = wl.n_slots < buffers * wl.E
+            if on_demand:
+                passes = OP.prefill_on_demand(o.st, l, ids_o.ravel(), wl.E)
+            else:
+                b = OP.prefill_admit(o.st, l, wl.E, buffers)
             i2s, s2i, ts, tick = g.tables()
             assert i2s == o.st.id2slot and s2i == o.st.slot2id and ts == o.st.slot_ts, l
             assert tick == o.st.tick
             counts = np.bincount(ids_o.ravel(), minlength=wl.E)
             assert counts.sum() == wl.T * wl.k
-            if check_bytes:
+            if check_bytes and on_demand:
+                for i, e in enumerate(passes[-1]):
+                    assert np.array_equal(g.slot_bytes(i), g.bank(l * wl.E + e)), (l, e)
+            elif check_bytes:
                 for e in (0, wl.E // 2, wl.E - 1):
                     assert np.array_equal(g.slot_bytes(b * wl.E + e), g.bank(l * wl.E + e)), (l, e)
             yg = y.float().cpu().numpy().astype(np.float64)
@@ -64,7 +73,8 @@ def run_prefill(wl, sample_tokens=None, check_bytes=True, decode_after=False, bu
             worst = max(worst, err)
             log(f"  layer {l}: tokens checked {len(rows)}, max rel err {err:.3e} "
                 f"(bf16 rounding alone {bf16_round_err(ref):.3e}); experts used "
-                f"{int((counts > 0).sum())}, max n_e {int(counts.max())}, min n_e {int(counts.min())}")
+                f"{int((counts > 0).sum())}, max n_e {int(counts.max())}, min n_e {int(counts.min())}"
+                + (f"; on-demand passes {len(passes)}" if on_demand else ""))
             assert err <= TOL, (l, err)
         if decode_after:
             # decode continues from what prefill left resident
@@ -99,6 +109,23 @@ def test_prefill_mini_single_buffer():
     wl = dataclasses.replace(W.DSV4_PREFILL, L=3, E=16, k=4, H=512, I=512, T=333, n_slots=24)
     log("prefill mini, one buffer: L=3 E=16 k=4 H=512 I=512 T=333 n=24")
     run_prefill(wl, decode_after=True, buffers=1)
+
+
+def test_prefill_mini_on_demand_passes():
+    """n < E: the on-demand fallback loads the routed experts in passes of at
+    most n (4 passes of 5, 5, 5, 1 when all 16 are routed); every token, the
+    tables after each layer, the last pass's slot bytes, decode after."""
+    wl = dataclasses.replace(W.DSV4_PREFILL, L=3, E=16, k=4, H=512, I=512, T=333, n_slots=5)
+    log("prefill mini, on demand: L=3 E=16 k=4 H=512 I=512 T=333 n=5")
+    run_prefill(wl, decode_after=True)
+
+
+def test_prefill_mini_on_demand_one_pass():
+    """E <= n < 2E with two buffers configured: one on-demand pass over the
+    routed experts; T small enough that some experts are not routed."""
+    wl = dataclasses.replace(W.DSV4_PREFILL, L=3, E=16, k=2, H=512, I=512, T=5, n_slots=20)
+    log("prefill mini, on demand one pass: L=3 E=16 k=2 H=512 I=512 T=5 n=20")
+    run_prefill(wl, decode_after=True)
 
 
 def test_prefill_mini_large_tiles():
