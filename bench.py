@@ -127,6 +127,9 @@ def parse():
                          "expert format + GPU name)")
     ap.add_argument("--prefill-only", action="store_true",
                     help="run only the prefill leg (for profiling); prints its fields")
+    ap.add_argument("--prefill-main-only", action="store_true",
+                    help="with --prefill-only: only the two-buffer passes (no one-buffer or "
+                         "on-demand pass), so every GEMM launch covers a whole layer")
     ap.add_argument("--record-traffic", nargs=3, metavar=("KIND", "FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/traffic.json[KIND] (decode_ffn | prefill_gemm) from the "
                          "counter CSVs of a FETCH_SIZE run and a WRITE_SIZE run of this bench "
@@ -137,7 +140,7 @@ def parse():
     return ap.parse_args()
 
 
-def bench_prefill():
+def bench_prefill(main_only=False):
     """One untimed pass and one timed pass of the DeepSeek-shaped MXFP4
     prefill chunk (8 layers x 8,192 tokens, two full-layer buffers of 256
     experts, the next layer's slab streamed while the current one computes),
@@ -186,25 +189,28 @@ def bench_prefill():
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
         tm = B.moe_ctx_timing(ctx)
-        # the ablation with the second full-layer buffer disabled: each
-        # layer's slab copy waits for the previous layer's compute
-        B.moe_prefill_set_buffers(ctx, 1)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        one_pass()
-        torch.cuda.synchronize()
-        wall1 = time.perf_counter() - t0
-        B.moe_prefill_set_buffers(ctx, 2)
-        # the pool shrunk (elastic resize) to the DeepSeek-shaped decode
-        # budget, which cannot hold two full layers: on-demand loading
-        n_od = W.DSV4_MXFP4.n_slots
-        B.moe_cache_resize(ctx, n_od, 10000)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        one_pass()
-        torch.cuda.synchronize()
-        wall_od = time.perf_counter() - t0
-        used = int((torch.bincount(ids[wl.L - 1].flatten().long(), minlength=wl.E) > 0).sum())
+        wall1 = wall_od = None
+        used, n_od = 0, W.DSV4_MXFP4.n_slots
+        if not main_only:
+            # the ablation with the second full-layer buffer disabled: each
+            # layer's slab copy waits for the previous layer's compute
+            B.moe_prefill_set_buffers(ctx, 1)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            one_pass()
+            torch.cuda.synchronize()
+            wall1 = time.perf_counter() - t0
+            B.moe_prefill_set_buffers(ctx, 2)
+            # the pool shrunk (elastic resize) to the DeepSeek-shaped decode
+            # budget, which cannot hold two full layers: on-demand loading
+            n_od = W.DSV4_MXFP4.n_slots
+            B.moe_cache_resize(ctx, n_od, 10000)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            one_pass()
+            torch.cuda.synchronize()
+            wall_od = time.perf_counter() - t0
+            used = int((torch.bincount(ids[wl.L - 1].flatten().long(), minlength=wl.E) > 0).sum())
         flops = wl.L * 6.0 * wl.H * wl.I * wl.T * wl.k
         gemm_ms = tm["prefill_gemm"]["ms"]
         tflops = flops / (gemm_ms * 1e-3) / 1e12
@@ -225,11 +231,11 @@ def bench_prefill():
             "prefill_layer_ms": round(wall / wl.L * 1e3, 3),
             "prefill_chunk_tok_s": round(wl.T / wall, 1),
             "prefill_copy_gbps": round(slab * copies / (copy_ms * 1e-3) / 1e9, 1) if copy_ms else None,
-            "prefill_single_buffer": {"layer_ms": round(wall1 / wl.L * 1e3, 3),
-                                      "penalty_pct": round((wall1 / wall - 1.0) * 100, 1)},
-            "prefill_on_demand": {"n_slots": n_od, "layer_ms": round(wall_od / wl.L * 1e3, 3),
-                                  "routed_experts_last_layer": used,
-                                  "passes_last_layer": -(-used // n_od)},
+            "prefill_single_buffer": None if main_only else {
+                "layer_ms": round(wall1 / wl.L * 1e3, 3), "penalty_pct": round((wall1 / wall - 1.0) * 100, 1)},
+            "prefill_on_demand": None if main_only else {
+                "n_slots": n_od, "layer_ms": round(wall_od / wl.L * 1e3, 3),
+                "routed_experts_last_layer": used, "passes_last_layer": -(-used // n_od)},
         }
     finally:
         if ctx:
@@ -327,7 +333,7 @@ def main():
     import workload as W
 
     if a.prefill_only:
-        print(json.dumps(bench_prefill()), flush=True)
+        print(json.dumps(bench_prefill(a.prefill_main_only)), flush=True)
         return
     if a.record_traffic:
         kind, fd, wd = a.record_traffic
