@@ -140,3 +140,13 @@ def test_prefill_full_sampled():
     wl = W.DSV4_PREFILL
     log("prefill full: 8 layers x 8192 tokens, E=256, H=4096, I=2048, n=512")
     run_prefill(wl, sample_tokens=4)
+
+
+@pytest.mark.timeout(900)
+def test_prefill_full_on_demand_sampled():
+    """The full chunk at the DeepSeek-shaped decode budget (225 slots, fewer
+    than two full layers), as the bench's on-demand leg runs it: two passes
+    per layer; sampled tokens, tables after every layer, last pass's bytes."""
+    wl = dataclasses.replace(W.DSV4_PREFILL, n_slots=W.DSV4_MXFP4.n_slots)
+    log("prefill full, on demand: 8 layers x 8192 tokens, E=256, H=4096, I=2048, n=225")
+    run_prefill(wl, sample_tokens=4)
