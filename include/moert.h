@@ -211,6 +211,10 @@ moe_status moe_cache_resize(moe_ctx* ctx, int32_t new_n_slots, int32_t timeout_m
  * at most n_slots per pass, into slots [0, P) (one tick per pass; occupants
  * evicted, a pass expert resident elsewhere emptied there), and runs the
  * grouped GEMM over each pass's experts on `stream`; nothing is prefetched.
+ * Cache hits do not cross the bus [satyajit, "Four backends, and the one that has to
+ * be measured", the prefill hit-D2D option]: in
+ * the first pass an expert already in its target slot is not copied and one
+ * resident at or beyond slot P is copied device to device.
  * MOE_ENOSPC if n_slots == 0. */
 moe_status moe_prefill_layer(moe_ctx* ctx, int32_t layer, const void* x, int32_t T,
                              const int32_t* ids, const float* w, void* y, moe_stream stream);

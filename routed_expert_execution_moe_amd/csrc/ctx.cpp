@@ -835,7 +835,7 @@ static moe_status prefill_setup(moe_ctx* ctx) {
   MOE_HIP(ctx, hipMalloc((void**)&pf.hmid, 2 * Tk * c.inter));
   MOE_HIP(ctx, hipMalloc((void**)&pf.prow, 4 * Tk * c.hidden));
   MOE_HIP(ctx, hipMalloc((void**)&pf.slot_of, 4 * (size_t)c.n_experts));
-  MOE_HIP(ctx, hipHostMalloc((void**)&pf.counts_host, 4 * (size_t)c.n_experts, hipHostMallocDefault));
+  MOE_HIP(ctx, hipHostMalloc((void**)&pf.counts_host, 8 * (size_t)c.n_experts, hipHostMallocDefault));
   for (int b = 0; b < 2; ++b)
     MOE_HIP(ctx, hipEventCreateWithFlags(&pf.ev_copied[b], hipEventDisableTiming));
   MOE_HIP(ctx, hipEventCreateWithFlags(&pf.ev_start, hipEventDisableTiming));
@@ -881,11 +881,17 @@ moe_status moert::prefill_settle(moe_ctx* ctx, hipStream_t s) {
 // On-demand prefill, used when the pool cannot hold the full-layer buffers
 // (signalovernoise essay; snackonai, "The Architecture, Unpacked"): the
 // layer's routed experts are known only after routing, so the host reads the
-// per-expert counts (one stream synchronisation per layer), then loads the
-// routed experts in ascending order, at most n_slots per pass, into slots
-// [0, P) with one copy per run of consecutive experts, and runs the grouped
+// per-expert counts and the layer's row of id2slot (one stream
+// synchronisation per layer), then loads the routed experts in ascending
+// order, at most n_slots per pass, into slots [0, P), and runs the grouped
 // GEMM over that pass's experts only.  Each pass writes the partial rows of
 // its own pairs, so one merge after the last pass sees every pair once.
+// Cache hits cross no bus (satyajit, "Four backends, and the one that has
+// to be measured": the prefill hit-D2D option): in the first pass an expert already in its target
+// slot is not copied, and one resident in a slot at or beyond P (which no copy
+// of the pass writes) is copied device to device; every other expert comes
+// from its host bank, one copy per run of consecutive experts.  Later passes
+// find nothing of theirs resident: the first pass filled every slot.
 static moe_status prefill_on_demand(moe_ctx* ctx, int32_t layer, const void* x, int32_t T,
                                     const int32_t* ids, const float* w, void* y, hipStream_t s) {
   auto& pf = ctx->pf;
@@ -893,21 +899,40 @@ static moe_status prefill_on_demand(moe_ctx* ctx, int32_t layer, const void* x, 
   moe_status st = prefill_settle(ctx, s);
   if (st != MOE_OK) return st;
   MOE_HIP(ctx, launch_prefill_group(ctx, ids, T, s));
-  MOE_HIP(ctx, hipMemcpyAsync(pf.counts_host, pf.counts, 4 * (size_t)E, hipMemcpyDeviceToHost, s));
+  int32_t* counts = pf.counts_host;
+  int32_t* resident = pf.counts_host + E;
+  MOE_HIP(ctx, hipMemcpyAsync(counts, pf.counts, 4 * (size_t)E, hipMemcpyDeviceToHost, s));
+  MOE_HIP(ctx, hipMemcpyAsync(resident, ctx->id2slot + (size_t)layer * E, 4 * (size_t)E,
+                              hipMemcpyDeviceToHost, s));
   MOE_HIP(ctx, hipStreamSynchronize(s));
   std::vector<int32_t> routed;
   for (int e = 0; e < E; ++e)
-    if (pf.counts_host[e] > 0) routed.push_back(e);
+    if (counts[e] > 0) routed.push_back(e);
   const int n = ctx->n_slots, nu = (int)routed.size();
   for (int p0 = 0; p0 < nu; p0 += n) {
     const int P = std::min(n, nu - p0);
     MOE_HIP(ctx, launch_prefill_pass_admit(ctx, layer, p0, P, s));
     MOE_HIP(ctx, timing_begin(ctx, MOE_T_PREFILL_COPY, s));
     for (int i = 0; i < P;) {
-      int j = i + 1;
-      while (j < P && routed[p0 + j] == routed[p0 + j - 1] + 1) ++j;
+      const int e = routed[p0 + i];
+      const int from = p0 == 0 ? resident[e] : -1;
+      if (from == i) {  // already in place
+        ++i;
+        continue;
+      }
+      if (from >= P) {  // resident beyond the pass's slots: device to device
+        MOE_HIP(ctx, hipMemcpyAsync(ctx->pool.base + (size_t)i * ctx->stride,
+                                    ctx->pool.base + (size_t)from * ctx->stride, ctx->stride,
+                                    hipMemcpyDeviceToDevice, s));
+        ++i;
+        continue;
+      }
+      int j = i + 1;  // a run of consecutive experts that cross the bus
+      while (j < P && routed[p0 + j] == routed[p0 + j - 1] + 1 &&
+             (p0 != 0 || (resident[routed[p0 + j]] != j && resident[routed[p0 + j]] < P)))
+        ++j;
       MOE_HIP(ctx, hipMemcpyAsync(ctx->pool.base + (size_t)i * ctx->stride,
-                                  ctx->host_pool + ((size_t)layer * E + routed[p0 + i]) * ctx->stride,
+                                  ctx->host_pool + ((size_t)layer * E + e) * ctx->stride,
                                   (size_t)(j - i) * ctx->stride, hipMemcpyHostToDevice, s));
       i = j;
     }

@@ -170,7 +170,7 @@ struct moe_ctx {
     int32_t* tiles = nullptr;              // GEMM tile schedule
     int32_t max_tiles = 0;
     int32_t* slot_of = nullptr;            // [E] on-demand pass: slot of each expert, -1 outside
-    int32_t* counts_host = nullptr;        // [E] pinned copy of counts (on-demand)
+    int32_t* counts_host = nullptr;        // [2E] pinned: counts, then the layer's id2slot row (on-demand)
   } pf;
 
   moert::Timing* timing = nullptr;

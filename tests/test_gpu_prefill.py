@@ -150,3 +150,79 @@ def test_prefill_full_on_demand_sampled():
     wl = dataclasses.replace(W.DSV4_PREFILL, n_slots=W.DSV4_MXFP4.n_slots)
     log("prefill full, on demand: 8 layers x 8192 tokens, E=256, H=4096, I=2048, n=225")
     run_prefill(wl, sample_tokens=4)
+
+
+def test_prefill_on_demand_cache_hits():
+    """Decode first: two layers of 16 experts through 24 slots leave some of
+    layer 1's experts in slots 16..23.  An on-demand prefill of layer 1 (one
+    pass of at most 16) then copies those device to device and brings the
+    rest over PCIe; the same chunk once more finds every expert in its pass
+    slot and copies nothing.  The tables
+    follow the oracle's on-demand admission, every pass slot holds its bank's
+    bytes, every token is within tolerance, and decode continues."""
+    import torch
+    wl = dataclasses.replace(W.DSV4_PREFILL, L=2, E=16, k=4, H=512, I=512, T=333, n_slots=24)
+    log("prefill on demand after decode: L=2 E=16 k=4 H=512 I=512 T=333 n=24")
+    g = GpuRun(wl, n_slots=wl.n_slots, max_tokens=8, max_prefill_tokens=wl.T)
+    try:
+        o = OracleRun(wl, g.bank, n_slots=wl.n_slots, max_tokens=8)
+        dl = dataclasses.replace(wl, T=1, steps=12, prefill=False)
+        logits = W.decode_logits(dl)
+
+        def decode_steps(steps):
+            for s in steps:
+                for l in range(wl.L):
+                    xdec = W.hidden(dl, 200 + s, l)
+                    ids_g, _ = g.decode_call(l, logits[s, l], xdec)
+                    ids_o, w_o = o.route(logits[s, l])
+                    assert np.array_equal(ids_g, ids_o)
+                    compare_plan(g.plan_view(1), o.plan(l, ids_o), 1)
+                    ref = o.output(l, x_f64(dl, xdec), ids_o, w_o)
+                    assert rel_err(g.y[:1].float().cpu().numpy().astype(np.float64), ref)[0] <= TOL
+
+        decode_steps(range(10))
+        layer = 1
+        lg = W.prefill_logits(wl, layer)
+        ids_o, w_o = o.route(lg)
+        routed = sorted(set(ids_o.ravel().tolist()))
+        P = min(len(routed), wl.n_slots)
+        i2s = g.tables()[0]
+        beyond = [e for e in routed if i2s[layer * wl.E + e] >= P]
+        in_place = [e for i, e in enumerate(routed) if i2s[layer * wl.E + e] == i]
+        log(f"  before prefill: {len(routed)} routed, resident beyond the pass {beyond}, in place {in_place}")
+        assert beyond, "the scenario must leave a routed expert beyond the pass's slots"
+        dev = g.dev
+        ids = torch.empty((wl.T, wl.k), dtype=torch.int32, device=dev)
+        w = torch.empty((wl.T, wl.k), dtype=torch.float32, device=dev)
+        y = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device=dev)
+        x = W.hidden(wl, 0, layer)
+        g.B.moe_route_topk(g.ctx, torch.from_numpy(lg).to(dev), wl.T, ids, w)
+        g.B.moe_prefill_layer(g.ctx, layer, g.to_dev_x(x), wl.T, ids, w, y)
+        torch.cuda.synchronize()
+        assert np.array_equal(ids.cpu().numpy(), ids_o)
+        passes = OP.prefill_on_demand(o.st, layer, ids_o.ravel(), wl.E)
+        assert len(passes) == 1
+        i2s, s2i, ts, tick = g.tables()
+        assert i2s == o.st.id2slot and s2i == o.st.slot2id and ts == o.st.slot_ts and tick == o.st.tick
+        for i, e in enumerate(passes[0]):
+            assert np.array_equal(g.slot_bytes(i), g.bank(layer * wl.E + e)), (i, e)
+        ref = OY.moe_layer(x_f64(wl, x), ids_o, w_o, layer, wl.E, o.weights)
+        err, _ = rel_err(y.float().cpu().numpy().astype(np.float64), ref)
+        log(f"  prefill: max rel err {err:.3e}")
+        assert err <= TOL
+        # the same chunk again: every expert is already in its pass slot, so
+        # nothing is copied; tables, bytes and outputs as before
+        y.zero_()
+        g.B.moe_prefill_layer(g.ctx, layer, g.to_dev_x(x), wl.T, ids, w, y)
+        torch.cuda.synchronize()
+        assert OP.prefill_on_demand(o.st, layer, ids_o.ravel(), wl.E) == passes
+        i2s, s2i, ts, tick = g.tables()
+        assert i2s == o.st.id2slot and s2i == o.st.slot2id and ts == o.st.slot_ts and tick == o.st.tick
+        for i, e in enumerate(passes[0]):
+            assert np.array_equal(g.slot_bytes(i), g.bank(layer * wl.E + e)), (i, e)
+        err2, _ = rel_err(y.float().cpu().numpy().astype(np.float64), ref)
+        log(f"  prefill again (all in place): max rel err {err2:.3e}")
+        assert err2 <= TOL
+        decode_steps(range(10, 12))
+    finally:
+        g.close()
