@@ -167,13 +167,15 @@ def plan(st: Residency, layer: int, ids, E: int, K: int, bw_pcie: int, bw_host: 
 def resize(st: Residency, n_new: int):
     """Rebuild the slot pool under a new budget without touching the host
     pool (satyajit, "Elastic memory ..."; snackonai, "Resizing the cache
-    without a restart").  Reading: shrinking evicts in the same order the LRU
-    surfaces victims, (tick, slot) ascending, until min(n_new, occupied)
-    experts remain; the survivors are packed to slots 0.. in
-    ascending old-slot order (every move goes to a lower or equal index, so
-    copying in that order is safe in place), keep their ticks; dropped ids
-    become non-resident; growing appends empty slots.  Returns the moves
-    [(old_slot, new_slot)] in copy order."""
+    without a restart": shrinking costs throughput and nothing else).
+    Reading: shrinking evicts in the same order the LRU surfaces victims,
+    (tick, slot) ascending, until min(n_new, occupied) experts remain; a
+    survivor below n_new stays in its slot, and the survivors at or above
+    n_new move, in ascending old-slot order, into the free slots below n_new
+    in ascending order, so the fewest bytes move and no move reads a slot
+    another move writes.  Survivors keep their ticks; dropped ids become
+    non-resident; growing appends empty slots.  Returns the moves
+    [(old_slot, new_slot)]."""
     assert n_new >= 0
     n = st.n_slots
     occupied = [s for s in range(n) if st.slot2id[s] >= 0]
@@ -184,13 +186,18 @@ def resize(st: Residency, n_new: int):
             st.id2slot[st.slot2id[s]] = -1
     new_ids = [-1] * n_new
     new_ts = [-1] * n_new
-    moves = []
-    for j, s in enumerate(sorted(keep)):
+    for s in sorted(keep):
+        if s < n_new:
+            new_ids[s] = st.slot2id[s]
+            new_ts[s] = st.slot_ts[s]
+    free = [j for j in range(n_new) if new_ids[j] < 0]
+    movers = [s for s in sorted(keep) if s >= n_new]
+    moves = list(zip(movers, free))
+    for s, j in moves:
         u = st.slot2id[s]
         new_ids[j] = u
         new_ts[j] = st.slot_ts[s]
         st.id2slot[u] = j
-        moves.append((s, j))
     st.slot2id = new_ids
     st.slot_ts = new_ts
     return moves

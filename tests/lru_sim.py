@@ -4,7 +4,10 @@ It keeps the slots in an OrderedDict ordered from least to most recently used
 (a recency list, not timestamps).  After each call the slots the call touched
 move to the most-recent end in ascending slot order, which is the batch
 semantics the oracle expresses with one tick per call and (tick, slot)
-ordering.  The split q uses Python's round() on exact fractions.
+ordering.  Each slot also remembers the number of the call that last touched
+it, only so that a resize, which renumbers slots, can put the slots one call
+touched back in ascending order of their new numbers.  The split q uses
+Python's round() on exact fractions.
 """
 from collections import OrderedDict
 from fractions import Fraction
@@ -16,6 +19,8 @@ class RecencySim:
     def __init__(self, n_slots):
         self.order = OrderedDict((s, None) for s in range(n_slots))
         self.where = {}
+        self.stamp = {}
+        self.calls = 0
 
     @property
     def n(self):
@@ -25,6 +30,8 @@ class RecencySim:
         c = RecencySim(0)
         c.order = OrderedDict(self.order)
         c.where = dict(self.where)
+        c.stamp = dict(self.stamp)
+        c.calls = self.calls
         return c
 
     def call(self, layer, ids, E, K, bp, bh, mode, max_fetch=0):
@@ -53,8 +60,10 @@ class RecencySim:
             self.order[s] = u
             self.where[u] = s
             fills.append((u, s, -1 if old is None else old))
+        self.calls += 1
         for s in sorted(hit_slots | {v for v in victims[:q]}):
             self.order.move_to_end(s)
+            self.stamp[s] = self.calls
         slot_map = [[self.where.get(layer * E + int(e), -1) for e in row] for row in ids]
         return dict(uniq=uniq, hits=hits, misses=misses, q=q, victims=victims, fills=fills,
                     cpu=misses[q:], slot_map=slot_map)
@@ -65,13 +74,20 @@ class RecencySim:
         for s in occupied:
             if s not in keep:
                 del self.where[self.order[s]]
-        renum = {s: j for j, s in enumerate(sorted(keep))}
-        new = OrderedDict((j, None) for j in range(len(keep), n_new))
-        for s in keep:
+        # survivors below the budget keep their slot; the rest take the
+        # lowest free slots below it, in ascending order of their old slot
+        stay = {s for s in keep if s < n_new}
+        holes = iter(j for j in range(n_new) if j not in stay)
+        renum = {s: (s if s in stay else next(holes)) for s in sorted(keep)}
+        taken = set(renum.values())
+        new = OrderedDict((j, None) for j in range(n_new) if j not in taken)
+        stamp = {renum[s]: self.stamp[s] for s in keep}
+        for s in sorted(keep, key=lambda s: (self.stamp[s], renum[s])):
             u = self.order[s]
             new[renum[s]] = u
             self.where[u] = renum[s]
         self.order = new
+        self.stamp = stamp
 
     def recency_order(self):
         return list(self.order.keys())

@@ -248,10 +248,18 @@ def test_resize_keeps_most_recent_and_moves_forward():
     lru_first = sorted([s for s in range(12) if st.slot2id[s] >= 0],
                        key=lambda s: (st.slot_ts[s], s))
     keep_ids = {st.slot2id[s] for s in lru_first[-5:]}
+    before = st.copy()
     moves = P.resize(st, 5)
     assert {u for u in st.slot2id if u >= 0} == keep_ids
-    assert all(j <= s for s, j in moves)
-    assert [j for _, j in moves] == list(range(len(moves)))
+    # survivors below the budget stay; only those beyond it move, into the
+    # lowest free slots, sources and destinations disjoint
+    assert all(s >= 5 > j for s, j in moves)
+    assert [s for s, _ in moves] == sorted(s for s in range(5, 12) if before.slot2id[s] in keep_ids)
+    for s in range(5):
+        if before.slot2id[s] in keep_ids:
+            assert st.slot2id[s] == before.slot2id[s] and st.slot_ts[s] == before.slot_ts[s]
+    holes = [j for j in range(5) if before.slot2id[j] not in keep_ids]
+    assert [j for _, j in moves] == holes[:len(moves)]
     P.resize(st, 9)
     assert st.slot2id[5:] == [-1] * 4 and st.slot_ts[5:] == [-1] * 4
 
@@ -386,3 +394,22 @@ def test_prefill_on_demand_invariants():
             if s >= 0:
                 pi = next(i for i, p in enumerate(passes) if u - layer * E in p)
                 assert st.slot_ts[s] == before.tick + pi + 1
+
+
+def test_resize_worked_example():
+    """n = 6, slots hold u = 10..15 with ticks [5, 1, 6, 2, 7, 3]; resize to
+    3 keeps the three most recent (ticks 7, 6, 5: slots 4, 2, 0).  Slots 0
+    and 2 are below the budget and stay; slot 4 moves to the only free slot
+    below it, 1.  Then growing to 5 appends two empty slots and moves
+    nothing."""
+    st = P.Residency(20, 6)
+    st.slot2id = [10, 11, 12, 13, 14, 15]
+    st.slot_ts = [5, 1, 6, 2, 7, 3]
+    for s, u in enumerate(st.slot2id):
+        st.id2slot[u] = s
+    st.tick = 7
+    assert P.resize(st, 3) == [(4, 1)]
+    assert st.slot2id == [10, 14, 12] and st.slot_ts == [5, 7, 6]
+    assert [st.id2slot[u] for u in range(10, 16)] == [0, -1, 2, -1, 1, -1]
+    assert P.resize(st, 5) == []
+    assert st.slot2id == [10, 14, 12, -1, -1] and st.slot_ts == [5, 7, 6, -1, -1]
