@@ -118,6 +118,7 @@ def parse():
     ap.add_argument("--cpu-baseline-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-elastic", action="store_true", help="skip the resize-schedule leg")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the decode run replayed from a captured HIP graph")
     ap.add_argument("--no-calibrated", action="store_true",
@@ -469,6 +470,61 @@ def main():
         measured.update(bw_pcie_mbps=prof["bw_pcie_mbps"], bw_host_mbps=prof["bw_host_mbps"],
                         bw_h2d_mbps=prof["bw_h2d_mbps"], recommended_mode=prof["backend"])
 
+    def run_elastic():
+        """The 8-stream workload's resize schedule (37% -> 15% -> 30% -> 30% of
+        the pool) applied to a decode context of this workload at a safe point
+        between steps: wall time of each moe_cache_resize (synchronous), the
+        slots kept and moved (device-to-device compaction), and a checksum of
+        the whole host pool before and after (the library never writes it)."""
+        from concurrent.futures import ThreadPoolExecutor
+        hiplib = ctypes.CDLL("libamdhip64.so.7")
+        hiplib.hipMemcpy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int]
+
+        def slot_table(ctx):
+            v = B.moe_plan_view_get(ctx)
+            out = np.empty(v.n_slots, np.int32)
+            assert hiplib.hipMemcpy(out.ctypes.data, v.slot2id, out.nbytes, 2) == 0
+            return out
+
+        def checksum():
+            words = pool_np.view(np.uint64)
+            parts = np.array_split(np.arange(len(words)), 16)
+            with ThreadPoolExecutor(16) as ex:
+                sums = ex.map(lambda r: int(np.add.reduce(words[r[0]:r[-1] + 1], dtype=np.uint64)), parts)
+            return sum(sums) & (2 ** 64 - 1)
+
+        ck0 = checksum()
+        ctx = B.moe_create(make_cfg(0), pool, pool_bytes)
+        try:
+            def dec(s):
+                for l in range(wl.L):
+                    B.moe_route_topk(ctx, lg_d[s, l], wl.T, ids[l], w[l])
+                    B.moe_cache_plan(ctx, l, ids[l], wl.T, x_d[s, l])
+                    B.moe_expert_ffn(ctx, l, x_d[s, l], wl.T)
+                    B.moe_merge(ctx, w[l], wl.T, y[l])
+            for s in range(min(64, n_run)):
+                dec(s)
+            torch.cuda.synchronize()
+            res = []
+            for _, n_new in sorted(W.QWEN_ELASTIC.resize.items()):
+                before = slot_table(ctx)
+                t0 = time.perf_counter()
+                B.moe_cache_resize(ctx, n_new, 60_000)
+                ms = (time.perf_counter() - t0) * 1e3
+                after = slot_table(ctx)
+                where = {int(u): i for i, u in enumerate(before) if u >= 0}
+                moved = sum(1 for i, u in enumerate(after) if u >= 0 and where[int(u)] != i)
+                res.append({"to_slots": n_new, "ms": round(ms, 3), "occupied_before": len(where),
+                            "kept": int((after >= 0).sum()), "moved_slots": moved,
+                            "moved_bytes_d2d": moved * stride})
+                for s in range(16):
+                    dec((64 + 16 * len(res) + s) % n_run)
+                torch.cuda.synchronize()
+        finally:
+            B.moe_destroy(ctx)
+        return {"schedule": W.QWEN_ELASTIC.name + " resize points, on this decode context",
+                "resizes": res, "host_pool_unchanged": checksum() == ck0}
+
     if not a.no_calibrated:
         dt_m, _, sm0, sm1 = run(0, calibrate)
         acc_m = (sm1.hits - sm0.hits) + (sm1.fills - sm0.fills) + (sm1.cpu - sm0.cpu)
@@ -476,6 +532,7 @@ def main():
                         fills_per_layer=round((sm1.fills - sm0.fills) / (steps * wl.L), 3),
                         cpu_experts_per_layer=round((sm1.cpu - sm0.cpu) / (steps * wl.L), 3),
                         miss_rate=round(1 - (sm1.hits - sm0.hits) / max(acc_m, 1), 4))
+    elastic = None if a.no_elastic else run_elastic()
     calls = steps * wl.L
     us_per_layer = dt / calls * 1e6
     n_gpu_experts = (st1.hits - st0.hits) + (st1.fills - st0.fills)
@@ -539,6 +596,7 @@ def main():
         "miss_rate": round(1 - (st1.hits - st0.hits) / max(accesses, 1), 4),
         "fills_per_layer": round((st1.fills - st0.fills) / calls, 3),
         "cpu_experts_per_layer": round((st1.cpu - st0.cpu) / calls, 3),
+        "elastic_resize": elastic,
     }
     pool_np = None
     B.moe_host_pool_free(pool)

@@ -183,10 +183,11 @@ moe_status moe_merge(moe_ctx* ctx, const float* w, int32_t T, void* y, moe_strea
  * "Elastic memory, because the machine is not yours"; snackonai, "Resizing
  * the cache without a restart"].  Drains the context's streams (waiting up to
  * timeout_ms, else MOE_ETIMEDOUT with nothing changed), evicts in LRU victim
- * order until min(new_n_slots, occupied) experts remain, packs the survivors
- * to slots 0.. in ascending old-slot order with device-to-device copies (each
- * to a lower or equal index), keeps their recency, and maps or unmaps device
- * memory beyond the new budget.  The host pool is never read or written.
+ * order until min(new_n_slots, occupied) experts remain, leaves a survivor
+ * below the new budget in its slot and moves the survivors beyond it into the
+ * free slots below it (both in ascending order; one device-to-device copy
+ * kernel, since no move reads a slot another move writes), keeps their
+ * recency, and maps or unmaps device memory beyond the new budget.  The host pool is never read or written.
  * 0 <= new_n_slots <= max_slots.  Synchronous. */
 moe_status moe_cache_resize(moe_ctx* ctx, int32_t new_n_slots, int32_t timeout_ms);
 

@@ -189,7 +189,11 @@ static moe_status pool_create(moe_ctx* ctx) {
         g == 0) {
       P.vmm = false;
     } else {
-      size_t chunk = (size_t)64 << 20;
+      // chunks of 1/64 of the reserved range, 64 MiB to 1 GiB: every map or
+      // unmap call costs about a quarter of a millisecond whatever its size,
+      // so a large pool resizes in few calls and a small one keeps a fine
+      // granularity
+      const size_t chunk = std::min<size_t>((size_t)1 << 30, std::max<size_t>((size_t)64 << 20, want / 64));
       P.gran = (chunk + g - 1) / g * g;
       P.reserved = std::max<size_t>(P.gran, (want + P.gran - 1) / P.gran * P.gran);
       void* base = nullptr;
@@ -674,27 +678,42 @@ extern "C" moe_status moe_cache_resize(moe_ctx* ctx, int32_t new_n, int32_t time
   size_t n_keep = std::min<size_t>((size_t)new_n, occ.size());
   std::vector<char> keep(std::max(1, n), 0);
   for (size_t i = lru.size() - n_keep; i < lru.size(); ++i) keep[lru[i]] = 1;
-  // new tables
+  // new tables: a survivor below new_n keeps its slot; the survivors at or
+  // beyond it take the free slots below it, both in ascending order, so the
+  // fewest bytes move and no move reads a slot another move writes
   std::vector<int32_t> i2s((size_t)ctx->n_ids, -1);
   std::vector<int32_t> ns2i(std::max(1, new_n), -1);
   std::vector<int64_t> nts(std::max(1, new_n), -1);
-  std::vector<std::pair<int32_t, int32_t>> moves;
-  int32_t j = 0;
-  for (int s = 0; s < n; ++s) {
+  std::vector<int32_t> moves;  // (from, to) pairs
+  for (int s = 0; s < std::min(n, new_n); ++s) {
     if (!keep[s]) continue;
-    ns2i[j] = s2i[s];
-    nts[j] = ts[s];
-    i2s[s2i[s]] = j;
-    if (s != j) moves.push_back({s, j});
-    ++j;
+    ns2i[s] = s2i[s];
+    nts[s] = ts[s];
+    i2s[s2i[s]] = s;
   }
-  // grow the mapping first, copy survivors forward, then release the tail
+  int32_t hole = 0;
+  for (int s = new_n; s < n; ++s) {
+    if (!keep[s]) continue;
+    while (ns2i[hole] >= 0) ++hole;  // a free slot below new_n exists: kept <= new_n
+    ns2i[hole] = s2i[s];
+    nts[hole] = ts[s];
+    i2s[s2i[s]] = hole;
+    moves.push_back(s);
+    moves.push_back(hole);
+  }
+  const int n_moves = (int)moves.size() / 2;
+  // grow the mapping first, move the survivors, then release the tail
   size_t need = (size_t)std::max(new_n, n) * ctx->stride;
   if ((st = pool_map_to(ctx, need)) != MOE_OK) return st;
-  for (auto& mv : moves)
-    MOE_HIP(ctx, hipMemcpyAsync(ctx->pool.base + (size_t)mv.second * ctx->stride,
-                                ctx->pool.base + (size_t)mv.first * ctx->stride, ctx->stride,
-                                hipMemcpyDeviceToDevice, ctx->copy));
+  int32_t* moves_dev = nullptr;
+  if (n_moves) {
+    MOE_HIP(ctx, hipMalloc((void**)&moves_dev, 4 * moves.size()));
+    hipError_t e = hipMemcpyAsync(moves_dev, moves.data(), 4 * moves.size(), hipMemcpyHostToDevice, ctx->copy);
+    if (e == hipSuccess) e = launch_slot_moves(ctx, moves_dev, n_moves, ctx->copy);
+    if (e == hipSuccess) e = hipStreamSynchronize(ctx->copy);
+    (void)hipFree(moves_dev);
+    MOE_HIP(ctx, e);
+  }
   MOE_HIP(ctx, hipMemcpyAsync(ctx->id2slot, i2s.data(), 4 * i2s.size(), hipMemcpyHostToDevice, ctx->copy));
   if (new_n) {
     MOE_HIP(ctx, hipMemcpyAsync(ctx->slot2id, ns2i.data(), 4 * (size_t)new_n, hipMemcpyHostToDevice, ctx->copy));

@@ -143,4 +143,39 @@ hipError_t launch_merge(moe_ctx* ctx, const float* w, int T, void* y, hipStream_
   return hipGetLastError();
 }
 
+// Resize compaction: moves[2i] -> moves[2i+1], whole slots of `stride`
+// bytes.  No move reads a slot another move writes (the survivors beyond the
+// new budget go to free slots below it), so every move runs at once: kParts
+// workgroups per move, each copying a contiguous part with four 16-byte
+// loads in flight per lane.
+constexpr int kMoveParts = 32;
+
+__global__ __launch_bounds__(256) void slot_move_kernel(uint8_t* __restrict__ base, size_t stride,
+                                                        const int32_t* __restrict__ moves) {
+  const int mv = blockIdx.x / kMoveParts, part = blockIdx.x % kMoveParts;
+  const u32x4* src = (const u32x4*)(base + (size_t)moves[2 * mv] * stride);
+  u32x4* dst = (u32x4*)(base + (size_t)moves[2 * mv + 1] * stride);
+  const size_t n16 = stride / 16, per = (n16 + kMoveParts - 1) / kMoveParts;
+  const size_t b = (size_t)part * per, e = b + per < n16 ? b + per : n16;
+  size_t i = b + threadIdx.x;
+  for (; i + 3 * 256 < e; i += 4 * 256) {
+    const u32x4 v0 = __builtin_nontemporal_load(src + i);
+    const u32x4 v1 = __builtin_nontemporal_load(src + i + 256);
+    const u32x4 v2 = __builtin_nontemporal_load(src + i + 512);
+    const u32x4 v3 = __builtin_nontemporal_load(src + i + 768);
+    __builtin_nontemporal_store(v0, dst + i);
+    __builtin_nontemporal_store(v1, dst + i + 256);
+    __builtin_nontemporal_store(v2, dst + i + 512);
+    __builtin_nontemporal_store(v3, dst + i + 768);
+  }
+  for (; i < e; i += 256) __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
+}
+
+hipError_t launch_slot_moves(moe_ctx* ctx, const int32_t* moves, int n_moves, hipStream_t s) {
+  if (n_moves <= 0) return hipSuccess;
+  hipLaunchKernelGGL(slot_move_kernel, dim3((unsigned)n_moves * kMoveParts), dim3(256), 0, s,
+                     ctx->pool.base, ctx->stride, moves);
+  return hipGetLastError();
+}
+
 }  // namespace moert

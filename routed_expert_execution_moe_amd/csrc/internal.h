@@ -200,6 +200,9 @@ hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* 
 hipError_t launch_plan(moe_ctx* ctx, int layer, const int32_t* ids, int T, const void* x,
                        hipStream_t s);
 hipError_t launch_fill(moe_ctx* ctx, hipStream_t s);
+// resize compaction: n_moves (from, to) slot pairs (device, int32 [n][2]),
+// no slot both read and written
+hipError_t launch_slot_moves(moe_ctx* ctx, const int32_t* moves, int n_moves, hipStream_t s);
 // the fill kernel on explicit lists: q = counts->q experts fill_u[i] of the
 // mapped host banks to dst + fill_slot[i] * stride
 hipError_t launch_fill_lists(const uint8_t* host_dev, uint8_t* dst, size_t stride,
