@@ -119,6 +119,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-elastic", action="store_true", help="skip the resize-schedule leg")
+    ap.add_argument("--max-fetch", type=int, default=0,
+                    help="cap on PCIe fills per layer call (0: none); also bounds the victim list")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the decode run replayed from a captured HIP graph")
     ap.add_argument("--no-calibrated", action="store_true",
@@ -360,7 +362,7 @@ def main():
         return B.config(wl.L, wl.E, wl.k, wl.H, wl.I, wl.w_dtype, wl.act_dtype, wl.n_slots,
                         max_slots=max([wl.n_slots] + list(wl.resize.values())), max_tokens=wl.T,
                         bw_pcie_mbps=wl.bw_pcie_mbps, bw_host_mbps=wl.bw_host_mbps, mode=mode,
-                        timing=timing)
+                        max_fetch=a.max_fetch, timing=timing)
 
     stride = B.moe_expert_bytes(make_cfg(0))
     pool_bytes = wl.n_ids * stride
@@ -572,7 +574,7 @@ def main():
         "config": {"workload": wl.name, "layers": wl.L, "experts": wl.E, "top_k": wl.k,
                    "hidden": wl.H, "inter": wl.I, "slots": wl.n_slots, "tokens_per_call": wl.T,
                    "mode": a.mode, "bw_pcie_mbps": wl.bw_pcie_mbps,
-                   "bw_host_mbps": wl.bw_host_mbps},
+                   "bw_host_mbps": wl.bw_host_mbps, "max_fetch": a.max_fetch},
         "roofline": {
             "bound": "hbm",
             "kernel": "expert FFN (gate/up GEMV + down GEMV over the unique GPU-resident experts)",
