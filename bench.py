@@ -130,6 +130,8 @@ def parse():
                          "expert format + GPU name)")
     ap.add_argument("--prefill-only", action="store_true",
                     help="run only the prefill leg (for profiling); prints its fields")
+    ap.add_argument("--prefill-tokens", type=int, default=None,
+                    help="with --prefill-only: chunk length other than the workload's 8,192")
     ap.add_argument("--prefill-main-only", action="store_true",
                     help="with --prefill-only: only the two-buffer passes (no one-buffer or "
                          "on-demand pass), so every GEMM launch covers a whole layer")
@@ -143,7 +145,7 @@ def parse():
     return ap.parse_args()
 
 
-def bench_prefill(main_only=False):
+def bench_prefill(main_only=False, tokens=None):
     """One untimed pass and one timed pass of the DeepSeek-shaped MXFP4
     prefill chunk (8 layers x 8,192 tokens, two full-layer buffers of 256
     experts, the next layer's slab streamed while the current one computes),
@@ -161,6 +163,9 @@ def bench_prefill(main_only=False):
     import workload as W
 
     wl = W.DSV4_PREFILL
+    if tokens:  # another chunk length of the same workload (the one-buffer penalty sweep)
+        import dataclasses
+        wl = dataclasses.replace(wl, T=tokens)
     dev = torch.device("cuda:0")
     cfg = B.config(wl.L, wl.E, wl.k, wl.H, wl.I, wl.w_dtype, wl.act_dtype, wl.n_slots,
                    max_tokens=1, bw_pcie_mbps=wl.bw_pcie_mbps, bw_host_mbps=wl.bw_host_mbps,
@@ -336,7 +341,7 @@ def main():
     import workload as W
 
     if a.prefill_only:
-        print(json.dumps(bench_prefill(a.prefill_main_only)), flush=True)
+        print(json.dumps(bench_prefill(a.prefill_main_only, a.prefill_tokens)), flush=True)
         return
     if a.record_traffic:
         kind, fd, wd = a.record_traffic
