@@ -31,10 +31,14 @@ def run_decode(wl, mode=0, check_output=lambda s, l: True, check_fill=lambda s, 
         for s in range(wl.steps):
             if s in resize:
                 g.B.moe_cache_resize(g.ctx, resize[s], 60_000)
-                o.resize(resize[s])
+                moves = o.resize(resize[s])
                 i2s, s2i, ts, tick = g.tables()
                 assert i2s == o.st.id2slot and s2i == o.st.slot2id and ts == o.st.slot_ts, s
-                log(f"  resized to {resize[s]} before step {s}")
+                # moved survivors (and a few that stayed) hold their banks' bytes
+                stayed = [j for j, u in enumerate(s2i) if u >= 0 and j not in {d for _, d in moves}]
+                for j in [d for _, d in moves][:24] + stayed[:4]:
+                    assert np.array_equal(g.slot_bytes(j), g.bank(s2i[j])), (s, j)
+                log(f"  resized to {resize[s]} before step {s}: {len(moves)} survivors moved")
             for l in range(wl.L):
                 x = W.hidden(wl, s, l)
                 ids_g, w_g = g.decode_call(l, logits[s, l], x)
