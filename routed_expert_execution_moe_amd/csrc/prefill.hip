@@ -136,6 +136,11 @@ __device__ inline float e8m0_scale(uint32_t s) {
 // cost two-way conflicts: 3.0 -> 0.95 conflict cycles per LDS instruction)
 __device__ inline int aswz_key(int row) { return (row >> 1) & 7; }
 __device__ inline int swz(int row, int chunk) { return row * kRowBytes + ((chunk ^ aswz_key(row)) << 4); }
+// B rows: 64 codes = 32 B, two 16-byte halves; a lane reads half kg of row n
+// (n = 32 consecutive rows per 32 lanes).  Rows 8 apart share banks, so the
+// halves of rows with (n / 8) odd are stored swapped (0.95 -> 0 conflict
+// cycles per LDS instruction together with the A swizzle)
+__device__ inline int bswz_half(int row, int half) { return half ^ ((row >> 3) & 1); }
 
 struct GemmArgs {
   const uint8_t* slot_base;   // slot s at slot_base + s * stride
@@ -241,8 +246,9 @@ __global__ __launch_bounds__(kGemmThreads, 2) void grouped_gemm_kernel(GemmArgs 
   // each); lane l fills slot l of a block: row 8*blk + l/8, slot l%8, which
   // holds chunk (l%8) ^ aswz_key(row) of that row (the XOR swizzle).  B: wave w
   // fills blocks 2w, 2w+1 (32 rows of 32 bytes); lane l: row 32*blk + l/2,
-  // half l%2.  Scales: wave w fills rows 64w..64w+63, 4 bytes each (the
-  // blocks of two K steps).  Waves 0-1 copy gate rows, 2-3 up rows (GLU).
+  // LDS half l%2, which holds the row's half bswz_half(row, l%2).  Scales:
+  // wave w fills rows 64w..64w+63, 4 bytes each (the blocks of two K steps).
+  // Waves 0-1 copy gate rows, 2-3 up rows (GLU).
   const uint8_t* a_base = (const uint8_t*)a.a_src;
   uint32_t a_off[4];
 #pragma unroll
@@ -258,7 +264,8 @@ __global__ __launch_bounds__(kGemmThreads, 2) void grouped_gemm_kernel(GemmArgs 
   uint32_t b_off[2];
 #pragma unroll
   for (int q = 0; q < 2; ++q)
-    b_off[q] = (uint32_t)((mrow_base + (wave * 2 + q) * 32 + (lane >> 1)) * (K / 2) + (lane & 1) * 16);
+    b_off[q] = (uint32_t)((mrow_base + (wave * 2 + q) * 32 + (lane >> 1)) * (K / 2) +
+                          bswz_half((wave * 2 + q) * 32 + (lane >> 1), lane & 1) * 16);
   const uint32_t s_off = (uint32_t)((mrow_base + wave * 64 + lane) * (K / 32));
 
   // the K offset advances the (scalar) base, the per-lane offsets stay fixed
@@ -308,7 +315,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void grouped_gemm_kernel(GemmArgs 
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
         const int n = brow[j] + lr;
-        braw[j] = *(const uint4*)(sb + n * 32 + kg * 16);
+        braw[j] = *(const uint4*)(sb + n * 32 + bswz_half(n, kg) * 16);
         bsc[j] = e8m0_scale(ss[n * 4 + (kt & 1) * 2 + kg]);
       }
       // every A fragment of the step is requested up front, so one LDS
