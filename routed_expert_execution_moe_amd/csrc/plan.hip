@@ -379,7 +379,10 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     pb.gpu_u[p] = u;
     pb.gpu_slot[p] = s_eslot[e];
   }
-  __threadfence_system();  // host block writes visible before the doorbell
+  // host block writes visible before the doorbell; without host work the
+  // outputs are read only by later kernels on this stream, which the kernel
+  // boundary orders (n_cpu is uniform over the workgroup)
+  if (n_cpu > 0) __threadfence_system();
   __syncthreads();
   if (tid == 0) {
     moe_plan_counts c;
