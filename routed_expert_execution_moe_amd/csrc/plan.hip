@@ -379,10 +379,12 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     pb.gpu_u[p] = u;
     pb.gpu_slot[p] = s_eslot[e];
   }
-  // host block writes visible before the doorbell; without host work the
-  // outputs are read only by later kernels on this stream, which the kernel
-  // boundary orders (n_cpu is uniform over the workgroup)
-  if (n_cpu > 0) __threadfence_system();
+  // host block writes visible before the doorbell: every thread that wrote
+  // part of the block (ids and slot map: tid < Tk; x: tid < x_bytes / 16)
+  // releases at system scope before the barrier, after which thread 0 rings.
+  // Threads that wrote only device memory skip the fence: later kernels on
+  // this stream read those outputs, and the kernel boundary orders them.
+  if (n_cpu > 0 && (tid < Tk || tid < a.x_bytes / 16)) __threadfence_system();
   __syncthreads();
   if (tid == 0) {
     moe_plan_counts c;
