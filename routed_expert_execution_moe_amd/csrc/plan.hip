@@ -103,12 +103,17 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     key[i] = s < n ? (uint32_t)(a.slot_ts[s] + 1) : kSentinel;
     sid_r[i] = s < n ? a.slot2id[s] : -1;
   }
+  // the first routed id of this thread and the residency of expert tid of
+  // this layer are requested here too, so neither costs a round trip after
+  // the barrier (nothing in this kernel writes id2slot before classifying)
+  const int id0 = tid < Tk ? a.ids[tid] : 0;
+  const int slot_pre = tid < E ? a.id2slot[a.layer * E + tid] : -1;
   __syncthreads();
   const int64_t tick = s_tick;
 
   // -------------------------------------------------------------- 1. dedup
   for (int i = tid; i < Tk; i += kPlanThreads) {
-    int e = a.ids[i];
+    int e = i == tid ? id0 : a.ids[i];
     if (e >= 0 && e < E) atomicOr(&s_mask[e >> 5], 1u << (e & 31));
     else atomicAdd(&s_bad, 1);  // out-of-range ids: zero rows from the host branch
   }
@@ -118,8 +123,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   const int e = tid;
   const bool present = e < E && ((s_mask[e >> 5] >> (e & 31)) & 1u);
   const int u = a.layer * E + e;
-  int slot = -1;
-  if (present) slot = a.id2slot[u];
+  const int slot = present ? slot_pre : -1;
   const bool hit = present && slot >= 0;
   const bool miss = present && slot < 0;
   const uint64_t b_pres = __ballot(present), b_hit = __ballot(hit), b_miss = __ballot(miss);
