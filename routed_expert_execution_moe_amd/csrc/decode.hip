@@ -114,13 +114,31 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ w,
   }
   const int h = blockIdx.x * blockDim.x + threadIdx.x;
   if (h >= H) return;
+  // eight pairs at a time: their partial values and weights are all
+  // requested before the first product, so the loads' latencies overlap
+  // (the rows were just written on other XCDs and come from HBM); the sum
+  // still runs over ascending j
   float acc = 0.f;
-  for (int j = 0; j < k; ++j) {
-    const int p = t * k + j;
-    float v;
-    if (slot_map[p] >= 0) v = pg[(size_t)p * H + h];
-    else v = __hip_atomic_load(pc + (size_t)p * H + h, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-    acc = fmaf(w[p], v, acc);
+  for (int j0 = 0; j0 < k; j0 += 8) {
+    float v[8], wv[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int p = t * k + j0 + q;
+      v[q] = 0.f;
+      wv[q] = 0.f;
+      if (j0 + q < k) {
+        wv[q] = w[p];
+        // one load form for both sources (a system-scope load is what the
+        // host rows need; the device rows, written by an earlier kernel on
+        // this stream, read the same through it), so no load waits at a
+        // branch join
+        const float* src = (slot_map[p] >= 0 ? pg : pc) + (size_t)p * H + h;
+        v[q] = __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      if (j0 + q < k) acc = fmaf(wv[q], v[q], acc);
   }
   if constexpr (AT == MOE_F32) {
     ((float*)y)[(size_t)t * H + h] = acc;
