@@ -423,22 +423,53 @@ template <int AT>
 __global__ __launch_bounds__(256) void prefill_merge_kernel(const float* __restrict__ w,
                                                             const int32_t* __restrict__ ids,
                                                             const float* __restrict__ P, int k, int H,
-                                                            int E, void* __restrict__ y) {
-  const int t = blockIdx.y;
-  const int h = blockIdx.x * blockDim.x + threadIdx.x;
-  if (h >= H) return;
-  float acc = 0.f;
-  for (int j = 0; j < k; ++j) {
-    const int p = t * k + j;
-    const int e = ids[p];
-    if (e >= 0 && e < E) acc = fmaf(w[p], P[(size_t)p * H + h], acc);
+                                                            int E, int T, void* __restrict__ y) {
+  // four tokens per workgroup, one wave each; lane l holds columns 4l..4l+3
+  // of the workgroup's 256-column slice and reads them as one 16-byte load
+  // per pair.  Eight pairs are requested before the first product, so their
+  // HBM latencies overlap; the sum still runs over ascending j per column.
+  const int t = __builtin_amdgcn_readfirstlane(blockIdx.y * 4 + (threadIdx.x >> 6));
+  if (t >= T) return;
+  const int h = blockIdx.x * 256 + (threadIdx.x & 63) * 4;
+  float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+  for (int j0 = 0; j0 < k; j0 += 8) {
+    float4 v[8];
+    float wv[8];
+    bool ok[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int p = t * k + j0 + q;
+      ok[q] = false;
+      wv[q] = 0.f;
+      v[q] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (j0 + q < k) {
+        const int e = ids[p];
+        ok[q] = e >= 0 && e < E;  // pairs of no expert contribute nothing
+        if (ok[q]) {
+          wv[q] = w[p];
+          v[q] = *(const float4*)&P[(size_t)p * H + h];
+        }
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      if (ok[q]) {
+        a0 = fmaf(wv[q], v[q].x, a0);
+        a1 = fmaf(wv[q], v[q].y, a1);
+        a2 = fmaf(wv[q], v[q].z, a2);
+        a3 = fmaf(wv[q], v[q].w, a3);
+      }
   }
-  if constexpr (AT == MOE_F32) {
-    ((float*)y)[(size_t)t * H + h] = acc;
-  } else {
-    uint32_t u = __float_as_uint(acc);
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    ((uint16_t*)y)[(size_t)t * H + h] = (uint16_t)(u >> 16);
+  const float acc[4] = {a0, a1, a2, a3};
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    if constexpr (AT == MOE_F32) {
+      ((float*)y)[(size_t)t * H + h + c] = acc[c];
+    } else {
+      uint32_t u = __float_as_uint(acc[c]);
+      u += 0x7FFFu + ((u >> 16) & 1u);
+      ((uint16_t*)y)[(size_t)t * H + h + c] = (uint16_t)(u >> 16);
+    }
   }
 }
 
@@ -510,8 +541,9 @@ hipError_t launch_prefill_merge(moe_ctx* ctx, const int32_t* ids, const float* w
   const int E = c.n_experts, k = c.top_k, H = c.hidden;
   hipError_t e = timing_begin(ctx, MOE_T_PREFILL_MERGE, s);
   if (e != hipSuccess) return e;
-  dim3 mg((H + 255) / 256, T);
-  hipLaunchKernelGGL(prefill_merge_kernel<MOE_BF16>, mg, dim3(256), 0, s, w, ids, ctx->pf.prow, k, H, E, y);
+  // H is a multiple of 256 for every context that runs prefill
+  dim3 mg(H / 256, (T + 3) / 4);
+  hipLaunchKernelGGL(prefill_merge_kernel<MOE_BF16>, mg, dim3(256), 0, s, w, ids, ctx->pf.prow, k, H, E, T, y);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   return timing_end(ctx, s);
 }
