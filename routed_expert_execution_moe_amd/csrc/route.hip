@@ -5,10 +5,11 @@
 // 64-bit key, its order-preserving unsigned image above the complement of
 // its index, so one unsigned maximum ranks larger logits first and equal
 // logits by lower index (NaN counts as -inf, -0 as +0).  k rounds of a wave
-// maximum pick the experts (DPP within each row of 16 lanes, two swaps
-// across rows); the winner's key is then cleared.  The softmax over the k
-// selected logits gives the weights.  The pages leave the router design out
-// of scope (snackonai, "The Promise"); a softmax router is the assumption.
+// maximum pick the experts (DPP within each row of 16 lanes, then the four
+// row maxima read as scalars); the winner's key is then cleared.  The
+// softmax over the k selected logits gives the weights.  The pages leave the
+// router design out of scope (snackonai, "The Promise"); a softmax router is
+// the assumption.
 #include "internal.h"
 
 namespace moert {
@@ -35,11 +36,11 @@ __device__ inline uint64_t dpp_max(uint64_t k) {
   return o > k ? o : k;
 }
 
-__device__ inline uint64_t xor_max(uint64_t k, int off) {
-  const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)k, off);
-  const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(k >> 32), off);
-  const uint64_t o = ((uint64_t)hi << 32) | lo;
-  return o > k ? o : k;
+// the key of lane l as a wave-uniform value
+__device__ inline uint64_t lane_key(uint64_t k, int l) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)k, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(k >> 32), l);
+  return ((uint64_t)hi << 32) | lo;
 }
 
 template <int PER>
@@ -68,8 +69,11 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
     b = dpp_max<0x4E>(b);   // quad_perm [2,3,0,1]
     b = dpp_max<0x141>(b);  // row_half_mirror
     b = dpp_max<0x140>(b);  // row_mirror
-    b = xor_max(b, 16);
-    b = xor_max(b, 32);
+    // every lane now holds its row's maximum; the four rows' maxima are
+    // read as scalars, so the wave maximum needs no trip through LDS
+    const uint64_t r0 = lane_key(b, 0), r1 = lane_key(b, 16), r2 = lane_key(b, 32), r3 = lane_key(b, 48);
+    const uint64_t m01 = r0 > r1 ? r0 : r1, m23 = r2 > r3 ? r2 : r3;
+    b = m01 > m23 ? m01 : m23;
 #pragma unroll
     for (int i = 0; i < PER; ++i) key[i] = key[i] == b ? 0 : key[i];
     if (lane == j) my_key = b;
