@@ -56,6 +56,9 @@ __global__ void group_zero_kernel(int32_t* counts, int32_t* cursor, int E) {
   }
 }
 
+// pairs per workgroup in the histogram and the scatter
+constexpr int kGroupChunk = 2048;
+
 __global__ __launch_bounds__(256) void group_hist_kernel(const int32_t* __restrict__ ids, int Tk, int E,
                                                          int32_t* counts) {
   __shared__ int32_t h[kMaxExperts];
@@ -100,13 +103,41 @@ __global__ __launch_bounds__(1024) void group_scan_kernel(const int32_t* counts,
   }
 }
 
+// Each workgroup takes a chunk of kGroupChunk consecutive pairs: ranks inside
+// the chunk come from LDS atomics, then one global atomic per (workgroup,
+// expert) reserves the chunk's run in that expert's range, so the shared
+// cursors see at most E atomics per workgroup instead of one per pair.
 __global__ __launch_bounds__(256) void group_scatter_kernel(const int32_t* __restrict__ ids, int Tk,
                                                             int E, const int32_t* offsets,
                                                             int32_t* cursor, int32_t* perm) {
-  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < Tk; i += gridDim.x * blockDim.x) {
-    int e = ids[i];
-    if (e >= 0 && e < E) perm[offsets[e] + atomicAdd(&cursor[e], 1)] = i;
+  __shared__ int32_t s_n[kMaxExperts];
+  constexpr int kPer = kGroupChunk / 256;
+  for (int e = threadIdx.x; e < E; e += blockDim.x) s_n[e] = 0;
+  __syncthreads();
+  const int base = blockIdx.x * kGroupChunk + threadIdx.x;
+  int ex[kPer], rank[kPer];
+#pragma unroll
+  for (int q = 0; q < kPer; ++q) {
+    const int i = base + q * 256;
+    ex[q] = -1;
+    rank[q] = 0;
+    if (i < Tk) {
+      const int e = ids[i];
+      if (e >= 0 && e < E) {
+        ex[q] = e;
+        rank[q] = atomicAdd(&s_n[e], 1);
+      }
+    }
   }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    const int n = s_n[e];
+    s_n[e] = n ? offsets[e] + atomicAdd(&cursor[e], n) : 0;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < kPer; ++q)
+    if (ex[q] >= 0) perm[s_n[ex[q]] + rank[q]] = base + q * 256;
 }
 
 // ------------------------------------------------------------------ GEMM
@@ -480,7 +511,9 @@ hipError_t launch_prefill_group(moe_ctx* ctx, const int32_t* ids, int T, hipStre
   hipError_t e = timing_begin(ctx, MOE_T_PREFILL_GROUP, s);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(group_zero_kernel, dim3((E + 255) / 256), dim3(256), 0, s, pf.counts, pf.cursor, E);
-  const int gb = std::min(1024, (Tk + 255) / 256);
+  // one workgroup per chunk of pairs: the scatter covers every pair without
+  // a stride loop; the histogram takes the same grid (its loop strides)
+  const int gb = (Tk + kGroupChunk - 1) / kGroupChunk;
   hipLaunchKernelGGL(group_hist_kernel, dim3(gb), dim3(256), 0, s, ids, Tk, E, pf.counts);
   hipLaunchKernelGGL(group_scan_kernel, dim3(1), dim3(1024), 0, s, pf.counts, E, pf.offsets, pf.tiles);
   hipLaunchKernelGGL(group_scatter_kernel, dim3(gb), dim3(256), 0, s, ids, Tk, E, pf.offsets,
