@@ -80,13 +80,17 @@ __global__ __launch_bounds__(1024) void group_scan_kernel(const int32_t* counts,
                                                           int32_t* offsets, int32_t* tiles) {
   __shared__ int32_t s_off[kMaxExperts + 1];
   __shared__ int32_t s_toff[kMaxExperts + 1];
+  __shared__ int32_t s_cnt[kMaxExperts];
+  // the counts come into LDS in parallel, so the serial walk below reads LDS
+  for (int e = threadIdx.x; e < E; e += blockDim.x) s_cnt[e] = counts[e];
+  __syncthreads();
   if (threadIdx.x == 0) {
     int o = 0, t = 0;
     for (int e = 0; e < E; ++e) {
       s_off[e] = o;
       s_toff[e] = t;
-      o += counts[e];
-      t += (counts[e] + kBM - 1) / kBM;
+      o += s_cnt[e];
+      t += (s_cnt[e] + kBM - 1) / kBM;
     }
     s_off[E] = o;
     s_toff[E] = t;
@@ -95,9 +99,10 @@ __global__ __launch_bounds__(1024) void group_scan_kernel(const int32_t* counts,
   for (int e = threadIdx.x; e <= E; e += blockDim.x) offsets[e] = s_off[e];
   if (threadIdx.x == 0) offsets[E + 1] = s_toff[E];
   for (int e = threadIdx.x; e < E; e += blockDim.x) {
-    const int nt = (counts[e] + kBM - 1) / kBM;
+    const int c = s_cnt[e];
+    const int nt = (c + kBM - 1) / kBM;
     for (int m = 0; m < nt; ++m) {
-      const int half = counts[e] - m * kBM <= kBM / 2;  // a last tile of at most 64 rows
+      const int half = c - m * kBM <= kBM / 2;  // a last tile of at most 64 rows
       tiles[s_toff[e] + m] = (e << 20) | ((m * kBM / 64) << 1) | half;
     }
   }
