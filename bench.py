@@ -344,7 +344,7 @@ def main():
     a = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if a.gpus != 1 or world != 1:
-        print(f"bench.py runs on one GPU only: this build has no multi-GPU path "
+        print(f"bench.py runs on one GPU only: the library has no multi-GPU path "
               f"(asked for --gpus {a.gpus}, WORLD_SIZE {world}).", file=sys.stderr)
         sys.exit(2)
 
