@@ -155,8 +155,12 @@ moe_status moe_cache_plan(moe_ctx* ctx, int32_t layer, const int32_t* ids, int32
 
 /* Grouped SwiGLU evaluation of every GPU-resident routed expert of the last
  * plan (hits and fills; each slot's weights read once per call) into the
- * context's fp32 partial rows P_gpu[T][k][H].  x (device) [T][H] act dtype;
- * layer and T must equal the last moe_cache_plan's. */
+ * context's fp32 partial rows P_gpu[T][k][H] [snackonai, "The Code,
+ * Annotated", "The split policy itself": the GPU path runs the cache update,
+ * then the batched copy, then grouped evaluation of the resident experts].
+ * It follows the plan's fill on the same stream.  x (device) [T][H] act
+ * dtype; layer and T must equal the last moe_cache_plan's.  MOE_EINVAL out of
+ * call order (see the conventions above). */
 moe_status moe_expert_ffn(moe_ctx* ctx, int32_t layer, const void* x, int32_t T,
                           moe_stream stream);
 
@@ -187,8 +191,11 @@ moe_status moe_merge(moe_ctx* ctx, const float* w, int32_t T, void* y, moe_strea
  * below the new budget in its slot and moves the survivors beyond it into the
  * free slots below it (both in ascending order; one device-to-device copy
  * kernel, since no move reads a slot another move writes), keeps their
- * recency, and maps or unmaps device memory beyond the new budget.  The host pool is never read or written.
- * 0 <= new_n_slots <= max_slots.  Synchronous. */
+ * recency, and maps or unmaps device memory beyond the new budget.  The host
+ * pool is never read or written.  A full-layer slab that a prefill call
+ * streamed ahead and no call has consumed yet is admitted first (one tick),
+ * as a decode call would admit it.  0 <= new_n_slots <= max_slots.
+ * Synchronous. */
 moe_status moe_cache_resize(moe_ctx* ctx, int32_t new_n_slots, int32_t timeout_ms);
 
 /* One prefill chunk of MoE layer `layer` [satyajit, "Prefill: hide the pool
@@ -204,7 +211,9 @@ moe_status moe_cache_resize(moe_ctx* ctx, int32_t new_n_slots, int32_t timeout_m
  * x (device) [T][H] act dtype; ids (device) int32 [T][k]; w (device) fp32
  * [T][k]; y (device) [T][H].  1 <= T <= max_prefill_tokens.
  * Supported for MXFP4 experts with bf16 activations, H % 256 == 0 and
- * I % 128 == 0 (MOE_EUNSUPPORTED otherwise).
+ * I % 128 == 0 (MOE_EUNSUPPORTED otherwise).  moe_create refuses a
+ * max_prefill_tokens with max_prefill_tokens*H*2 or max_prefill_tokens*k*I*2
+ * at or above 2^32 (the GEMM's per-row byte offsets are 32-bit).
  * When n_slots < buffers x E the buffers do not fit, and the call falls back
  * to on-demand loading instead of oversubscribing [signalovernoise essay;
  * snackonai, "The Architecture, Unpacked"]: it synchronises `stream` once to
@@ -232,7 +241,9 @@ moe_status moe_prefill_set_buffers(moe_ctx* ctx, int32_t n_buffers);
  * residency tables (for inspection and tests; reading them requires the
  * plan's stream to have completed).  Counts layout: see moe_plan_counts. */
 typedef struct {
-  int32_t n_uniq, n_hit, n_miss, q, n_cpu, n_gpu, K, tick_lo;
+  int32_t n_uniq, n_hit, n_miss, q, n_cpu, n_gpu, K;
+  int32_t tick_lo;  /* low 32 bits of the call's LRU tick (the full 64-bit
+                       tick is moe_plan_view.tick)                           */
 } moe_plan_counts;
 
 typedef struct {
@@ -259,6 +270,34 @@ typedef struct {
 } moe_plan_view;
 
 moe_status moe_plan_view_get(moe_ctx* ctx, moe_plan_view* out);
+
+/* Device addresses of the last prefill layer's grouping of its routed
+ * (token, rank) pairs by expert and of its intermediates, for inspection and
+ * tests [satyajit, "Prefill: hide the pool behind the wire": the layer's
+ * tokens are evaluated expert by expert out of the full-layer buffer].
+ * Reading them requires the prefill call's stream to have completed; the next
+ * prefill call overwrites them.  MOE_EINVAL before the first prefill call.
+ *   counts  [E]    routed pairs per expert
+ *   offsets [E+2]  offsets[e] = first position of expert e (exclusive scan of
+ *                  counts, offsets[E] = T*k); offsets[E+1] = number of M-tiles
+ *   perm    [T*k]  position -> pair index t*k + j, the pairs of expert e at
+ *                  positions [offsets[e], offsets[e+1]) in no particular order
+ *   tiles   [offsets[E+1]]  (e << 20) | ((m0 / 64) << 1) | half: the 128-row
+ *                  M-tiles of each expert in order, m0 its first row within the
+ *                  expert, half = 1 for a last tile of at most 64 rows
+ *   hmid    [T*k][I] bf16 silu(gate) * up per position
+ *   prow    [T*k][H] fp32 expert output per pair */
+typedef struct {
+  const int32_t* counts;
+  const int32_t* offsets;
+  const int32_t* perm;
+  const int32_t* tiles;
+  const uint16_t* hmid;
+  const float* prow;
+  int32_t n_experts, max_pairs, max_tiles;
+} moe_prefill_view;
+
+moe_status moe_prefill_view_get(moe_ctx* ctx, moe_prefill_view* out);
 
 /* Pool table [snackonai, "Resizing the cache without a restart"]: occupancy
  * and counters accumulated on the device since moe_create.  Synchronises the

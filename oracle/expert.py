@@ -54,16 +54,19 @@ def e8m0_value(byte: int) -> float:
 
 _E2M1 = np.array([e2m1_value(c) for c in range(16)], dtype=np.float64)
 _E8M0 = np.array([e8m0_value(b) for b in range(256)], dtype=np.float64)
+# the two elements a code byte holds, (low nibble, high nibble) = (even, odd)
+_E2M1_PAIR = np.stack([_E2M1[np.arange(256) & 0x0F], _E2M1[np.arange(256) >> 4]], axis=-1)
 
 
 def mxfp4_matrix(codes: np.ndarray, scales: np.ndarray, rows: int, cols: int) -> np.ndarray:
-    """Dequantise a rows x cols MXFP4 matrix (contraction axis = cols)."""
+    """Dequantise a rows x cols MXFP4 matrix (contraction axis = cols): each
+    code byte gives elements 2i (low nibble) and 2i+1 (high nibble), and each
+    run of 32 elements along a row is multiplied by its E8M0 scale."""
     c = np.asarray(codes, np.uint8).reshape(rows, cols // 2)
     s = np.asarray(scales, np.uint8).reshape(rows, cols // 32)
-    vals = np.empty((rows, cols), np.float64)
-    vals[:, 0::2] = _E2M1[c & 0x0F]
-    vals[:, 1::2] = _E2M1[c >> 4]
-    return vals * np.repeat(_E8M0[s], 32, axis=1)
+    vals = _E2M1_PAIR[c].reshape(rows, cols // 32, 32)
+    vals *= _E8M0[s][:, :, None]
+    return vals.reshape(rows, cols)
 
 
 def expert_weights(raw: np.ndarray, w_dtype: str, H: int, I: int):

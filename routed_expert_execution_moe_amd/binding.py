@@ -52,6 +52,13 @@ class PlanView(ctypes.Structure):
                 ("max_slots", ctypes.c_int32), ("umax", ctypes.c_int32), ("kmax", ctypes.c_int32)]
 
 
+class PrefillView(ctypes.Structure):
+    _fields_ = [("counts", ctypes.c_void_p), ("offsets", ctypes.c_void_p), ("perm", ctypes.c_void_p),
+                ("tiles", ctypes.c_void_p), ("hmid", ctypes.c_void_p), ("prow", ctypes.c_void_p),
+                ("n_experts", ctypes.c_int32), ("max_pairs", ctypes.c_int32),
+                ("max_tiles", ctypes.c_int32)]
+
+
 class Stats(ctypes.Structure):
     _fields_ = [("n_slots", ctypes.c_int32), ("occupied", ctypes.c_int32),
                 ("plans", ctypes.c_int64), ("hits", ctypes.c_int64), ("fills", ctypes.c_int64),
@@ -109,6 +116,7 @@ def lib():
             "moe_set_cpu_layers": ([vp, ctypes.POINTER(ctypes.c_uint8), i32], i32),
             "moe_prefill_layer": ([vp, i32, vp, i32, vp, vp, vp, vp], i32),
             "moe_plan_view_get": ([vp, ctypes.POINTER(PlanView)], i32),
+            "moe_prefill_view_get": ([vp, ctypes.POINTER(PrefillView)], i32),
             "moe_ctx_stats": ([vp, ctypes.POINTER(Stats)], i32),
             "moe_ctx_timing": ([vp, ctypes.POINTER(Timing), i32], i32),
             "moe_strerror": ([i32], ctypes.c_char_p),
@@ -245,6 +253,12 @@ def moe_prefill_layer(ctx, layer, x, T, ids, w, y, stream=None):
 def moe_plan_view_get(ctx) -> PlanView:
     v = PlanView()
     _check(lib().moe_plan_view_get(ctx, ctypes.byref(v)), "moe_plan_view_get")
+    return v
+
+
+def moe_prefill_view_get(ctx) -> PrefillView:
+    v = PrefillView()
+    _check(lib().moe_prefill_view_get(ctx, ctypes.byref(v)), "moe_prefill_view_get")
     return v
 
 

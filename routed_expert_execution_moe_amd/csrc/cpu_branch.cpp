@@ -236,11 +236,13 @@ struct HostBranch {
 
 static void poller(moe_ctx* ctx) {
   HostBranch* hb = ctx->hb;
-  const volatile int64_t* bell = (const volatile int64_t*)ctx->hstage;  // HostBlockHeader::seq
+  // HostBlockHeader::seq, written last by the control kernel after a
+  // system-scope release; an acquire load here orders the block's reads
+  const int64_t* bell = (const int64_t*)ctx->hstage;
   int64_t last = 0;
   int idle = 0;
   while (!hb->stop.load(std::memory_order_relaxed)) {
-    const int64_t s = *bell;
+    const int64_t s = __atomic_load_n(bell, __ATOMIC_ACQUIRE);
     if (s == last) {
       // spin while calls are arriving; back off to short sleeps when idle
       if (++idle < (1 << 16)) {
@@ -251,7 +253,6 @@ static void poller(moe_ctx* ctx) {
       continue;
     }
     idle = 0;
-    std::atomic_thread_fence(std::memory_order_acquire);
     if (ctx->timing) {
       auto t0 = std::chrono::steady_clock::now();
       cpu_branch_body(ctx);
@@ -263,9 +264,8 @@ static void poller(moe_ctx* ctx) {
       cpu_branch_body(ctx);
     }
     last = s;
-    // rows first, then the completion word (x86 stores are not reordered)
-    std::atomic_thread_fence(std::memory_order_release);
-    ((volatile HostSync*)ctx->sync)->done = s;
+    // rows first, then the completion word the merge kernel waits for
+    __atomic_store_n(&ctx->sync->done, s, __ATOMIC_RELEASE);
     hb->last.store(s, std::memory_order_release);
   }
 }
@@ -299,8 +299,8 @@ void host_branch_stop(moe_ctx* ctx) {
 
 bool host_branch_idle(moe_ctx* ctx) {
   if (!ctx->hb) return true;
-  const volatile int64_t* bell = (const volatile int64_t*)ctx->hstage;
-  return ctx->hb->last.load(std::memory_order_acquire) == *bell;
+  return ctx->hb->last.load(std::memory_order_acquire) ==
+         __atomic_load_n((const int64_t*)ctx->hstage, __ATOMIC_ACQUIRE);
 }
 
 // The host branch's arithmetic: SwiGLU of the experts `ex` read in place from

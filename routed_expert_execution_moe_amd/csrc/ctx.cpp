@@ -83,6 +83,13 @@ static std::string validate(const moe_config* c) {
   if (c->cpu_threads < 0) return "cpu_threads must be >= 0";
   if (c->max_prefill_tokens < 0 || c->max_prefill_tokens > 65536) return "max_prefill_tokens must be in 0..65536";
   if ((int64_t)c->n_layers * c->n_experts > (int64_t)1 << 30) return "too many expert ids";
+  // the grouped GEMM addresses an activation row (token rows of x, pair rows
+  // of the intermediate) with a 32-bit byte offset from the tensor's base
+  if (c->max_prefill_tokens > 0 &&
+      ((int64_t)c->max_prefill_tokens * c->hidden * 2 >= ((int64_t)1 << 32) ||
+       (int64_t)c->max_prefill_tokens * c->top_k * c->inter * 2 >= ((int64_t)1 << 32)))
+    return "max_prefill_tokens too large: max_prefill_tokens*hidden*2 and "
+           "max_prefill_tokens*top_k*inter*2 must stay below 2^32 bytes";
   return "";
 }
 
@@ -608,6 +615,22 @@ extern "C" moe_status moe_plan_view_get(moe_ctx* ctx, moe_plan_view* v) {
   return MOE_OK;
 }
 
+extern "C" moe_status moe_prefill_view_get(moe_ctx* ctx, moe_prefill_view* v) {
+  if (!ctx || !v) return fail(nullptr, MOE_EINVAL, "moe_prefill_view_get: NULL argument");
+  const auto& pf = ctx->pf;
+  if (!pf.ready) return fail(ctx, MOE_EINVAL, "moe_prefill_view_get: no prefill layer has run");
+  v->counts = pf.counts;
+  v->offsets = pf.offsets;
+  v->perm = pf.perm;
+  v->tiles = pf.tiles;
+  v->hmid = pf.hmid;
+  v->prow = pf.prow;
+  v->n_experts = ctx->cfg.n_experts;
+  v->max_pairs = ctx->cfg.max_prefill_tokens * ctx->cfg.top_k;
+  v->max_tiles = pf.max_tiles;
+  return MOE_OK;
+}
+
 extern "C" moe_status moe_ctx_stats(moe_ctx* ctx, moe_stats* out) {
   CHECK_CTX(ctx);
   if (!out) return fail(ctx, MOE_EINVAL, "moe_ctx_stats: out is NULL");
@@ -660,6 +683,12 @@ extern "C" moe_status moe_cache_resize(moe_ctx* ctx, int32_t new_n, int32_t time
   if (ctx->state != kIdle) return fail(ctx, MOE_EINVAL, "moe_cache_resize: a layer call is open");
   moe_status st = drain(ctx, timeout_ms);
   if (st != MOE_OK) return st;
+  // a slab streamed ahead for the next prefill layer and not yet consumed is
+  // in its buffer now (drain waited for the copy stream): admit it, as a
+  // decode call would, so the tables describe every slot's bytes before the
+  // keep set is chosen
+  if ((st = prefill_settle(ctx, ctx->copy)) != MOE_OK) return st;
+  MOE_HIP(ctx, hipStreamSynchronize(ctx->copy));
   const int32_t n = ctx->n_slots;
   std::vector<int32_t> s2i(std::max(1, n));
   std::vector<int64_t> ts(std::max(1, n));
@@ -724,9 +753,6 @@ extern "C" moe_status moe_cache_resize(moe_ctx* ctx, int32_t new_n, int32_t time
   MOE_HIP(ctx, hipStreamSynchronize(ctx->copy));
   if ((st = pool_unmap_to(ctx, (size_t)new_n * ctx->stride)) != MOE_OK) return st;
   ctx->n_slots = new_n;
-  // resize drained the copy stream: an unconsumed prefetch is simply gone
-  // (its slots were emptied above unless admitted)
-  ctx->pf.buf_layer[0] = ctx->pf.buf_layer[1] = -1;
   return MOE_OK;
 }
 
@@ -1008,10 +1034,11 @@ extern "C" moe_status moe_prefill_layer(moe_ctx* ctx, int32_t layer, const void*
       (st = prefill_issue(ctx, layer + 1)) != MOE_OK)
     return st;
   MOE_HIP(ctx, hipStreamWaitEvent(s, pf.ev_copied[b], 0));
-  if (!pf.admitted[b]) {
-    MOE_HIP(ctx, launch_prefill_admit(ctx, layer, b, s));
-    pf.admitted[b] = true;
-  }
+  // every prefill layer call takes one tick and stamps the buffer's experts
+  // with it, also when the buffer already holds this layer (a repeated call):
+  // the experts are used again, so their recency is refreshed
+  MOE_HIP(ctx, launch_prefill_admit(ctx, layer, b, s));
+  pf.admitted[b] = true;
   MOE_HIP(ctx, launch_prefill_compute(ctx, layer, x, T, ids, w, y, s));
   return MOE_OK;
 }

@@ -15,13 +15,16 @@
 //              rank sort of the K survivors;
 //   5. rewrite the first q misses take the first q victims; slot_map[t][j]
 //              gets the slot, or -1 for the host.
-// Recency is one tick per call; hits and fills take that tick.
+// Recency is one tick per call; hits and fills take that tick.  The 64-bit
+// ticks enter the select as 32-bit keys relative to the call's tick
+// (lru_key.h), exact across 2^32.
 #include "internal.h"
+#include "lru_key.h"
 
 namespace moert {
 
 constexpr int kWaves = kPlanThreads / 64;
-constexpr uint32_t kSentinel = 0xFFFFFFFFu;
+constexpr uint32_t kSentinel = kLruNoCandidate;
 
 struct PlanArgs {
   const int32_t* ids;
@@ -72,7 +75,6 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   __shared__ int32_t s_scan[kPlanThreads];
   __shared__ int32_t s_scan2[kPlanThreads];
   __shared__ uint64_t s_sel[kMaxExperts];
-  __shared__ int64_t s_tick;
   __shared__ int32_t s_nuniq, s_nhit, s_m, s_q, s_keff, s_evict, s_ngpu, s_bad;
   __shared__ uint32_t s_prefix, s_pmask, s_kk;
   __shared__ uint32_t s_kmin[kWaves], s_kmax[kWaves];
@@ -88,20 +90,23 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   for (int i = tid; i < a.umax * kFfnSub; i += kPlanThreads)
     pb.ffn_done[i * kFfnDoneStride] = 0;  // the expert FFN counts from zero
   if (tid == 0) {
-    s_tick = a.st->tick + 1;
     s_evict = 0;
     s_bad = 0;
   }
   // the slot table rows of this thread's slots, requested now so their
-  // latency overlaps the dedup and classification
-  // (key = tick + 1, so an empty slot's key is 0)
+  // latency overlaps the dedup and classification; each tick becomes its
+  // 32-bit recency key relative to this call's tick (an empty slot's is 0)
+  // (up to 8 slots per thread the occupants are held too; beyond, the
+  // registers go to the keys and a victim's occupant is read when selected)
+  constexpr bool kHoldOld = SPT <= 8;
+  const int64_t now = a.st->tick + 1;
   uint32_t key[SPT];
-  int32_t sid_r[SPT];
+  int32_t sid_r[kHoldOld ? SPT : 1];
 #pragma unroll
   for (int i = 0; i < SPT; ++i) {
     const int s = tid * SPT + i;
-    key[i] = s < n ? (uint32_t)(a.slot_ts[s] + 1) : kSentinel;
-    sid_r[i] = s < n ? a.slot2id[s] : -1;
+    key[i] = s < n ? lru_key(a.slot_ts[s], now) : kSentinel;
+    if constexpr (kHoldOld) sid_r[i] = s < n ? a.slot2id[s] : -1;
   }
   // the first routed id of this thread and the residency of expert tid of
   // this layer are requested here too, so neither costs a round trip after
@@ -109,7 +114,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   const int id0 = tid < Tk ? a.ids[tid] : 0;
   const int slot_pre = tid < E ? a.id2slot[a.layer * E + tid] : -1;
   __syncthreads();
-  const int64_t tick = s_tick;
+  const int64_t tick = now;
 
   // -------------------------------------------------------------- 1. dedup
   for (int i = tid; i < Tk; i += kPlanThreads) {
@@ -172,8 +177,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
 
   // -------------------------------------------------------------- 4. victims
   if (keff > 0) {
-    // keys of this thread's contiguous slots: tick + 1 (empty = 0), hits and
-    // slots past n excluded
+    // keys of this thread's contiguous slots (empty = 0), hits and slots
+    // past n excluded
     const int s0 = tid * SPT;
     uint32_t kmin = kSentinel, kmax = 0;
 #pragma unroll
@@ -306,11 +311,11 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
       const uint32_t kv = key[i];
       const uint64_t packed = ((uint64_t)kv << 32) | (uint32_t)(s0 + i);
       if (kv < tau) {
-        s_selold[pl] = sid_r[i];
+        s_selold[pl] = kHoldOld ? sid_r[kHoldOld ? i : 0] : a.slot2id[s0 + i];
         s_sel[pl++] = packed;
       } else if (kv == tau && kv != kSentinel) {
         if (pe < r) {
-          s_selold[tl + pe] = sid_r[i];
+          s_selold[tl + pe] = kHoldOld ? sid_r[kHoldOld ? i : 0] : a.slot2id[s0 + i];
           s_sel[tl + pe] = packed;
         }
         ++pe;

@@ -3,7 +3,9 @@ oracle side by side, for the GPU parity tests."""
 from __future__ import annotations
 
 import ctypes
+import os
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
@@ -146,6 +148,44 @@ class GpuRun:
             self.pool = None
 
 
+def oracle_threads() -> int:
+    """Threads for decoding expert banks: the host cores this process may
+    use, at most 16 (the GPU machine's CPU share)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+class WindowedWeights:
+    """weights_of(u) for a known order of calls: the next `window` experts of
+    `order` are decoded ahead on a thread pool (numpy releases the GIL while
+    it converts), each handed out once.  Only the scheduling is parallel; the
+    decoding is the oracle's own expert_weights."""
+
+    def __init__(self, order, decode, window=None, pool=None):
+        self.order = list(order)
+        self.decode = decode
+        self.window = window or 2 * oracle_threads()
+        self.pool = pool
+        self.futs = {}
+        self.next = 0
+        self._fill()
+
+    def _fill(self):
+        while self.next < len(self.order) and len(self.futs) < self.window:
+            u = self.order[self.next]
+            self.futs[u] = self.pool.submit(self.decode, u)
+            self.next += 1
+
+    def __call__(self, u):
+        f = self.futs.pop(u, None)
+        w = self.decode(u) if f is None else f.result()
+        self._fill()
+        return w
+
+
 class OracleRun:
     """The oracle's state machine for the same workload."""
 
@@ -182,8 +222,18 @@ class OracleRun:
         self.K = OP.victim_bound(self.max_tokens, self.wl.k, self.wl.E, n_new, self.max_fetch)
         return moves
 
+    def decode_weights(self, u):
+        return OX.expert_weights(self._src(u), self.wl.w_dtype, self.wl.H, self.wl.I)
+
     def output(self, layer, x, ids, w):
-        return OY.moe_layer(x, ids, w, layer, self.wl.E, self.weights)
+        """The fp64 MoE-layer output; the experts are decoded ahead in the
+        order the oracle's layer evaluation asks for them (ascending e)."""
+        order = [layer * self.wl.E + e for e in sorted(set(np.asarray(ids).ravel().tolist()))]
+        if len(order) <= 1:
+            return OY.moe_layer(x, ids, w, layer, self.wl.E, self.weights)
+        with ThreadPoolExecutor(oracle_threads()) as pool:
+            ww = WindowedWeights(order, self.decode_weights, pool=pool)
+            return OY.moe_layer(x, ids, w, layer, self.wl.E, ww)
 
 
 def x_f64(wl, x):
@@ -204,7 +254,7 @@ def compare_plan(gp: dict, op, T):
     assert gp["cpu"] == op.cpu
     assert gp["gpu"] == [tuple(g) for g in op.gpu]
     assert gp["slot_map"] == op.slot_map
-    assert c["tick_lo"] == op.tick
+    assert c["tick_lo"] == ((op.tick + 2**31) % 2**32) - 2**31  # low 32 bits, signed
 
 
 def rel_err(y_gpu, y_ref):

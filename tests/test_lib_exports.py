@@ -65,6 +65,30 @@ def test_expert_bytes_and_validation(lib):
         assert f(ctypes.byref(cfg(**bad))) == 0, bad
 
 
+def test_prefill_row_offsets_stay_32_bit(lib):
+    """The grouped GEMM addresses activation rows with 32-bit byte offsets, so
+    a prefill chunk with T*H*2 or T*k*I*2 at 2^32 bytes or more is refused;
+    the largest chunks just below the bound are accepted."""
+    from routed_expert_execution_moe_amd.binding import MoeConfig
+    f = lib.moe_expert_bytes
+    f.argtypes = [ctypes.POINTER(MoeConfig)]
+    f.restype = ctypes.c_size_t
+
+    def ok(T, k, H, I):
+        c = MoeConfig(n_layers=2, n_experts=256, top_k=k, hidden=H, inter=I, w_dtype=2,
+                      act_dtype=1, n_slots=0, max_slots=0, max_tokens=1, bw_pcie_mbps=1,
+                      bw_host_mbps=1, max_fetch=0, mode=0, cpu_threads=0, max_prefill_tokens=T)
+        return f(ctypes.byref(c)) != 0
+
+    assert ok(8192, 8, 4096, 2048)           # the DeepSeek-shaped chunk
+    assert ok(65536, 8, 4096, 2048)          # T*k*I*2 = 2^31
+    assert ok(65535, 16, 16384, 2048)        # T*H*2 = 2^31 - 2^15, T*k*I*2 just below 2^32
+    assert not ok(65536, 16, 4096, 2048)     # T*k*I*2 = 2^32
+    assert not ok(65536, 8, 4096, 8192)      # T*k*I*2 = 2^33
+    assert not ok(65536, 1, 16384 * 2, 64)   # hidden out of range anyway
+    assert not ok(65536, 32, 64, 4096)       # T*k*I*2 = 2^34
+
+
 def test_strerror(lib):
     lib.moe_strerror.restype = ctypes.c_char_p
     lib.moe_strerror.argtypes = [ctypes.c_int]

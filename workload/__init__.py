@@ -35,10 +35,17 @@ TAG_WEIGHT, TAG_HIDDEN, TAG_NOISE, TAG_PERM, TAG_ROUTER = 1, 2, 3, 4, 5
 
 
 def build(force: bool = False) -> str:
-    """Compile gen.c into _gen.so with gcc (OpenMP)."""
+    """Compile gen.c into _gen.so with gcc (OpenMP).  -ffast-math is a compile
+    flag only: linking with it would add the startup code that sets
+    flush-to-zero / denormals-are-zero for the whole process when the library
+    loads, changing the arithmetic of every other module in it."""
     if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
         tmp = _LIB + ".tmp%d" % os.getpid()
-        subprocess.check_call(["gcc", "-O3", "-ffast-math", "-mavx2", "-mfma", "-fopenmp", "-fPIC", "-shared", "-o", tmp, _SRC, "-lm"])
+        obj = tmp + ".o"
+        subprocess.check_call(["gcc", "-O3", "-ffast-math", "-mavx2", "-mfma", "-fopenmp", "-fPIC", "-c",
+                               "-o", obj, _SRC])
+        subprocess.check_call(["gcc", "-shared", "-fopenmp", "-o", tmp, obj, "-lm"])
+        os.remove(obj)
         os.replace(tmp, _LIB)
     return _LIB
 
