@@ -27,6 +27,13 @@ def hip():
     return _hip
 
 
+def h2d(ptr: int, arr: np.ndarray) -> None:
+    a = np.ascontiguousarray(arr)
+    if a.nbytes:
+        rc = hip().hipMemcpy(ptr, a.ctypes.data, a.nbytes, 1)
+        assert rc == 0, f"hipMemcpy H2D failed: {rc}"
+
+
 def d2h(ptr: int, count: int, dtype) -> np.ndarray:
     out = np.empty(count, dtype)
     if count:
@@ -137,6 +144,16 @@ class GpuRun:
     def p_gpu_rows(self, T):
         v = self.B.moe_plan_view_get(self.ctx)
         return d2h(v.p_gpu, T * self.wl.k * self.wl.H, np.float32).reshape(T, self.wl.k, self.wl.H)
+
+    def prefill_grouping(self, T):
+        """(counts, offsets[E+1], n_tiles, perm, tiles) of the last prefill
+        layer, read back from the device."""
+        v = self.B.moe_prefill_view_get(self.ctx)
+        E, Tk = self.wl.E, T * self.wl.k
+        counts = d2h(v.counts, E, np.int32)
+        off = d2h(v.offsets, E + 2, np.int32)
+        n_tiles = int(off[E + 1])
+        return counts, off[:E + 1], n_tiles, d2h(v.perm, Tk, np.int32), d2h(v.tiles, n_tiles, np.int32)
 
     def close(self):
         if getattr(self, "ctx", None):
@@ -255,6 +272,29 @@ def compare_plan(gp: dict, op, T):
     assert gp["gpu"] == [tuple(g) for g in op.gpu]
     assert gp["slot_map"] == op.slot_map
     assert c["tick_lo"] == ((op.tick + 2**31) % 2**32) - 2**31  # low 32 bits, signed
+
+
+def check_grouping(g, ids, E, T, tile_rows=128):
+    """The GPU's grouping of the prefill layer's T*k pairs against the
+    oracle's (oracle.layer.group_by_expert): per-expert counts and offsets
+    bit-exact; the pairs at each expert's positions are exactly that expert's
+    pairs (order inside an expert is free: every output row is computed on its
+    own); the M-tile list covers each expert's rows once, in order."""
+    from oracle import layer as OY
+    counts, off, n_tiles, perm, tiles = g.prefill_grouping(T)
+    c_o, off_o, perm_o = OY.group_by_expert(ids, E)
+    assert np.array_equal(counts, c_o)
+    assert np.array_equal(off, off_o)
+    assert np.array_equal(np.sort(perm), np.arange(ids.size))  # a permutation of the pairs
+    expert_at = np.repeat(np.arange(E), c_o)                  # expert of each position
+    assert np.array_equal(np.asarray(ids).ravel()[perm], expert_at)
+    want = []
+    for e in range(E):
+        for m in range((int(c_o[e]) + tile_rows - 1) // tile_rows):
+            half = int(c_o[e]) - m * tile_rows <= tile_rows // 2
+            want.append((e << 20) | ((m * tile_rows // 64) << 1) | int(half))
+    assert n_tiles == len(want) and tiles.tolist() == want
+    return c_o
 
 
 def rel_err(y_gpu, y_ref):

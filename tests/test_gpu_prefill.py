@@ -3,10 +3,14 @@ stream, grouped MFMA GEMM over uneven per-expert token counts, merge.
 
 Mid-size: every token of every layer against the fp64 oracle, ragged T
 (not a multiple of the 128-row tile), tables after every layer against the
-oracle's buffer admission, buffer bytes against the host banks, and a decode
-call that follows (what survives prefill seeds decode).  Full size (8 layers,
-8,192 tokens, 256 experts, H 4096, I 2048): sampled tokens against the
-oracle, every token's routing counts, tables and buffer bytes.
+oracle's buffer admission, the GPU's grouping of pairs by expert against the
+oracle's, buffer bytes against the host banks, and a decode call that follows
+(what survives prefill seeds decode).  Full size (8 layers, 8,192 tokens, 256
+experts, H 4096, I 2048): every token of the first layer and 256 sampled
+tokens of each other layer against the oracle, the grouping, tables and
+buffer bytes of every layer, a repeated layer bit-identical, then the same
+chunk through the on-demand fallback after shrinking the pool, bit-identical
+to the two-buffer outputs.
 Tolerance: max |y - y_oracle| <= 2e-2 x RMS(y_oracle) per token."""
 import dataclasses
 
@@ -15,8 +19,8 @@ import pytest
 
 import workload as W
 from oracle import layer as OY, plan as OP
-from tests.harness import (GpuRun, OracleRun, bf16_round_err, compare_plan, log, rel_err,
-                           x_f64)
+from tests.harness import (GpuRun, OracleRun, bf16_round_err, check_grouping, compare_plan, log,
+                           rel_err, x_f64)
 
 pytestmark = pytest.mark.gpu
 TOL = 2e-2
@@ -54,7 +58,7 @@ def run_prefill(wl, sample_tokens=None, check_bytes=True, decode_after=False, bu
             i2s, s2i, ts, tick = g.tables()
             assert i2s == o.st.id2slot and s2i == o.st.slot2id and ts == o.st.slot_ts, l
             assert tick == o.st.tick
-            counts = np.bincount(ids_o.ravel(), minlength=wl.E)
+            counts = check_grouping(g, ids_o, wl.E, wl.T)
             assert counts.sum() == wl.T * wl.k
             if check_bytes and on_demand:
                 for i, e in enumerate(passes[-1]):
@@ -135,21 +139,168 @@ def test_prefill_mini_large_tiles():
     run_prefill(wl)
 
 
+def _bits_to_f64(bits):
+    return W.bf16_bits_to_f32(bits.view(np.uint16)).astype(np.float64)
+
+
 @pytest.mark.timeout(900)
-def test_prefill_full_sampled():
+def test_prefill_full():
+    """The full chunk: 8 layers x 8,192 tokens through two full-layer buffers
+    (512 slots), then the last layer once more, then the pool shrunk to the
+    DeepSeek-shaped decode budget (225 slots, fewer than two full layers) and
+    the same chunk through on-demand loading, then decode."""
+    import torch
     wl = W.DSV4_PREFILL
-    log("prefill full: 8 layers x 8192 tokens, E=256, H=4096, I=2048, n=512")
-    run_prefill(wl, sample_tokens=4)
+    n_od = W.DSV4_MXFP4.n_slots
+    log("prefill full: 8 layers x 8192 tokens, E=256, H=4096, I=2048, n=512, then n=225 on demand")
+    g = GpuRun(wl, n_slots=wl.n_slots, max_tokens=8, max_prefill_tokens=wl.T)
+    try:
+        o = OracleRun(wl, g.bank, n_slots=wl.n_slots, max_tokens=8)
+        dev = g.dev
+        ids = torch.empty((wl.T, wl.k), dtype=torch.int32, device=dev)
+        w = torch.empty((wl.T, wl.k), dtype=torch.float32, device=dev)
+        y = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device=dev)
+        rng = np.random.default_rng(7)
+
+        def layer_call(l):
+            lg = W.prefill_logits(wl, l)
+            x = W.hidden(wl, 0, l)
+            g.B.moe_route_topk(g.ctx, torch.from_numpy(lg).to(dev), wl.T, ids, w)
+            g.B.moe_prefill_layer(g.ctx, l, g.to_dev_x(x), wl.T, ids, w, y)
+            torch.cuda.synchronize()
+            ids_o, w_o = o.route(lg)
+            assert np.array_equal(ids.cpu().numpy(), ids_o), l
+            return x, ids_o, w_o, y.view(torch.int16).cpu().numpy().copy()
+
+        def tables_match(where):
+            i2s, s2i, ts, tick = g.tables()
+            assert i2s == o.st.id2slot and s2i == o.st.slot2id and ts == o.st.slot_ts, where
+            assert tick == o.st.tick, where
+
+        ys = []
+        for l in range(wl.L):
+            x, ids_o, w_o, yb = layer_call(l)
+            b = OP.prefill_admit(o.st, l, wl.E, 2)
+            tables_match(l)
+            counts = check_grouping(g, ids_o, wl.E, wl.T)
+            top = int(np.argmax(counts))
+            for e in sorted({0, wl.E // 2, wl.E - 1, top}):
+                assert np.array_equal(g.slot_bytes(b * wl.E + e), g.bank(l * wl.E + e)), (l, e)
+            ys.append(yb)
+            if l == 0:
+                rows = np.arange(wl.T)
+            else:
+                rows = np.union1d(rng.choice(wl.T, size=256, replace=False), [0, wl.T - 1])
+            xf = x_f64(wl, x)
+            ref = o.output(l, xf[rows], ids_o[rows], w_o[rows])
+            err, _ = rel_err(_bits_to_f64(yb)[rows], ref)
+            log(f"  layer {l}: {len(rows)} tokens, max rel err {err:.3e} (bf16 rounding alone "
+                f"{bf16_round_err(ref):.3e}); experts routed {int((counts > 0).sum())}, n_e "
+                f"{int(counts.min())}..{int(counts.max())}, M-tiles {int(((counts + 127) // 128).sum())}")
+            assert err <= TOL, (l, err)
+
+        # the last layer once more: its buffer already holds it; one more tick,
+        # and the output bit for bit the same (grouping order is free, rows are not)
+        last = wl.L - 1
+        _, ids_o, _, yb = layer_call(last)
+        OP.prefill_admit(o.st, last, wl.E, 2)
+        tables_match("repeat")
+        check_grouping(g, ids_o, wl.E, wl.T)
+        assert np.array_equal(yb, ys[last]), "repeated layer differs"
+        log("  last layer repeated: bit-identical output, tables as the oracle's")
+
+        # shrink to the decode budget: prefill now loads on demand
+        g.B.moe_cache_resize(g.ctx, n_od, 60_000)
+        o.resize(n_od)
+        tables_match("resize")
+        for l in range(wl.L):
+            _, ids_o, _, yb = layer_call(l)
+            passes = OP.prefill_on_demand(o.st, l, ids_o.ravel(), wl.E)
+            tables_match(("on demand", l))
+            check_grouping(g, ids_o, wl.E, wl.T)
+            lp = passes[-1]
+            for i in sorted({0, len(lp) // 2, len(lp) - 1}):
+                assert np.array_equal(g.slot_bytes(i), g.bank(l * wl.E + lp[i])), (l, i)
+            assert np.array_equal(yb, ys[l]), ("on-demand output differs from two buffers", l)
+            log(f"  on demand, layer {l}: {len(passes)} passes, output bit-identical to two buffers")
+
+        # decode continues from what the chunk left resident
+        dl = dataclasses.replace(wl, T=1, steps=2, prefill=False)
+        logits = W.decode_logits(dl)
+        for s_ in range(2):
+            for l in range(wl.L):
+                xdec = W.hidden(dl, 100 + s_, l)
+                ids_g, _ = g.decode_call(l, logits[s_, l], xdec)
+                ids_o, w_o = o.route(logits[s_, l])
+                assert np.array_equal(ids_g, ids_o)
+                compare_plan(g.plan_view(1), o.plan(l, ids_o), 1)
+                ref = o.output(l, x_f64(dl, xdec), ids_o, w_o)
+                assert rel_err(g.y[:1].float().cpu().numpy().astype(np.float64), ref)[0] <= TOL
+        log("  decode after the chunk: plans bit-exact, outputs within tolerance")
+    finally:
+        g.close()
 
 
-@pytest.mark.timeout(900)
-def test_prefill_full_on_demand_sampled():
-    """The full chunk at the DeepSeek-shaped decode budget (225 slots, fewer
-    than two full layers), as the bench's on-demand leg runs it: two passes
-    per layer; sampled tokens, tables after every layer, last pass's bytes."""
-    wl = dataclasses.replace(W.DSV4_PREFILL, n_slots=W.DSV4_MXFP4.n_slots)
-    log("prefill full, on demand: 8 layers x 8192 tokens, E=256, H=4096, I=2048, n=225")
-    run_prefill(wl, sample_tokens=4)
+def test_prefill_then_resize_with_pending_slab():
+    """Prefill layers 0..2 of 4 with two buffers: layer 2's call streams layer
+    3 into the other buffer ahead of time.  A resize at that point admits the
+    pending slab first (as decode would), then keeps the most recent experts;
+    tables bit-exact against the oracle (admit layer 3, then resize), every
+    survivor's slot holds its bank's bytes, and decode continues with plans
+    bit-exact and outputs within tolerance.  Then a grow and the same again."""
+    import torch
+    wl = dataclasses.replace(W.DSV4_PREFILL, L=4, E=16, k=4, H=512, I=512, T=200, n_slots=40)
+    log("prefill then resize with a pending slab: L=4 E=16 k=4 H=512 I=512 T=200 n=40")
+    g = GpuRun(wl, n_slots=wl.n_slots, max_slots=64, max_tokens=8, max_prefill_tokens=wl.T)
+    try:
+        o = OracleRun(wl, g.bank, n_slots=wl.n_slots, max_tokens=8)
+        dev = g.dev
+        ids = torch.empty((wl.T, wl.k), dtype=torch.int32, device=dev)
+        w = torch.empty((wl.T, wl.k), dtype=torch.float32, device=dev)
+        y = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device=dev)
+        dl = dataclasses.replace(wl, T=1, steps=6, prefill=False)
+        logits = W.decode_logits(dl)
+
+        def tables_match(where):
+            i2s, s2i, ts, tick = g.tables()
+            assert i2s == o.st.id2slot and s2i == o.st.slot2id and ts == o.st.slot_ts, where
+            assert tick == o.st.tick, where
+            for sl, u in enumerate(s2i):
+                if u >= 0:
+                    assert np.array_equal(g.slot_bytes(sl), g.bank(u)), (where, sl, u)
+
+        for rnd, n_new in enumerate((17, 64)):
+            for l in range(3):
+                lg = W.prefill_logits(wl, l)
+                x = W.hidden(wl, rnd, l)
+                g.B.moe_route_topk(g.ctx, torch.from_numpy(lg).to(dev), wl.T, ids, w)
+                g.B.moe_prefill_layer(g.ctx, l, g.to_dev_x(x), wl.T, ids, w, y)
+                torch.cuda.synchronize()
+                ids_o, w_o = o.route(lg)
+                if o.st.n_slots >= 2 * wl.E:
+                    OP.prefill_admit(o.st, l, wl.E, 2)
+                else:
+                    OP.prefill_on_demand(o.st, l, ids_o.ravel(), wl.E)
+                ref = OY.moe_layer(x_f64(wl, x), ids_o, w_o, l, wl.E, o.weights)
+                assert rel_err(y.float().cpu().numpy().astype(np.float64), ref)[0] <= TOL
+            if o.st.n_slots >= 2 * wl.E:
+                OP.prefill_admit(o.st, 3, wl.E, 2)  # the slab streamed ahead, admitted by the resize
+            g.B.moe_cache_resize(g.ctx, n_new, 60_000)
+            o.resize(n_new)
+            tables_match(("resize", n_new))
+            for s_ in range(3 * rnd, 3 * rnd + 3):
+                for l in range(wl.L):
+                    xdec = W.hidden(dl, 50 + s_, l)
+                    ids_g, _ = g.decode_call(l, logits[s_, l], xdec)
+                    ids_o, w_o = o.route(logits[s_, l])
+                    assert np.array_equal(ids_g, ids_o)
+                    compare_plan(g.plan_view(1), o.plan(l, ids_o), 1)
+                    ref = o.output(l, x_f64(dl, xdec), ids_o, w_o)
+                    assert rel_err(g.y[:1].float().cpu().numpy().astype(np.float64), ref)[0] <= TOL
+            tables_match(("decode after resize", n_new))
+            log(f"  resized to {n_new} with a pending slab: tables, slot bytes and decode as the oracle's")
+    finally:
+        g.close()
 
 
 def test_prefill_on_demand_cache_hits():

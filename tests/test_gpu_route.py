@@ -16,6 +16,8 @@ CASES = [  # (E, k, T)
     (100, 8, 70),
     (128, 8, 255),  # 64 workgroups of four tokens, the last one ragged
     (256, 8, 33),
+    (300, 8, 40),     # 257..512 experts: eight logits per lane
+    (512, 16, 21),
     (1000, 32, 100),
 ]
 
