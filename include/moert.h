@@ -229,6 +229,31 @@ moe_status moe_cache_resize(moe_ctx* ctx, int32_t new_n_slots, int32_t timeout_m
 moe_status moe_prefill_layer(moe_ctx* ctx, int32_t layer, const void* x, int32_t T,
                              const int32_t* ids, const float* w, void* y, moe_stream stream);
 
+/* moe_prefill_layer for callers that cannot allocate memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * the same call, the same kernels and the same results, but the chunk's
+ * grouping and GEMM intermediates (per-expert counts, offsets and cursors, the
+ * M-tile list, the pair permutation, the bf16 intermediate and the fp32
+ * expert rows) live in the library's fixed device scratch instead of the
+ * block moe_prefill_layer allocates on its first call.  The call makes no
+ * hipMalloc, hipFree or other allocating call; the context's prefill events
+ * and pinned staging already exist (moe_create makes them when
+ * max_prefill_tokens > 0).
+ * Limit: the scratch is 64 MiB per GPU, held from the first moe_create on
+ * that GPU until the process ends.  A chunk fits when its T*k routed pairs
+ * need at most that: about 4*(4E + T*k/128) + T*k*(4 + 2I + 4H) bytes (each
+ * array rounded up to 256 B), i.e. T*k <= 3,275 pairs (T <= 409 at k = 8) for
+ * E = 256, H = 4096, I = 2048.  A larger T returns MOE_EINVAL (moe_last_error() gives
+ * the limit for the context's shape) and enqueues nothing.
+ * Every context on one GPU shares that GPU's scratch, and each call leaves
+ * its intermediates there (moe_prefill_view_get shows them until the next
+ * prefill call on the context): calls on one GPU whose work overlaps in time
+ * (other streams, other contexts, other host threads) race on it; serialise
+ * them.  Everything a call reads from the scratch it first writes or zeroes
+ * on the device (by kernels, not memset nodes). */
+moe_status moe_prefill_layer_noalloc(moe_ctx* ctx, int32_t layer, const void* x, int32_t T,
+                                     const int32_t* ids, const float* w, void* y, moe_stream stream);
+
 /* Full-layer buffers for prefill: 2 (default; the next layer streams while
  * this one computes) or 1 (the ablation the pages measure by disabling the
  * second buffer [snackonai, "It In Action"]: each layer's copy waits for the

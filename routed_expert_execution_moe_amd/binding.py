@@ -115,6 +115,7 @@ def lib():
             "moe_prefill_set_buffers": ([vp, i32], i32),
             "moe_set_cpu_layers": ([vp, ctypes.POINTER(ctypes.c_uint8), i32], i32),
             "moe_prefill_layer": ([vp, i32, vp, i32, vp, vp, vp, vp], i32),
+            "moe_prefill_layer_noalloc": ([vp, i32, vp, i32, vp, vp, vp, vp], i32),
             "moe_plan_view_get": ([vp, ctypes.POINTER(PlanView)], i32),
             "moe_prefill_view_get": ([vp, ctypes.POINTER(PrefillView)], i32),
             "moe_ctx_stats": ([vp, ctypes.POINTER(Stats)], i32),
@@ -248,6 +249,11 @@ def moe_prefill_set_buffers(ctx, n_buffers):
 def moe_prefill_layer(ctx, layer, x, T, ids, w, y, stream=None):
     _check(lib().moe_prefill_layer(ctx, layer, _ptr(x), T, _ptr(ids), _ptr(w), _ptr(y),
                                    _stream(stream)), "moe_prefill_layer")
+
+
+def moe_prefill_layer_noalloc(ctx, layer, x, T, ids, w, y, stream=None):
+    _check(lib().moe_prefill_layer_noalloc(ctx, layer, _ptr(x), T, _ptr(ids), _ptr(w), _ptr(y),
+                                           _stream(stream)), "moe_prefill_layer_noalloc")
 
 
 def moe_plan_view_get(ctx) -> PlanView:

@@ -242,6 +242,18 @@ static int32_t victim_bound(const moe_config& c, int32_t n_slots) {
   return (int32_t)K;
 }
 
+// Largest number of routed pairs whose prefill intermediates fit the fixed
+// device scratch.
+static int64_t scratch_pairs(const moe_config& c) {
+  int64_t lo = 0, hi = (int64_t)65536 * kMaxTopK;
+  while (lo < hi) {
+    const int64_t mid = (lo + hi + 1) / 2;
+    if (prefill_layout(c, mid, nullptr, nullptr) <= kPrefillScratchBytes) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
 static void free_all(moe_ctx* ctx);
 static moe_status timing_create(moe_ctx* ctx);
 static void timing_destroy(moe_ctx* ctx);
@@ -398,6 +410,25 @@ extern "C" moe_status moe_create(const moe_config* cfg, void* host_pool, size_t 
   if (!ctx->cpu) return bail(fail(nullptr, MOE_ENOMEM, "host worker pool"));
   if (!host_branch_start(ctx)) return bail(fail(nullptr, MOE_ENOMEM, "host branch poller"));
   if (cfg->timing && (st = timing_create(ctx)) != MOE_OK) return bail(st);
+  if (cfg->max_prefill_tokens > 0) {
+    // the prefill path's events and pinned staging, and the device address of
+    // the library's fixed scratch on this device (the no-allocation prefill
+    // entry point); moe_prefill_layer's own intermediates wait for its first call
+    auto& pf = ctx->pf;
+    for (int b = 0; b < 2 && e == hipSuccess; ++b)
+      e = hipEventCreateWithFlags(&pf.ev_copied[b], hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&pf.ev_start, hipEventDisableTiming);
+    if (e == hipSuccess)
+      e = hipHostMalloc((void**)&pf.counts_host, 8 * (size_t)cfg->n_experts, hipHostMallocDefault);
+    if (e != hipSuccess) return bail(hip_fail(ctx, e, "prefill events and staging"));
+    e = prefill_scratch_init(ctx->device);
+    if (e != hipSuccess) return bail(hip_fail(ctx, e, "hipGetSymbolAddress of the prefill scratch"));
+    uint8_t* base = prefill_scratch_ptr(ctx->device);
+    const int64_t pairs = std::min<int64_t>((int64_t)cfg->max_prefill_tokens * cfg->top_k,
+                                            scratch_pairs(*cfg));
+    if (base && pairs > 0) prefill_layout(*cfg, pairs, base, &pf.scratch);
+    pf.ready = true;
+  }
   *out = ctx;
   return MOE_OK;
 }
@@ -414,8 +445,7 @@ static void free_all(moe_ctx* ctx) {
   F(ctx->id2slot); F(ctx->slot2id); F(ctx->slot_ts); F(ctx->dstate);
   F(ctx->p_gpu); F(ctx->h_mid); F(ctx->plan_alloc);
   auto& pf = ctx->pf;
-  F(pf.counts); F(pf.offsets); F(pf.cursor); F(pf.perm); F(pf.hmid); F(pf.prow); F(pf.tiles);
-  F(pf.slot_of);
+  F(pf.own_block);
   if (pf.counts_host) (void)hipHostFree(pf.counts_host);
   for (int b = 0; b < 2; ++b)
     if (pf.ev_copied[b]) (void)hipEventDestroy(pf.ev_copied[b]);
@@ -617,17 +647,17 @@ extern "C" moe_status moe_plan_view_get(moe_ctx* ctx, moe_plan_view* v) {
 
 extern "C" moe_status moe_prefill_view_get(moe_ctx* ctx, moe_prefill_view* v) {
   if (!ctx || !v) return fail(nullptr, MOE_EINVAL, "moe_prefill_view_get: NULL argument");
-  const auto& pf = ctx->pf;
-  if (!pf.ready) return fail(ctx, MOE_EINVAL, "moe_prefill_view_get: no prefill layer has run");
-  v->counts = pf.counts;
-  v->offsets = pf.offsets;
-  v->perm = pf.perm;
-  v->tiles = pf.tiles;
-  v->hmid = pf.hmid;
-  v->prow = pf.prow;
+  const PrefillBufs* pb = ctx->pf.last;
+  if (!pb) return fail(ctx, MOE_EINVAL, "moe_prefill_view_get: no prefill layer has run");
+  v->counts = pb->counts;
+  v->offsets = pb->offsets;
+  v->perm = pb->perm;
+  v->tiles = pb->tiles;
+  v->hmid = pb->hmid;
+  v->prow = pb->prow;
   v->n_experts = ctx->cfg.n_experts;
-  v->max_pairs = ctx->cfg.max_prefill_tokens * ctx->cfg.top_k;
-  v->max_tiles = pf.max_tiles;
+  v->max_pairs = (int32_t)pb->max_pairs;
+  v->max_tiles = pb->max_tiles;
   return MOE_OK;
 }
 
@@ -866,25 +896,17 @@ extern "C" moe_status moe_set_split(moe_ctx* ctx, int64_t bw_pcie_mbps, int64_t 
 }
 
 // ------------------------------------------------------------------ prefill
+// moe_prefill_layer's intermediates, sized for max_prefill_tokens, allocated
+// on its first call (one block).
 static moe_status prefill_setup(moe_ctx* ctx) {
   auto& pf = ctx->pf;
-  if (pf.ready) return MOE_OK;
+  if (pf.own_block) return MOE_OK;
   const moe_config& c = ctx->cfg;
-  const size_t Tk = (size_t)c.max_prefill_tokens * c.top_k;
-  MOE_HIP(ctx, hipMalloc((void**)&pf.counts, 4 * (size_t)c.n_experts));
-  MOE_HIP(ctx, hipMalloc((void**)&pf.offsets, 4 * (size_t)(c.n_experts + 2)));
-  pf.max_tiles = (int32_t)(Tk / 128 + c.n_experts);
-  MOE_HIP(ctx, hipMalloc((void**)&pf.tiles, 4 * (size_t)pf.max_tiles));
-  MOE_HIP(ctx, hipMalloc((void**)&pf.cursor, 4 * (size_t)c.n_experts));
-  MOE_HIP(ctx, hipMalloc((void**)&pf.perm, 4 * Tk));
-  MOE_HIP(ctx, hipMalloc((void**)&pf.hmid, 2 * Tk * c.inter));
-  MOE_HIP(ctx, hipMalloc((void**)&pf.prow, 4 * Tk * c.hidden));
-  MOE_HIP(ctx, hipMalloc((void**)&pf.slot_of, 4 * (size_t)c.n_experts));
-  MOE_HIP(ctx, hipHostMalloc((void**)&pf.counts_host, 8 * (size_t)c.n_experts, hipHostMallocDefault));
-  for (int b = 0; b < 2; ++b)
-    MOE_HIP(ctx, hipEventCreateWithFlags(&pf.ev_copied[b], hipEventDisableTiming));
-  MOE_HIP(ctx, hipEventCreateWithFlags(&pf.ev_start, hipEventDisableTiming));
-  pf.ready = true;
+  const int64_t pairs = (int64_t)c.max_prefill_tokens * c.top_k;
+  uint8_t* block = nullptr;
+  MOE_HIP(ctx, hipMalloc((void**)&block, prefill_layout(c, pairs, nullptr, nullptr)));
+  prefill_layout(c, pairs, block, &pf.own);
+  pf.own_block = block;
   return MOE_OK;
 }
 
@@ -937,26 +959,27 @@ moe_status moert::prefill_settle(moe_ctx* ctx, hipStream_t s) {
 // of the pass writes) is copied device to device; every other expert comes
 // from its host bank, one copy per run of consecutive experts.  Later passes
 // find nothing of theirs resident: the first pass filled every slot.
-static moe_status prefill_on_demand(moe_ctx* ctx, int32_t layer, const void* x, int32_t T,
-                                    const int32_t* ids, const float* w, void* y, hipStream_t s) {
+static moe_status prefill_on_demand(moe_ctx* ctx, const PrefillBufs& pb, int32_t layer, const void* x,
+                                    int32_t T, const int32_t* ids, const float* w, void* y, hipStream_t s) {
   auto& pf = ctx->pf;
   const int E = ctx->cfg.n_experts;
   moe_status st = prefill_settle(ctx, s);
   if (st != MOE_OK) return st;
-  MOE_HIP(ctx, launch_prefill_group(ctx, ids, T, s));
+  MOE_HIP(ctx, launch_prefill_group(ctx, pb, ids, T, s));
   int32_t* counts = pf.counts_host;
   int32_t* resident = pf.counts_host + E;
-  MOE_HIP(ctx, hipMemcpyAsync(counts, pf.counts, 4 * (size_t)E, hipMemcpyDeviceToHost, s));
+  MOE_HIP(ctx, hipMemcpyAsync(counts, pb.counts, 4 * (size_t)E, hipMemcpyDeviceToHost, s));
   MOE_HIP(ctx, hipMemcpyAsync(resident, ctx->id2slot + (size_t)layer * E, 4 * (size_t)E,
                               hipMemcpyDeviceToHost, s));
   MOE_HIP(ctx, hipStreamSynchronize(s));
-  std::vector<int32_t> routed;
+  int32_t routed[kMaxExperts];
+  int nu = 0;
   for (int e = 0; e < E; ++e)
-    if (counts[e] > 0) routed.push_back(e);
-  const int n = ctx->n_slots, nu = (int)routed.size();
+    if (counts[e] > 0) routed[nu++] = e;
+  const int n = ctx->n_slots;
   for (int p0 = 0; p0 < nu; p0 += n) {
     const int P = std::min(n, nu - p0);
-    MOE_HIP(ctx, launch_prefill_pass_admit(ctx, layer, p0, P, s));
+    MOE_HIP(ctx, launch_prefill_pass_admit(ctx, pb, layer, p0, P, s));
     MOE_HIP(ctx, timing_begin(ctx, MOE_T_PREFILL_COPY, s));
     for (int i = 0; i < P;) {
       const int e = routed[p0 + i];
@@ -982,9 +1005,9 @@ static moe_status prefill_on_demand(moe_ctx* ctx, int32_t layer, const void* x, 
       i = j;
     }
     MOE_HIP(ctx, timing_end(ctx, s));
-    MOE_HIP(ctx, launch_prefill_gemm(ctx, layer, x, T, pf.slot_of, s));
+    MOE_HIP(ctx, launch_prefill_gemm(ctx, pb, layer, x, T, pb.slot_of, s));
   }
-  MOE_HIP(ctx, launch_prefill_merge(ctx, ids, w, T, y, s));
+  MOE_HIP(ctx, launch_prefill_merge(ctx, pb, ids, w, T, y, s));
   return MOE_OK;
 }
 
@@ -1005,26 +1028,33 @@ extern "C" moe_status moe_prefill_set_buffers(moe_ctx* ctx, int32_t n_buffers) {
   return MOE_OK;
 }
 
-extern "C" moe_status moe_prefill_layer(moe_ctx* ctx, int32_t layer, const void* x, int32_t T,
-                                        const int32_t* ids, const float* w, void* y,
-                                        moe_stream stream) {
-  CHECK_CTX(ctx);
+// Argument checks shared by both prefill entry points.
+static moe_status prefill_check(moe_ctx* ctx, int32_t layer, const void* x, int32_t T, const int32_t* ids,
+                                const float* w, void* y, const char* where) {
   const moe_config& c = ctx->cfg;
   if (!x || !ids || !w || !y || layer < 0 || layer >= c.n_layers || T < 1 || T > c.max_prefill_tokens)
-    return fail(ctx, MOE_EINVAL, "moe_prefill_layer: bad arguments");
-  if (ctx->state != kIdle) return fail(ctx, MOE_EINVAL, "moe_prefill_layer: a decode layer call is open");
+    return fail(ctx, MOE_EINVAL, std::string(where) + ": bad arguments");
+  if (ctx->state != kIdle)
+    return fail(ctx, MOE_EINVAL, std::string(where) + ": a decode layer call is open");
   if (c.w_dtype != MOE_MXFP4 || c.act_dtype != MOE_BF16 || c.hidden % 256 || c.inter % 128)
     return fail(ctx, MOE_EUNSUPPORTED,
-                "moe_prefill_layer: the grouped GEMM takes MXFP4 experts, bf16 activations, "
+                std::string(where) + ": the grouped GEMM takes MXFP4 experts, bf16 activations, "
                 "hidden % 256 == 0 and inter % 128 == 0");
   if (((uintptr_t)x & 15) || ((uintptr_t)ids & 3) || ((uintptr_t)w & 3) || ((uintptr_t)y & 3))
-    return fail(ctx, MOE_EINVAL, "moe_prefill_layer: x must be 16-byte aligned");
+    return fail(ctx, MOE_EINVAL, std::string(where) + ": x must be 16-byte aligned");
+  if (ctx->n_slots < 1) return fail(ctx, MOE_ENOSPC, std::string(where) + ": the slot pool is empty");
+  return MOE_OK;
+}
+
+// One prefill layer on the intermediates `pb`: the two-buffer pipeline, or
+// on-demand loading when the buffers do not fit.  No allocation.
+static moe_status prefill_layer_run(moe_ctx* ctx, const PrefillBufs& pb, int32_t layer, const void* x,
+                                    int32_t T, const int32_t* ids, const float* w, void* y, hipStream_t s) {
+  const moe_config& c = ctx->cfg;
   auto& pf = ctx->pf;
-  if (ctx->n_slots < 1) return fail(ctx, MOE_ENOSPC, "moe_prefill_layer: the slot pool is empty");
-  moe_status st = prefill_setup(ctx);
-  if (st != MOE_OK) return st;
-  hipStream_t s = (hipStream_t)stream;
-  if (ctx->n_slots < pf.buffers * c.n_experts) return prefill_on_demand(ctx, layer, x, T, ids, w, y, s);
+  pf.last = &pb;
+  if (ctx->n_slots < pf.buffers * c.n_experts) return prefill_on_demand(ctx, pb, layer, x, T, ids, w, y, s);
+  moe_status st = MOE_OK;
   const int b = prefill_buffer(ctx, layer);
   MOE_HIP(ctx, hipEventRecord(pf.ev_start, s));
   if (pf.buf_layer[b] != layer && (st = prefill_issue(ctx, layer)) != MOE_OK) return st;
@@ -1039,6 +1069,33 @@ extern "C" moe_status moe_prefill_layer(moe_ctx* ctx, int32_t layer, const void*
   // the experts are used again, so their recency is refreshed
   MOE_HIP(ctx, launch_prefill_admit(ctx, layer, b, s));
   pf.admitted[b] = true;
-  MOE_HIP(ctx, launch_prefill_compute(ctx, layer, x, T, ids, w, y, s));
+  MOE_HIP(ctx, launch_prefill_compute(ctx, pb, layer, x, T, ids, w, y, s));
   return MOE_OK;
+}
+
+extern "C" moe_status moe_prefill_layer(moe_ctx* ctx, int32_t layer, const void* x, int32_t T,
+                                        const int32_t* ids, const float* w, void* y,
+                                        moe_stream stream) {
+  CHECK_CTX(ctx);
+  moe_status st = prefill_check(ctx, layer, x, T, ids, w, y, "moe_prefill_layer");
+  if (st != MOE_OK) return st;
+  if ((st = prefill_setup(ctx)) != MOE_OK) return st;
+  return prefill_layer_run(ctx, ctx->pf.own, layer, x, T, ids, w, y, (hipStream_t)stream);
+}
+
+extern "C" moe_status moe_prefill_layer_noalloc(moe_ctx* ctx, int32_t layer, const void* x, int32_t T,
+                                                const int32_t* ids, const float* w, void* y,
+                                                moe_stream stream) {
+  CHECK_CTX(ctx);
+  moe_status st = prefill_check(ctx, layer, x, T, ids, w, y, "moe_prefill_layer_noalloc");
+  if (st != MOE_OK) return st;
+  const auto& sc = ctx->pf.scratch;
+  const int64_t pairs = (int64_t)T * ctx->cfg.top_k;
+  if (!sc.counts || pairs > sc.max_pairs)
+    return fail(ctx, MOE_EINVAL,
+                "moe_prefill_layer_noalloc: T*top_k = " + std::to_string(pairs) +
+                    " routed pairs exceed the " + std::to_string(sc.max_pairs) +
+                    " whose intermediates fit the library's fixed " +
+                    std::to_string(kPrefillScratchBytes >> 20) + " MiB device scratch at this shape");
+  return prefill_layer_run(ctx, sc, layer, x, T, ids, w, y, (hipStream_t)stream);
 }

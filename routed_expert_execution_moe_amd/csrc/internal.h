@@ -81,6 +81,33 @@ struct SlotPool {
   std::vector<PoolChunk> chunks;
 };
 
+// Device intermediates of one prefill chunk: the grouping of its routed
+// pairs by expert and the two GEMMs' outputs.  One block carved into
+// 256-byte aligned arrays (prefill_layout).
+struct PrefillBufs {
+  int32_t* counts = nullptr;   // [E] pairs per expert
+  int32_t* offsets = nullptr;  // [E+2] exclusive scan; [E+1] = M-tile count
+  int32_t* cursor = nullptr;   // [E] scatter cursors
+  int32_t* slot_of = nullptr;  // [E] on-demand pass: slot of each expert, -1 outside
+  int32_t* tiles = nullptr;    // [max_tiles] M-tile list
+  int32_t* perm = nullptr;     // [max_pairs] position -> pair index
+  uint16_t* hmid = nullptr;    // [max_pairs][I] bf16 intermediate
+  float* prow = nullptr;       // [max_pairs][H] fp32 expert rows
+  int32_t max_tiles = 0;
+  int64_t max_pairs = 0;
+};
+
+// Bytes of the intermediates of a chunk with `pairs` routed pairs; when
+// `base` is given, `out` is pointed into it.
+size_t prefill_layout(const moe_config& c, int64_t pairs, uint8_t* base, PrefillBufs* out);
+
+// The library's fixed device scratch for moe_prefill_layer_noalloc
+// (prefill.hip): its device address on `device`, looked up once per device
+// by prefill_scratch_init (called by moe_create with the device current).
+constexpr size_t kPrefillScratchBytes = (size_t)64 << 20;
+hipError_t prefill_scratch_init(int device);
+uint8_t* prefill_scratch_ptr(int device);
+
 struct CpuPool;     // host worker pool (cpu_branch.cpp)
 struct HostBranch;  // doorbell poller (cpu_branch.cpp)
 
@@ -152,25 +179,20 @@ struct moe_ctx {
   int state = moert::kIdle;
   int32_t cur_layer = -1, cur_T = 0;
 
-  // prefill (allocated lazily on the first prefill call)
+  // prefill: events and pinned staging at creation (max_prefill_tokens > 0);
+  // the intermediates of moe_prefill_layer allocated on its first call
   struct Prefill {
-    bool ready = false;
+    bool ready = false;                    // events and staging exist
     int32_t buffers = 2;                   // full-layer buffers in use (1: no prefetch)
     int32_t buf_layer[2] = {-1, -1};      // layer whose slab was issued into buffer b
     bool admitted[2] = {false, false};     // tables already describe buffer b
     hipEvent_t ev_copied[2] = {nullptr, nullptr};
     hipEvent_t ev_start = nullptr;
-    int32_t* counts = nullptr;             // [E]
-    int32_t* offsets = nullptr;            // [E+1]
-    int32_t* cursor = nullptr;             // [E]
-    int32_t* perm = nullptr;               // [Tmax*k] pair index, grouped by expert
-    uint16_t* xg = nullptr;                // unused placeholder
-    uint16_t* hmid = nullptr;              // [Tmax*k][I] bf16 intermediate
-    float* prow = nullptr;                 // [Tmax*k][H] fp32 partial rows
-    int32_t* tiles = nullptr;              // GEMM tile schedule
-    int32_t max_tiles = 0;
-    int32_t* slot_of = nullptr;            // [E] on-demand pass: slot of each expert, -1 outside
     int32_t* counts_host = nullptr;        // [2E] pinned: counts, then the layer's id2slot row (on-demand)
+    uint8_t* own_block = nullptr;          // moe_prefill_layer's intermediates (one allocation)
+    moert::PrefillBufs own;
+    const moert::PrefillBufs* last = nullptr;  // the set the last prefill call used
+    moert::PrefillBufs scratch;            // moe_prefill_layer_noalloc's, in the device scratch
   } pf;
 
   moert::Timing* timing = nullptr;
@@ -217,17 +239,19 @@ hipError_t launch_merge(moe_ctx* ctx, const float* w, int T, void* y, hipStream_
 hipError_t launch_prefill_admit(moe_ctx* ctx, int layer, int b, hipStream_t s);
 // the full-layer buffer of a prefill layer: layer % 2 with two buffers, else 0
 inline int prefill_buffer(const moe_ctx* ctx, int layer);
-hipError_t launch_prefill_compute(moe_ctx* ctx, int layer, const void* x, int T,
+hipError_t launch_prefill_compute(moe_ctx* ctx, const PrefillBufs& pb, int layer, const void* x, int T,
                                   const int32_t* ids, const float* w, void* y, hipStream_t s);
 // the three phases of launch_prefill_compute: grouping of the routed pairs;
 // GEMM1 + GEMM2 over the experts of the layer's buffer (slot_of == nullptr)
 // or over the experts slot_of maps (others skipped); the merge
-hipError_t launch_prefill_group(moe_ctx* ctx, const int32_t* ids, int T, hipStream_t s);
-hipError_t launch_prefill_gemm(moe_ctx* ctx, int layer, const void* x, int T, const int32_t* slot_of,
-                               hipStream_t s);
-hipError_t launch_prefill_merge(moe_ctx* ctx, const int32_t* ids, const float* w, int T, void* y,
+hipError_t launch_prefill_group(moe_ctx* ctx, const PrefillBufs& pb, const int32_t* ids, int T,
                                 hipStream_t s);
-hipError_t launch_prefill_pass_admit(moe_ctx* ctx, int layer, int p0, int P, hipStream_t s);
+hipError_t launch_prefill_gemm(moe_ctx* ctx, const PrefillBufs& pb, int layer, const void* x, int T,
+                               const int32_t* slot_of, hipStream_t s);
+hipError_t launch_prefill_merge(moe_ctx* ctx, const PrefillBufs& pb, const int32_t* ids, const float* w,
+                                int T, void* y, hipStream_t s);
+hipError_t launch_prefill_pass_admit(moe_ctx* ctx, const PrefillBufs& pb, int layer, int p0, int P,
+                                     hipStream_t s);
 hipError_t launch_table_reset(moe_ctx* ctx, hipStream_t s);
 moe_status prefill_settle(moe_ctx* ctx, hipStream_t s);
 

@@ -558,9 +558,10 @@ __global__ __launch_bounds__(kMaxExperts) void prefill_pass_admit_kernel(int lay
   }
 }
 
-hipError_t launch_prefill_pass_admit(moe_ctx* ctx, int layer, int p0, int P, hipStream_t s) {
+hipError_t launch_prefill_pass_admit(moe_ctx* ctx, const PrefillBufs& pb, int layer, int p0, int P,
+                                     hipStream_t s) {
   hipLaunchKernelGGL(prefill_pass_admit_kernel, dim3(1), dim3(kMaxExperts), 0, s, layer,
-                     ctx->cfg.n_experts, p0, P, ctx->pf.counts, ctx->pf.slot_of, ctx->id2slot,
+                     ctx->cfg.n_experts, p0, P, pb.counts, pb.slot_of, ctx->id2slot,
                      ctx->slot2id, ctx->slot_ts, ctx->dstate);
   return hipGetLastError();
 }

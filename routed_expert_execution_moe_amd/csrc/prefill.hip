@@ -34,6 +34,7 @@
 // buffer (written per wave, read back as 16-byte row pieces), so each lane
 // stores 16 bytes at a time; the pair index of each tile row is read once
 // into LDS at the start.
+#include <mutex>
 #include <type_traits>
 
 #include "internal.h"
@@ -509,10 +510,10 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(const float* __restr
   }
 }
 
-hipError_t launch_prefill_group(moe_ctx* ctx, const int32_t* ids, int T, hipStream_t s) {
+hipError_t launch_prefill_group(moe_ctx* ctx, const PrefillBufs& pf, const int32_t* ids, int T,
+                                hipStream_t s) {
   const moe_config& c = ctx->cfg;
   const int E = c.n_experts, Tk = T * c.top_k;
-  auto& pf = ctx->pf;
   hipError_t e = timing_begin(ctx, MOE_T_PREFILL_GROUP, s);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(group_zero_kernel, dim3((E + 255) / 256), dim3(256), 0, s, pf.counts, pf.cursor, E);
@@ -527,13 +528,12 @@ hipError_t launch_prefill_group(moe_ctx* ctx, const int32_t* ids, int T, hipStre
   return timing_end(ctx, s);
 }
 
-hipError_t launch_prefill_gemm(moe_ctx* ctx, int layer, const void* x, int T, const int32_t* slot_of,
-                               hipStream_t s) {
+hipError_t launch_prefill_gemm(moe_ctx* ctx, const PrefillBufs& pf, int layer, const void* x, int T,
+                               const int32_t* slot_of, hipStream_t s) {
   const moe_config& c = ctx->cfg;
   if (c.w_dtype != MOE_MXFP4 || c.act_dtype != MOE_BF16) return hipErrorNotSupported;
   const int E = c.n_experts, k = c.top_k, H = c.hidden, I = c.inter;
   const int Tk = T * k;
-  auto& pf = ctx->pf;
   hipError_t e = timing_begin(ctx, MOE_T_PREFILL_GEMM, s);
   if (e != hipSuccess) return e;
   GemmArgs a{};
@@ -573,27 +573,83 @@ hipError_t launch_prefill_gemm(moe_ctx* ctx, int layer, const void* x, int T, co
   return timing_end(ctx, s);
 }
 
-hipError_t launch_prefill_merge(moe_ctx* ctx, const int32_t* ids, const float* w, int T, void* y,
-                                hipStream_t s) {
+hipError_t launch_prefill_merge(moe_ctx* ctx, const PrefillBufs& pf, const int32_t* ids, const float* w,
+                                int T, void* y, hipStream_t s) {
   const moe_config& c = ctx->cfg;
   const int E = c.n_experts, k = c.top_k, H = c.hidden;
   hipError_t e = timing_begin(ctx, MOE_T_PREFILL_MERGE, s);
   if (e != hipSuccess) return e;
   // H is a multiple of 256 for every context that runs prefill
   dim3 mg(H / 256, (T + 3) / 4);
-  hipLaunchKernelGGL(prefill_merge_kernel<MOE_BF16>, mg, dim3(256), 0, s, w, ids, ctx->pf.prow, k, H, E, T, y);
+  hipLaunchKernelGGL(prefill_merge_kernel<MOE_BF16>, mg, dim3(256), 0, s, w, ids, pf.prow, k, H, E, T, y);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   return timing_end(ctx, s);
 }
 
-hipError_t launch_prefill_compute(moe_ctx* ctx, int layer, const void* x, int T, const int32_t* ids,
-                                  const float* w, void* y, hipStream_t s) {
+hipError_t launch_prefill_compute(moe_ctx* ctx, const PrefillBufs& pb, int layer, const void* x, int T,
+                                  const int32_t* ids, const float* w, void* y, hipStream_t s) {
   const moe_config& c = ctx->cfg;
   if (c.w_dtype != MOE_MXFP4 || c.act_dtype != MOE_BF16) return hipErrorNotSupported;
-  hipError_t e = launch_prefill_group(ctx, ids, T, s);
-  if (e == hipSuccess) e = launch_prefill_gemm(ctx, layer, x, T, nullptr, s);
-  if (e == hipSuccess) e = launch_prefill_merge(ctx, ids, w, T, y, s);
+  hipError_t e = launch_prefill_group(ctx, pb, ids, T, s);
+  if (e == hipSuccess) e = launch_prefill_gemm(ctx, pb, layer, x, T, nullptr, s);
+  if (e == hipSuccess) e = launch_prefill_merge(ctx, pb, ids, w, T, y, s);
   return e;
+}
+
+// ------------------------------------------------------------------ intermediates
+size_t prefill_layout(const moe_config& c, int64_t pairs, uint8_t* base, PrefillBufs* out) {
+  const size_t E = (size_t)c.n_experts;
+  const int64_t max_tiles = pairs / kBM + c.n_experts;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += (bytes + 255) / 256 * 256;
+    return o;
+  };
+  const size_t o_counts = take(4 * E), o_off = take(4 * (E + 2)), o_cur = take(4 * E),
+               o_slot = take(4 * E), o_tiles = take(4 * (size_t)max_tiles), o_perm = take(4 * (size_t)pairs),
+               o_hmid = take(2 * (size_t)pairs * c.inter), o_prow = take(4 * (size_t)pairs * c.hidden);
+  if (base && out) {
+    out->counts = (int32_t*)(base + o_counts);
+    out->offsets = (int32_t*)(base + o_off);
+    out->cursor = (int32_t*)(base + o_cur);
+    out->slot_of = (int32_t*)(base + o_slot);
+    out->tiles = (int32_t*)(base + o_tiles);
+    out->perm = (int32_t*)(base + o_perm);
+    out->hmid = (uint16_t*)(base + o_hmid);
+    out->prow = (float*)(base + o_prow);
+    out->max_tiles = (int32_t)max_tiles;
+    out->max_pairs = pairs;
+  }
+  return off;
+}
+
+// Fixed device scratch for callers that cannot allocate (the no-allocation
+// prefill entry point): one array per device, held until the process ends.
+// Host code never uses its name as an address: the device address comes from
+// hipGetSymbolAddress, looked up once per device with that device current.
+static __device__ __align__(256) uint8_t scratch[kPrefillScratchBytes];
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static uint8_t* g_scratch_ptr[kMaxDevices] = {};
+
+hipError_t prefill_scratch_init(int device) {
+  if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch_ptr[device]) return hipSuccess;
+  void* p = nullptr;
+  hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  if (e != hipSuccess) return e;
+  if (!p) return hipErrorInvalidSymbol;
+  g_scratch_ptr[device] = (uint8_t*)p;
+  return hipSuccess;
+}
+
+uint8_t* prefill_scratch_ptr(int device) {
+  if (device < 0 || device >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  return g_scratch_ptr[device];
 }
 
 }  // namespace moert
