@@ -66,6 +66,20 @@ def recorded_traffic(kind, workload):
     return t["bytes_per_launch"]
 
 
+def traffic_source(kind, workload):
+    """Where `traffic` comes from: the committed counter record (two rocprofv3
+    --pmc runs, FETCH_SIZE then WRITE_SIZE, of this bench on the named
+    workload with this kernel source), not this run's counters."""
+    if recorded_traffic(kind, workload) is None:
+        return None
+    with open(TRAFFIC_FILE) as fh:
+        t = json.load(fh)[kind]
+    return {"recorded": True, "file": "profiles/traffic.json", "workload": t["workload"],
+            "kernel_source_sha256": t["sha256"][:16],
+            "note": "HBM bytes per launch from earlier counter runs of this kernel source; "
+                    "this run's algorithmic bytes are achieved's numerator"}
+
+
 def record_traffic(kind, workload, fetch_dir, write_dir):
     """Write profiles/traffic.json[kind] from two rocprofv3 --pmc runs (one with
     FETCH_SIZE, one with WRITE_SIZE) of this bench: HBM bytes per dispatch of
@@ -139,6 +153,10 @@ def parse():
                     help="write profiles/traffic.json[KIND] (decode_ffn | prefill_gemm) from the "
                          "counter CSVs of a FETCH_SIZE run and a WRITE_SIZE run of this bench "
                          "(decode: on --workload; prefill: its prefill workload)")
+    ap.add_argument("--no-streams", action="store_true",
+                    help="skip the 8-stream elastic workload leg")
+    ap.add_argument("--streams-only", action="store_true",
+                    help="run only the 8-stream elastic workload leg (for profiling); prints its fields")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain streaming kernel of known size, whose "
                          "FETCH_SIZE / WRITE_SIZE counter readings scale those counters to bytes")
@@ -167,9 +185,10 @@ def bench_prefill(main_only=False, tokens=None):
         import dataclasses
         wl = dataclasses.replace(wl, T=tokens)
     dev = torch.device("cuda:0")
+    n_hd = 2 * wl.E + W.DSV4_MXFP4.n_slots  # two full-layer buffers + the decode budget
     cfg = B.config(wl.L, wl.E, wl.k, wl.H, wl.I, wl.w_dtype, wl.act_dtype, wl.n_slots,
-                   max_tokens=1, bw_pcie_mbps=wl.bw_pcie_mbps, bw_host_mbps=wl.bw_host_mbps,
-                   max_prefill_tokens=wl.T, timing=1)
+                   max_slots=n_hd, max_tokens=1, bw_pcie_mbps=wl.bw_pcie_mbps,
+                   bw_host_mbps=wl.bw_host_mbps, max_prefill_tokens=wl.T, timing=1)
     stride = B.moe_expert_bytes(cfg)
     pool_bytes = wl.n_ids * stride
     pool = B.moe_host_pool_alloc(pool_bytes)
@@ -209,6 +228,7 @@ def bench_prefill(main_only=False, tokens=None):
         torch.cuda.synchronize()
         tm_b2b = B.moe_ctx_timing(ctx)
         wall1 = wall_od = None
+        hd = None
         used, n_od = 0, W.DSV4_MXFP4.n_slots
         if not main_only:
             # the ablation with the second full-layer buffer disabled: each
@@ -230,6 +250,34 @@ def bench_prefill(main_only=False, tokens=None):
             torch.cuda.synchronize()
             wall_od = time.perf_counter() - t0
             used = int((torch.bincount(ids[wl.L - 1].flatten().long(), minlength=wl.E) > 0).sum())
+            # prefill after decode: the pool grown to two buffers plus the
+            # decode budget; 16 decode steps of the DeepSeek-shaped decode
+            # routing (T = 1) leave experts in slots outside the buffers, and
+            # the next two-buffer pass copies those device to device
+            B.moe_cache_resize(ctx, n_hd, 10000)
+            dlg = torch.from_numpy(np.ascontiguousarray(W.decode_logits(W.DSV4_MXFP4, steps=16))).to(dev)
+            i1 = torch.empty((1, wl.k), dtype=torch.int32, device=dev)
+            w1 = torch.empty((1, wl.k), dtype=torch.float32, device=dev)
+            y1 = torch.empty((1, wl.H), dtype=torch.bfloat16, device=dev)
+            for s_ in range(16):
+                for l in range(wl.L):
+                    x1 = x[l, s_:s_ + 1]
+                    B.moe_route_topk(ctx, dlg[s_, l], 1, i1, w1)
+                    B.moe_cache_plan(ctx, l, i1, 1, x1)
+                    B.moe_expert_ffn(ctx, l, x1, 1)
+                    B.moe_merge(ctx, w1, 1, y1)
+            torch.cuda.synchronize()
+            sh0 = B.moe_ctx_stats(ctx)
+            t0 = time.perf_counter()
+            one_pass()
+            torch.cuda.synchronize()
+            wall_hd = time.perf_counter() - t0
+            sh1 = B.moe_ctx_stats(ctx)
+            hd = {"n_slots": n_hd, "decode_steps_before": 16, "layer_ms": round(wall_hd / wl.L * 1e3, 3),
+                  "experts_device_to_device": sh1.prefill_d2d_experts - sh0.prefill_d2d_experts,
+                  "experts_over_pcie": sh1.prefill_h2d_experts - sh0.prefill_h2d_experts,
+                  "pcie_bytes_saved": (sh1.prefill_d2d_experts - sh0.prefill_d2d_experts)
+                  * W.expert_bytes(wl)}
         flops = wl.L * 6.0 * wl.H * wl.I * wl.T * wl.k
         gemm_ms = tm["prefill_gemm"]["ms"]
         tflops = flops / (gemm_ms * 1e-3) / 1e12
@@ -243,7 +291,8 @@ def bench_prefill(main_only=False, tokens=None):
                                  "MXFP4 dequantised in registers)", "achieved": round(tflops, 1),
                                  "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                                  "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
-                                 "traffic": recorded_traffic("prefill_gemm", wl.name)},
+                                 "traffic": recorded_traffic("prefill_gemm", wl.name),
+                                 "traffic_source": traffic_source("prefill_gemm", wl.name)},
             "prefill_gemm_ms_per_layer": round(gemm_ms / wl.L, 3),
             "prefill_gemm_back_to_back": {
                 "note": "the last layer's compute repeated with its buffer resident, no idle between bursts",
@@ -260,6 +309,134 @@ def bench_prefill(main_only=False, tokens=None):
             "prefill_on_demand": None if main_only else {
                 "n_slots": n_od, "layer_ms": round(wall_od / wl.L * 1e3, 3),
                 "routed_experts_last_layer": used, "passes_last_layer": -(-used // n_od)},
+            "prefill_after_decode_hit_d2d": hd,
+        }
+    finally:
+        if ctx:
+            B.moe_destroy(ctx)
+        B.moe_host_pool_free(pool)
+
+
+def bench_streams(steps=64, warmup=8):
+    """The 8-stream elastic workload (Qwen3.6-35B-A3B shape, 8 concurrent
+    batch-1 streams batched into T = 8 per layer call, its own seed and host
+    pool) on its own state: `steps` decode steps, the first `warmup` untimed,
+    with the workload's resize schedule (2,273 -> 921 -> 1,843 -> 1,843 slots)
+    applied before steps steps/4, steps/2 and 3*steps/4 (the pages' schedule
+    at 128 / 256 / 384 of 512 steps, scaled).  Per-phase HIP-event times over
+    the timed steps (control kernel, FFN; resize calls excluded), the FFN's
+    HBM rate, each resize's wall time, occupancy and bytes moved device to
+    device, and a checksum of the whole host pool before and after."""
+    import ctypes
+    from concurrent.futures import ThreadPoolExecutor
+
+    import numpy as np
+    import torch
+
+    import routed_expert_execution_moe_amd as B
+    import workload as W
+
+    wl = W.QWEN_ELASTIC
+    dev = torch.device("cuda:0")
+    points = sorted(wl.resize.items())
+    at = {steps * (i + 1) // 4: n for i, (_, n) in enumerate(points)}
+    cfg = B.config(wl.L, wl.E, wl.k, wl.H, wl.I, wl.w_dtype, wl.act_dtype, wl.n_slots,
+                   max_slots=max([wl.n_slots] + list(wl.resize.values())), max_tokens=wl.T,
+                   bw_pcie_mbps=wl.bw_pcie_mbps, bw_host_mbps=wl.bw_host_mbps, timing=1)
+    stride = B.moe_expert_bytes(cfg)
+    pool_bytes = wl.n_ids * stride
+    pool = B.moe_host_pool_alloc(pool_bytes)
+    ctx = None
+    try:
+        W.fill_banks(wl, pool, 0, wl.n_ids)
+        pool_np = np.ctypeslib.as_array((ctypes.c_uint8 * pool_bytes).from_address(pool))
+
+        def checksum():
+            words = pool_np.view(np.uint64)
+            parts = np.array_split(np.arange(len(words)), 16)
+            with ThreadPoolExecutor(16) as ex:
+                sums = ex.map(lambda r: int(np.add.reduce(words[r[0]:r[-1] + 1], dtype=np.uint64)), parts)
+            return sum(sums) & (2 ** 64 - 1)
+
+        logits = W.decode_logits(wl, steps=steps)
+        lg_d = torch.from_numpy(np.ascontiguousarray(logits)).to(dev)
+        xs = np.stack([np.stack([W.hidden(wl, s, l) for l in range(wl.L)]) for s in range(steps)])
+        x_d = torch.from_numpy(xs.view(np.int16)).to(dev).view(torch.bfloat16)
+        ids = torch.empty((wl.L, wl.T, wl.k), dtype=torch.int32, device=dev)
+        w = torch.empty((wl.L, wl.T, wl.k), dtype=torch.float32, device=dev)
+        y = torch.empty((wl.L, wl.T, wl.H), dtype=torch.bfloat16, device=dev)
+        ck0 = checksum()
+        ctx = B.moe_create(cfg, pool, pool_bytes)
+        hiplib = ctypes.CDLL("libamdhip64.so.7")
+        hiplib.hipMemcpy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int]
+
+        def slot_table():
+            v = B.moe_plan_view_get(ctx)
+            out = np.empty(v.n_slots, np.int32)
+            assert hiplib.hipMemcpy(out.ctypes.data, v.slot2id, out.nbytes, 2) == 0
+            return out
+
+        resizes, wall, timed_layers = [], 0.0, 0
+        tm_sum = None
+        st_a = st_b = None
+        for s in range(steps):
+            if s in at:
+                tm_part = B.moe_ctx_timing(ctx, reset=True)  # harvest before the resize
+                if s > warmup:
+                    tm_sum = tm_part if tm_sum is None else {
+                        k: dict(calls=tm_sum[k]["calls"] + v["calls"], ms=tm_sum[k]["ms"] + v["ms"])
+                        for k, v in tm_part.items()}
+                before = slot_table()
+                t0 = time.perf_counter()
+                B.moe_cache_resize(ctx, at[s], 60_000)
+                ms = (time.perf_counter() - t0) * 1e3
+                after = slot_table()
+                where = {int(u): i for i, u in enumerate(before) if u >= 0}
+                moved = sum(1 for i, u in enumerate(after) if u >= 0 and where[int(u)] != i)
+                resizes.append({"before_step": s, "to_slots": at[s], "ms": round(ms, 3),
+                                "occupied_before": len(where), "kept": int((after >= 0).sum()),
+                                "moved_slots": moved, "moved_bytes_d2d": moved * stride})
+            if s == warmup:
+                torch.cuda.synchronize()
+                B.moe_ctx_timing(ctx, reset=True)
+                st_a = B.moe_ctx_stats(ctx)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for l in range(wl.L):
+                B.moe_route_topk(ctx, lg_d[s, l], wl.T, ids[l], w[l])
+                B.moe_cache_plan(ctx, l, ids[l], wl.T, x_d[s, l])
+                B.moe_expert_ffn(ctx, l, x_d[s, l], wl.T)
+                B.moe_merge(ctx, w[l], wl.T, y[l])
+            torch.cuda.synchronize()
+            if s >= warmup:
+                wall += time.perf_counter() - t0
+                timed_layers += wl.L
+        st_b = B.moe_ctx_stats(ctx)
+        tm_part = B.moe_ctx_timing(ctx)
+        tm = tm_part if tm_sum is None else {
+            k: dict(calls=tm_sum[k]["calls"] + v["calls"], ms=tm_sum[k]["ms"] + v["ms"])
+            for k, v in tm_part.items()}
+        # FFN bytes: the unique GPU-resident experts' weights plus the
+        # activations (the fp32 partial rows, at most T*k*H*4 = 64 KB a call,
+        # are left out: well under 0.1% of the ~250 MB of weights)
+        gpu_experts = (st_b.hits - st_a.hits) + (st_b.fills - st_a.fills)
+        ffn_bytes = gpu_experts * W.expert_bytes(wl) + timed_layers * wl.T * wl.H * 2
+        per = {k: (round(v["ms"] * 1e3 / v["calls"], 2) if v["calls"] else None) for k, v in tm.items()}
+        ffn_gbps = ffn_bytes / (tm["ffn"]["ms"] * 1e-3) / 1e9 if tm["ffn"]["ms"] else None
+        acc = (st_b.hits - st_a.hits) + (st_b.fills - st_a.fills) + (st_b.cpu - st_a.cpu)
+        return {
+            "workload": wl.name, "tokens_per_call": wl.T, "steps": steps, "warmup": warmup,
+            "resize_before_steps": sorted(at),
+            "us_per_layer": round(wall / max(timed_layers, 1) * 1e6, 2),
+            "control_kernel_us": per.get("plan"), "ffn_us": per.get("ffn"), "fill_us": per.get("fill"),
+            "merge_us": per.get("merge"), "route_us": per.get("route"),
+            "ffn_expert_bytes_per_layer": round(gpu_experts * W.expert_bytes(wl) / max(timed_layers, 1)),
+            "ffn_gbps": round(ffn_gbps, 1) if ffn_gbps else None,
+            "ffn_frac_of_hbm": round(ffn_gbps / HBM_PEAK_GBPS, 4) if ffn_gbps else None,
+            "miss_rate": round(1 - (st_b.hits - st_a.hits) / max(acc, 1), 4),
+            "fills_per_layer": round((st_b.fills - st_a.fills) / max(timed_layers, 1), 3),
+            "cpu_experts_per_layer": round((st_b.cpu - st_a.cpu) / max(timed_layers, 1), 3),
+            "resizes": resizes, "host_pool_unchanged": checksum() == ck0,
         }
     finally:
         if ctx:
@@ -313,7 +490,8 @@ def cpu_baseline(wl, pool_np, stride, logits, xs, steps_range, budget_s):
         from threadpoolctl import threadpool_info
         blas_threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
     except Exception:  # noqa: BLE001
-        blas_threads = 1
+        blas_threads = None
+    cores = len(os.sched_getaffinity(0))
     st = OP.Residency(wl.n_ids, wl.n_slots)
     K = OP.victim_bound(wl.T, wl.k, wl.E, wl.n_slots)
 
@@ -334,8 +512,8 @@ def cpu_baseline(wl, pool_np, stride, logits, xs, steps_range, budget_s):
         if time.perf_counter() - t0 > budget_s:
             break
     dt = time.perf_counter() - t0
-    return dict(value=round(dt / calls * 1e6, 1), unit="us/layer", cores=blas_threads,
-                kind="oracle",
+    return dict(value=round(dt / calls * 1e6, 1), unit="us/layer", cores=cores,
+                blas_threads=blas_threads, kind="oracle",
                 sample=f"first {calls} layer calls of the timed steps (route, plan, fp64 expert "
                        f"FFN and merge from the pinned host banks; plan state starts cold)")
 
@@ -368,6 +546,9 @@ def main():
         return
     if a.copy_calibration:
         print(json.dumps(copy_calibration()), flush=True)
+        return
+    if a.streams_only:
+        print(json.dumps(bench_streams()), flush=True)
         return
     wl = {w.name: w for w in W.WORKLOADS}[a.workload]
     assert not wl.prefill, "decode workloads only"
@@ -604,6 +785,8 @@ def main():
             "unit": "GB/s",
             "frac": round(ffn_gbps / HBM_PEAK_GBPS, 4) if ffn_gbps else None,
             "traffic": recorded_traffic("decode_ffn", wl.name),
+            "traffic_source": traffic_source("decode_ffn", wl.name),
+            "algorithmic_bytes_per_launch": round(ffn_bytes / calls),
         },
         "cpu_baseline": cpu,
         "breakdown_us_per_call": per,
@@ -623,6 +806,8 @@ def main():
     }
     pool_np = None
     B.moe_host_pool_free(pool)
+    if not a.no_streams:
+        out["streams_8"] = bench_streams()
     if not a.no_prefill:
         out.update(bench_prefill())
     print(json.dumps(out), flush=True)

@@ -144,10 +144,12 @@ moe_status moe_route_topk(moe_ctx* ctx, const float* logits, int32_t T, int32_t*
  * hits' recency, surfaces the K = min(max_tokens*k, E, n_slots[, max_fetch])
  * least-recently-used slots by (tick, slot) excluding current hits, admits the
  * first q misses into the first q of them and writes slot_map[t][j] (slot id,
- * or -1 = run on the host).  One LRU tick per call.  The kernel itself hands
- * the remaining misses to the host branch (a doorbell in pinned memory that a
- * host thread answers); the call then enqueues the PCIe fill of the q
- * admitted experts into their slots (on `stream`).
+ * or -1 = run on the host).  One LRU tick per call.  The call then enqueues
+ * the PCIe fill of the q admitted experts into their slots (on `stream`);
+ * one more workgroup of that launch hands the remaining misses to the host
+ * branch (ids, slot map and activations into pinned memory, then a doorbell
+ * that a host thread answers), so the control kernel itself writes no host
+ * memory.
  * ids (device) int32 [T][k]; x (device) [T][H] act dtype, read by the host
  * branch.  1 <= T <= max_tokens. */
 moe_status moe_cache_plan(moe_ctx* ctx, int32_t layer, const int32_t* ids, int32_t T,
@@ -222,9 +224,15 @@ moe_status moe_cache_resize(moe_ctx* ctx, int32_t new_n_slots, int32_t timeout_m
  * evicted, a pass expert resident elsewhere emptied there), and runs the
  * grouped GEMM over each pass's experts on `stream`; nothing is prefetched.
  * Cache hits do not cross the bus [satyajit, "Four backends, and the one that has to
- * be measured", the prefill hit-D2D option]: in
- * the first pass an expert already in its target slot is not copied and one
- * resident at or beyond slot P is copied device to device.
+ * be measured", the prefill hit-D2D option]: when a layer's slab goes into
+ * its full-layer buffer, each of its experts resident in a slot outside the
+ * buffers is copied device to device and only the others cross PCIe (runs of
+ * consecutive experts, one copy each); for this the first two-buffer call
+ * after any decode call, resize or on-demand pass reads the residency table
+ * once (one synchronisation of `stream`).  On demand, in the first pass an
+ * expert already in its target slot is not copied and one resident at or
+ * beyond slot P is copied device to device.  Only the bytes' source changes;
+ * the tables are the same.  moe_ctx_stats counts the experts by source.
  * MOE_ENOSPC if n_slots == 0. */
 moe_status moe_prefill_layer(moe_ctx* ctx, int32_t layer, const void* x, int32_t T,
                              const int32_t* ids, const float* w, void* y, moe_stream stream);
@@ -331,6 +339,10 @@ typedef struct {
   int32_t n_slots, occupied;
   int64_t plans, hits, fills, cpu, evictions;
   int64_t prefill_layers, resizes;
+  /* prefill experts brought into full-layer buffers or on-demand pass slots:
+     over PCIe from the host pool, and device to device from a slot that
+     already held them (the cache hits that cross no bus) */
+  int64_t prefill_h2d_experts, prefill_d2d_experts;
 } moe_stats;
 
 moe_status moe_ctx_stats(moe_ctx* ctx, moe_stats* out);

@@ -63,7 +63,8 @@ class Stats(ctypes.Structure):
     _fields_ = [("n_slots", ctypes.c_int32), ("occupied", ctypes.c_int32),
                 ("plans", ctypes.c_int64), ("hits", ctypes.c_int64), ("fills", ctypes.c_int64),
                 ("cpu", ctypes.c_int64), ("evictions", ctypes.c_int64),
-                ("prefill_layers", ctypes.c_int64), ("resizes", ctypes.c_int64)]
+                ("prefill_layers", ctypes.c_int64), ("resizes", ctypes.c_int64),
+                ("prefill_h2d_experts", ctypes.c_int64), ("prefill_d2d_experts", ctypes.c_int64)]
 
 
 PHASES = ("route", "plan", "fill", "ffn", "merge", "host", "prefill_copy", "prefill_group",

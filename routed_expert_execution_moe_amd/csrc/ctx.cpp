@@ -328,6 +328,7 @@ extern "C" moe_status moe_create(const moe_config* cfg, void* host_pool, size_t 
     size_t o_cpu = take(4 * ctx->umax), o_gu = take(4 * ctx->umax), o_gs = take(4 * ctx->umax);
     size_t o_sm = take(4 * maxTk);
     size_t o_fd = take(4 * (size_t)kFfnDoneStride * kFfnSub * ctx->umax);
+    size_t o_hw = take(4);
     ALLOC(ctx->plan_alloc, off);
     uint8_t* b = ctx->plan_alloc;
     PlanBufs& p = ctx->plan;
@@ -344,6 +345,7 @@ extern "C" moe_status moe_create(const moe_config* cfg, void* host_pool, size_t 
     p.gpu_slot = (int32_t*)(b + o_gs);
     p.slot_map = (int32_t*)(b + o_sm);
     p.ffn_done = (int32_t*)(b + o_fd);
+    p.host_work = (int32_t*)(b + o_hw);
     p.hblock_bytes = sizeof(HostBlockHeader) + 2 * 4 * (size_t)maxTk;
     p.x_offset = (p.hblock_bytes + 255) / 256 * 256;
     p.act_bytes = dtype_bytes(cfg->act_dtype);
@@ -420,6 +422,8 @@ extern "C" moe_status moe_create(const moe_config* cfg, void* host_pool, size_t 
     if (e == hipSuccess) e = hipEventCreateWithFlags(&pf.ev_start, hipEventDisableTiming);
     if (e == hipSuccess)
       e = hipHostMalloc((void**)&pf.counts_host, 8 * (size_t)cfg->n_experts, hipHostMallocDefault);
+    if (e == hipSuccess)
+      e = hipHostMalloc((void**)&pf.snap, 4 * (size_t)n_ids, hipHostMallocDefault);
     if (e != hipSuccess) return bail(hip_fail(ctx, e, "prefill events and staging"));
     e = prefill_scratch_init(ctx->device);
     if (e != hipSuccess) return bail(hip_fail(ctx, e, "hipGetSymbolAddress of the prefill scratch"));
@@ -447,6 +451,7 @@ static void free_all(moe_ctx* ctx) {
   auto& pf = ctx->pf;
   F(pf.own_block);
   if (pf.counts_host) (void)hipHostFree(pf.counts_host);
+  if (pf.snap) (void)hipHostFree(pf.snap);
   for (int b = 0; b < 2; ++b)
     if (pf.ev_copied[b]) (void)hipEventDestroy(pf.ev_copied[b]);
   if (pf.ev_start) (void)hipEventDestroy(pf.ev_start);
@@ -586,17 +591,18 @@ extern "C" moe_status moe_cache_plan(moe_ctx* ctx, int32_t layer, const int32_t*
   hipStream_t s = (hipStream_t)stream;
   moe_status pst = prefill_settle(ctx, s);
   if (pst != MOE_OK) return pst;
-  // The control kernel hands the host branch its work first (doorbell in
-  // pinned memory, answered by the poller thread); the GPU miss path follows.
+  ctx->pf.snap_valid = false;  // fills may overwrite any slot outside the call's hits
+  // The control kernel decides; the next launch hands the host branch its
+  // work (doorbell in pinned memory, answered by the poller thread) while it
+  // fills the admitted experts.
   MOE_HIP(ctx, timing_begin(ctx, MOE_T_PLAN, s));
   MOE_HIP(ctx, launch_plan(ctx, layer, ids, T, x, s));
   MOE_HIP(ctx, timing_end(ctx, s));
-  // GPU miss path: batched copy of the admitted experts into their slots
-  if (ctx->n_slots > 0 && ctx->cfg.mode != MOE_CPU) {
-    MOE_HIP(ctx, timing_begin(ctx, MOE_T_FILL, s));
-    MOE_HIP(ctx, launch_fill(ctx, s));
-    MOE_HIP(ctx, timing_end(ctx, s));
-  }
+  // GPU miss path: batched copy of the admitted experts into their slots;
+  // one more workgroup of the same launch hands the CPU set to the host branch
+  MOE_HIP(ctx, timing_begin(ctx, MOE_T_FILL, s));
+  MOE_HIP(ctx, launch_fill(ctx, layer, ids, T, x, s));
+  MOE_HIP(ctx, timing_end(ctx, s));
   ctx->state = kPlanned;
   ctx->cur_layer = layer;
   ctx->cur_T = T;
@@ -675,7 +681,9 @@ extern "C" moe_status moe_ctx_stats(moe_ctx* ctx, moe_stats* out) {
   for (int s = 0; s < ctx->n_slots; ++s) out->occupied += s2i[s] >= 0;
   out->plans = ds.plans; out->hits = ds.hits; out->fills = ds.fills; out->cpu = ds.cpu;
   out->evictions = ds.evictions; out->prefill_layers = ds.prefill_layers;
-  out->resizes = 0;
+  out->resizes = ctx->n_resizes;
+  out->prefill_h2d_experts = ctx->pf.h2d_experts;
+  out->prefill_d2d_experts = ctx->pf.d2d_experts;
   return MOE_OK;
 }
 
@@ -783,6 +791,8 @@ extern "C" moe_status moe_cache_resize(moe_ctx* ctx, int32_t new_n, int32_t time
   MOE_HIP(ctx, hipStreamSynchronize(ctx->copy));
   if ((st = pool_unmap_to(ctx, (size_t)new_n * ctx->stride)) != MOE_OK) return st;
   ctx->n_slots = new_n;
+  ctx->pf.snap_valid = false;
+  ctx->n_resizes += 1;
   return MOE_OK;
 }
 
@@ -913,15 +923,39 @@ static moe_status prefill_setup(moe_ctx* ctx) {
 // Issue the slab copy of `layer` into its buffer on the copy stream.
 // It waits for everything enqueued on the caller's stream before this call
 // (ev_start): earlier readers of that buffer, decode work on those slots.
+// Experts of the layer resident in a slot outside the full-layer buffers (by
+// the residency snapshot) come device to device; the others cross PCIe from
+// the host pool, one copy per run of consecutive experts (satyajit, "Four
+// backends, and the one that has to be measured": cache hits cross no bus).
+// A source slot outside the buffers is written only by decode fills and
+// resizes, and both invalidate the snapshot and wait for this copy first.
 static moe_status prefill_issue(moe_ctx* ctx, int32_t layer) {
   auto& pf = ctx->pf;
   const int b = prefill_buffer(ctx, layer);
   const int E = ctx->cfg.n_experts;
+  const int outside = pf.buffers * E;  // first slot outside the buffers
+  const size_t st = ctx->stride;
+  uint8_t* dst = ctx->pool.base + (size_t)b * E * st;
+  const int32_t* res = pf.snap_valid ? pf.snap + (size_t)layer * E : nullptr;
+  auto resident = [&](int e) { return res && res[e] >= outside ? res[e] : -1; };
   MOE_HIP(ctx, hipStreamWaitEvent(ctx->copy, pf.ev_start, 0));
   MOE_HIP(ctx, timing_begin(ctx, MOE_T_PREFILL_COPY, ctx->copy));
-  MOE_HIP(ctx, hipMemcpyAsync(ctx->pool.base + (size_t)b * E * ctx->stride,
-                              ctx->host_pool + (size_t)layer * E * ctx->stride, (size_t)E * ctx->stride,
-                              hipMemcpyHostToDevice, ctx->copy));
+  for (int e = 0; e < E;) {
+    const int from = resident(e);
+    if (from >= 0) {
+      MOE_HIP(ctx, hipMemcpyAsync(dst + (size_t)e * st, ctx->pool.base + (size_t)from * st, st,
+                                  hipMemcpyDeviceToDevice, ctx->copy));
+      pf.d2d_experts += 1;
+      ++e;
+      continue;
+    }
+    int j = e + 1;
+    while (j < E && resident(j) < 0) ++j;
+    MOE_HIP(ctx, hipMemcpyAsync(dst + (size_t)e * st, ctx->host_pool + ((size_t)layer * E + e) * st,
+                                (size_t)(j - e) * st, hipMemcpyHostToDevice, ctx->copy));
+    pf.h2d_experts += j - e;
+    e = j;
+  }
   MOE_HIP(ctx, timing_end(ctx, ctx->copy));
   MOE_HIP(ctx, hipEventRecord(pf.ev_copied[b], ctx->copy));
   pf.buf_layer[b] = layer;
@@ -965,6 +999,7 @@ static moe_status prefill_on_demand(moe_ctx* ctx, const PrefillBufs& pb, int32_t
   const int E = ctx->cfg.n_experts;
   moe_status st = prefill_settle(ctx, s);
   if (st != MOE_OK) return st;
+  pf.snap_valid = false;  // the passes rewrite slots [0, P)
   MOE_HIP(ctx, launch_prefill_group(ctx, pb, ids, T, s));
   int32_t* counts = pf.counts_host;
   int32_t* resident = pf.counts_host + E;
@@ -992,6 +1027,7 @@ static moe_status prefill_on_demand(moe_ctx* ctx, const PrefillBufs& pb, int32_t
         MOE_HIP(ctx, hipMemcpyAsync(ctx->pool.base + (size_t)i * ctx->stride,
                                     ctx->pool.base + (size_t)from * ctx->stride, ctx->stride,
                                     hipMemcpyDeviceToDevice, s));
+        pf.d2d_experts += 1;
         ++i;
         continue;
       }
@@ -1002,6 +1038,7 @@ static moe_status prefill_on_demand(moe_ctx* ctx, const PrefillBufs& pb, int32_t
       MOE_HIP(ctx, hipMemcpyAsync(ctx->pool.base + (size_t)i * ctx->stride,
                                   ctx->host_pool + ((size_t)layer * E + e) * ctx->stride,
                                   (size_t)(j - i) * ctx->stride, hipMemcpyHostToDevice, s));
+      pf.h2d_experts += j - i;
       i = j;
     }
     MOE_HIP(ctx, timing_end(ctx, s));
@@ -1056,6 +1093,12 @@ static moe_status prefill_layer_run(moe_ctx* ctx, const PrefillBufs& pb, int32_t
   if (ctx->n_slots < pf.buffers * c.n_experts) return prefill_on_demand(ctx, pb, layer, x, T, ids, w, y, s);
   moe_status st = MOE_OK;
   const int b = prefill_buffer(ctx, layer);
+  if (!pf.snap_valid) {
+    // the residency table as this call finds it, for the hit-D2D slab copies
+    MOE_HIP(ctx, hipMemcpyAsync(pf.snap, ctx->id2slot, 4 * (size_t)ctx->n_ids, hipMemcpyDeviceToHost, s));
+    MOE_HIP(ctx, hipStreamSynchronize(s));
+    pf.snap_valid = true;
+  }
   MOE_HIP(ctx, hipEventRecord(pf.ev_start, s));
   if (pf.buf_layer[b] != layer && (st = prefill_issue(ctx, layer)) != MOE_OK) return st;
   // with two buffers, stream the next layer into the other one while this
@@ -1069,6 +1112,8 @@ static moe_status prefill_layer_run(moe_ctx* ctx, const PrefillBufs& pb, int32_t
   // the experts are used again, so their recency is refreshed
   MOE_HIP(ctx, launch_prefill_admit(ctx, layer, b, s));
   pf.admitted[b] = true;
+  // the admission empties this layer's other slots: no longer copy sources
+  for (int e = 0; e < c.n_experts; ++e) pf.snap[(size_t)layer * c.n_experts + e] = -1;
   MOE_HIP(ctx, launch_prefill_compute(ctx, pb, layer, x, T, ids, w, y, s));
   return MOE_OK;
 }

@@ -1,5 +1,6 @@
-// Decode data path: PCIe fill of admitted experts, dispatch of the expert
-// FFN (ffn.h) and the fixed-order merge.
+// Decode data path: PCIe fill of admitted experts (with the hand-off of the
+// CPU set to the host branch), dispatch of the expert FFN (ffn.h) and the
+// fixed-order merge.
 //
 // Fill (snackonai, "The split policy itself", execution order: cache update,
 // then the batched copy, then grouped evaluation): the host never learns
@@ -16,16 +17,70 @@ namespace moert {
 // ------------------------------------------------------------------ fill
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+// The hand-off of a call's CPU set to the host branch (snackonai, "The split
+// policy itself": the CPU branch runs the misses left to it): the host block
+// in pinned, device-mapped memory gets the routed ids, the slot map and the
+// activations, then the header and, last, the doorbell (the call's sequence
+// number, the device plan count).  One workgroup of the fill launch does it,
+// only when the control kernel flagged host work.
+struct Handoff {
+  uint8_t* hblock;                 // device address of the host block; nullptr: no hand-off
+  const int32_t* host_work;        // control kernel's flag
+  const int32_t* ids;              // [T*k] routed ids
+  const int32_t* slot_map;         // [T*k] slot or -1
+  const moe_plan_counts* counts;
+  const DevState* st;
+  const uint8_t* x;                // [T][H] activations
+  int64_t x_units;                 // 16-byte units of x
+  size_t x_offset;                 // byte offset of the activations in the block
+  int32_t Tk, T, layer;
+};
+
+__device__ void host_handoff(const Handoff& h) {
+  if (*h.host_work == 0) return;  // uniform
+  const int tid = threadIdx.x;
+  HostBlockHeader* hb = (HostBlockHeader*)h.hblock;
+  int32_t* hb_ids = (int32_t*)(h.hblock + sizeof(HostBlockHeader));
+  int32_t* hb_map = hb_ids + h.Tk;
+  for (int i = tid; i < h.Tk; i += blockDim.x) {
+    hb_ids[i] = h.ids[i];
+    hb_map[i] = h.slot_map[i];
+  }
+  const uint4* xs = (const uint4*)h.x;
+  uint4* xd = (uint4*)(h.hblock + h.x_offset);
+  for (int64_t i = tid; i < h.x_units; i += blockDim.x) xd[i] = xs[i];
+  // every thread's block writes complete at system scope before the barrier,
+  // then one thread writes the header and rings
+  __threadfence_system();
+  __syncthreads();
+  if (tid == 0) {
+    hb->c = *h.counts;
+    hb->layer = h.layer;
+    hb->T = h.T;
+    const int64_t seq = h.st->plans;
+    __threadfence_system();
+    __hip_atomic_store(&hb->seq, seq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    __threadfence_system();
+  }
+}
+
 __global__ __launch_bounds__(256) void fill_kernel(const uint8_t* __restrict__ host_dev,
                                                    uint8_t* __restrict__ slots, size_t stride,
                                                    const moe_plan_counts* __restrict__ counts,
                                                    const int32_t* __restrict__ fill_u,
-                                                   const int32_t* __restrict__ fill_slot) {
+                                                   const int32_t* __restrict__ fill_slot, Handoff h) {
+  // the last workgroup (when the launch carries a hand-off) serves the host
+  // branch; the others pull the admitted experts
+  const int nblk = (int)gridDim.x - (h.hblock ? 1 : 0);
+  if ((int)blockIdx.x >= nblk) {
+    host_handoff(h);
+    return;
+  }
   const int q = counts->q;
   if (q == 0) return;
   const size_t units = stride / 16;  // 16-byte units per expert
   const size_t total = (size_t)q * units;
-  const size_t nthreads = (size_t)gridDim.x * blockDim.x;
+  const size_t nthreads = (size_t)nblk * blockDim.x;
   // 16 loads of 16 bytes in flight per lane over 64 workgroups (4 MB in
   // flight): 54-55 GB/s from pinned host memory, a few % above wider grids
   constexpr int U = 16;
@@ -53,18 +108,36 @@ __global__ __launch_bounds__(256) void fill_kernel(const uint8_t* __restrict__ h
   }
 }
 
+constexpr int kFillBlocks = 64;
+
 hipError_t launch_fill_lists(const uint8_t* host_dev, uint8_t* dst, size_t stride,
                              const moe_plan_counts* counts, const int32_t* fill_u,
                              const int32_t* fill_slot, hipStream_t s) {
-  hipLaunchKernelGGL(fill_kernel, dim3(64), dim3(256), 0, s, host_dev, dst, stride, counts, fill_u,
-                     fill_slot);
+  Handoff none{};
+  hipLaunchKernelGGL(fill_kernel, dim3(kFillBlocks), dim3(256), 0, s, host_dev, dst, stride, counts,
+                     fill_u, fill_slot, none);
   return hipGetLastError();
 }
 
-hipError_t launch_fill(moe_ctx* ctx, hipStream_t s) {
-  if (ctx->n_slots == 0 || ctx->cfg.mode == MOE_CPU) return hipSuccess;
-  return launch_fill_lists(ctx->host_pool_dev, ctx->pool.base, ctx->stride, ctx->plan.counts,
-                           ctx->plan.fill_u, ctx->plan.fill_slot, s);
+hipError_t launch_fill(moe_ctx* ctx, int layer, const int32_t* ids, int T, const void* x, hipStream_t s) {
+  const PlanBufs& pb = ctx->plan;
+  Handoff h;
+  h.hblock = pb.hblock;
+  h.host_work = pb.host_work;
+  h.ids = ids;
+  h.slot_map = pb.slot_map;
+  h.counts = pb.counts;
+  h.st = ctx->dstate;
+  h.x = (const uint8_t*)x;
+  h.x_units = (int64_t)T * ctx->cfg.hidden * pb.act_bytes / 16;
+  h.x_offset = pb.x_offset;
+  h.Tk = T * ctx->cfg.top_k;
+  h.T = T;
+  h.layer = layer;
+  // no slots or CPU mode: q = 0, the fill workgroups exit at once
+  hipLaunchKernelGGL(fill_kernel, dim3(kFillBlocks + 1), dim3(256), 0, s, ctx->host_pool_dev, ctx->pool.base,
+                     ctx->stride, pb.counts, pb.fill_u, pb.fill_slot, h);
+  return hipGetLastError();
 }
 
 // ------------------------------------------------------------------ expert FFN

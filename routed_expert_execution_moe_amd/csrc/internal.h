@@ -34,9 +34,10 @@ struct DevState {
   int32_t pad;
 };
 
-// Everything the host branch needs from one plan, in pinned host memory the
-// control kernel writes directly.  `seq` is the doorbell: the kernel writes
-// it last (after a system-scope fence), and only when the call has host work.
+// Everything the host branch needs from one plan, in pinned host memory that
+// the fill kernel's hand-off workgroup writes directly after the control
+// kernel.  `seq` is the doorbell: it is written last (after a system-scope
+// fence), and only when the call has host work.
 struct HostBlockHeader {
   int64_t seq;
   moe_plan_counts c;
@@ -58,7 +59,9 @@ struct PlanBufs {
   int32_t *uniq, *hits, *misses, *victims, *fill_u, *fill_slot, *fill_old;
   int32_t *cpu_u, *gpu_u, *gpu_slot, *slot_map;
   int32_t* ffn_done;      // [umax * kFfnSub * kFfnDoneStride] gate/up items finished
-  // host block in pinned, device-mapped memory, written by the control kernel:
+  int32_t* host_work;     // [1] set by the control kernel: the host branch has work
+  // host block in pinned, device-mapped memory, written by the fill kernel's
+  // hand-off workgroup:
   // header | ids[maxTk] | slot_map[maxTk] | x[max_tokens][H] (act dtype)
   uint8_t* hblock;        // device address of the mapping
   size_t hblock_bytes;    // header + ids + slot map
@@ -193,7 +196,14 @@ struct moe_ctx {
     moert::PrefillBufs own;
     const moert::PrefillBufs* last = nullptr;  // the set the last prefill call used
     moert::PrefillBufs scratch;            // moe_prefill_layer_noalloc's, in the device scratch
+    // residency snapshot for the hit-D2D slab copies: id2slot as of the
+    // first two-buffer call since the last decode call, resize or on-demand
+    // pass (pinned [L*E]); entries of a layer admitted since are cleared
+    int32_t* snap = nullptr;
+    bool snap_valid = false;
+    int64_t h2d_experts = 0, d2d_experts = 0;
   } pf;
+  int64_t n_resizes = 0;
 
   moert::Timing* timing = nullptr;
 
@@ -221,7 +231,9 @@ hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* 
                              hipStream_t s);
 hipError_t launch_plan(moe_ctx* ctx, int layer, const int32_t* ids, int T, const void* x,
                        hipStream_t s);
-hipError_t launch_fill(moe_ctx* ctx, hipStream_t s);
+// the fill of the last plan, plus its hand-off to the host branch (one more
+// workgroup: the host block and the doorbell, when the plan has host work)
+hipError_t launch_fill(moe_ctx* ctx, int layer, const int32_t* ids, int T, const void* x, hipStream_t s);
 // resize compaction: n_moves (from, to) slot pairs (device, int32 [n][2]),
 // no slot both read and written
 hipError_t launch_slot_moves(moe_ctx* ctx, const int32_t* moves, int n_moves, hipStream_t s);

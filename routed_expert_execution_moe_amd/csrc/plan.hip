@@ -14,7 +14,8 @@
 //              the K-th smallest tick over register-resident keys, then a
 //              rank sort of the K survivors;
 //   5. rewrite the first q misses take the first q victims; slot_map[t][j]
-//              gets the slot, or -1 for the host.
+//              gets the slot, or -1 for the host; a flag says whether the
+//              host branch has work (the fill kernel hands it over).
 // Recency is one tick per call; hits and fills take that tick.  The 64-bit
 // ticks enter the select as 32-bit keys relative to the call's tick
 // (lru_key.h), exact across 2^32.
@@ -28,8 +29,6 @@ constexpr uint32_t kSentinel = kLruNoCandidate;
 
 struct PlanArgs {
   const int32_t* ids;
-  const uint8_t* x;     // activations [T][H], act dtype
-  int64_t x_bytes;      // T * H * element bytes
   int32_t T, k, layer, E, K, n, mode, max_fetch;
   int32_t umax;         // plan list bound; the FFN counters to clear
   int64_t bwp, bwh;
@@ -77,7 +76,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   __shared__ uint64_t s_sel[kMaxExperts];
   __shared__ int32_t s_nuniq, s_nhit, s_m, s_q, s_keff, s_evict, s_ngpu, s_bad;
   __shared__ uint32_t s_prefix, s_pmask, s_kk;
-  __shared__ uint32_t s_kmin[kWaves], s_kmax[kWaves];
+  __shared__ int64_t s_tmin[kWaves], s_tmax[kWaves];
+  __shared__ bool s_wempty[kWaves];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int E = a.E, Tk = a.T * a.k, n = a.n;
@@ -94,19 +94,20 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     s_bad = 0;
   }
   // the slot table rows of this thread's slots, requested now so their
-  // latency overlaps the dedup and classification; each tick becomes its
-  // 32-bit recency key relative to this call's tick (an empty slot's is 0)
-  // (up to 8 slots per thread the occupants are held too; beyond, the
-  // registers go to the keys and a victim's occupant is read when selected)
-  constexpr bool kHoldOld = SPT <= 8;
+  // latency overlaps the dedup and classification (up to 8 slots per
+  // thread; beyond, the ticks are read when the victims are chosen and a
+  // victim's occupant when it is selected, to spare registers)
+  constexpr bool kHold = SPT <= 8;
   const int64_t now = a.st->tick + 1;
-  uint32_t key[SPT];
-  int32_t sid_r[kHoldOld ? SPT : 1];
+  int64_t tsr[SPT];
+  int32_t sid_r[kHold ? SPT : 1];
+  if constexpr (kHold) {
 #pragma unroll
-  for (int i = 0; i < SPT; ++i) {
-    const int s = tid * SPT + i;
-    key[i] = s < n ? lru_key(a.slot_ts[s], now) : kSentinel;
-    if constexpr (kHoldOld) sid_r[i] = s < n ? a.slot2id[s] : -1;
+    for (int i = 0; i < SPT; ++i) {
+      const int s = tid * SPT + i;
+      tsr[i] = s < n ? a.slot_ts[s] : -1;
+      sid_r[i] = s < n ? a.slot2id[s] : -1;
+    }
   }
   // the first routed id of this thread and the residency of expert tid of
   // this layer are requested here too, so neither costs a round trip after
@@ -177,41 +178,60 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
 
   // -------------------------------------------------------------- 4. victims
   if (keff > 0) {
-    // keys of this thread's contiguous slots (empty = 0), hits and slots
-    // past n excluded
+    // candidates: this thread's contiguous slots below n that hold no
+    // current hit.  The occupied candidates' tick range (64-bit) and whether
+    // any candidate is empty, over the block
     const int s0 = tid * SPT;
-    uint32_t kmin = kSentinel, kmax = 0;
+    if constexpr (!kHold) {
+      // only current hits' ticks changed since entry, and hits are no candidates
+#pragma unroll
+      for (int i = 0; i < SPT; ++i) tsr[i] = s0 + i < n ? a.slot_ts[s0 + i] : -1;
+    }
+    int64_t tmin = INT64_MAX, tmax = -1;
+    bool empty = false;
 #pragma unroll
     for (int i = 0; i < SPT; ++i) {
-      int s = s0 + i;
+      const int s = s0 + i;
       if (s < n && !((s_hitbits[s >> 5] >> (s & 31)) & 1u)) {
-        kmin = min(kmin, key[i]);
-        kmax = max(kmax, key[i]);
+        if (tsr[i] < 0) {
+          empty = true;
+        } else {
+          tmin = min(tmin, tsr[i]);
+          tmax = max(tmax, tsr[i]);
+        }
       } else {
-        key[i] = kSentinel;  // current hits and slots past n are not candidates
+        tsr[i] = INT64_MIN;  // not a candidate
       }
     }
-    // keys relative to the smallest candidate: the select then only needs
-    // the digits that the spread of ticks actually uses
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) {
-      kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, off));
-      kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, off));
+      tmin = min(tmin, (int64_t)__shfl_xor((long long)tmin, off));
+      tmax = max(tmax, (int64_t)__shfl_xor((long long)tmax, off));
     }
+    const bool w_empty = __ballot(empty) != 0;
     if (lane == 0) {
-      s_kmin[wave] = kmin;
-      s_kmax[wave] = kmax;
+      s_tmin[wave] = tmin;
+      s_tmax[wave] = tmax;
+      s_wempty[wave] = w_empty;
     }
     __syncthreads();
-    kmin = kSentinel;
-    kmax = 0;
+    tmin = INT64_MAX;
+    tmax = -1;
+    empty = false;
     for (int w = 0; w < kWaves; ++w) {
-      kmin = min(kmin, s_kmin[w]);
-      kmax = max(kmax, s_kmax[w]);
+      tmin = min(tmin, s_tmin[w]);
+      tmax = max(tmax, s_tmax[w]);
+      empty |= s_wempty[w];
     }
+    // 32-bit keys relative to the oldest occupied candidate (lru_key.h),
+    // shifted so the smallest candidate key is 0: the select then only needs
+    // the digits that the candidates' age range actually uses
+    const uint32_t kmin = empty ? 0u : 1u;
+    const uint32_t kmax = tmax >= 0 ? lru_key(tmax, tmin) : 0u;
+    uint32_t key[SPT];
 #pragma unroll
     for (int i = 0; i < SPT; ++i)
-      if (key[i] != kSentinel) key[i] -= kmin;
+      key[i] = tsr[i] == INT64_MIN ? kSentinel : lru_key(tsr[i], tmin) - kmin;
     const uint32_t spread = kmax >= kmin ? kmax - kmin : 0;
     const int bits = spread ? 32 - __builtin_clz(spread) : 0;
     const int first_pass = bits > 21 ? 0 : bits > 10 ? 1 : 2;
@@ -311,11 +331,11 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
       const uint32_t kv = key[i];
       const uint64_t packed = ((uint64_t)kv << 32) | (uint32_t)(s0 + i);
       if (kv < tau) {
-        s_selold[pl] = kHoldOld ? sid_r[kHoldOld ? i : 0] : a.slot2id[s0 + i];
+        s_selold[pl] = kHold ? sid_r[kHold ? i : 0] : a.slot2id[s0 + i];
         s_sel[pl++] = packed;
       } else if (kv == tau && kv != kSentinel) {
         if (pe < r) {
-          s_selold[tl + pe] = kHoldOld ? sid_r[kHoldOld ? i : 0] : a.slot2id[s0 + i];
+          s_selold[tl + pe] = kHold ? sid_r[kHold ? i : 0] : a.slot2id[s0 + i];
           s_sel[tl + pe] = packed;
         }
         ++pe;
@@ -356,26 +376,13 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   for (int i = q + tid; i < mm; i += kPlanThreads) pb.cpu_u[i - q] = s_miss[i];
   __syncthreads();
 
-  // slot map (device and host block); GPU list in ascending u
-  // slot map; when the call has host work, the host block in pinned host
-  // memory gets ids, slot map and a copy of the activations
-  const int n_cpu = mm - q + (s_bad > 0);  // > 0: the host branch has work
-  HostBlockHeader* hb = (HostBlockHeader*)pb.hblock;
-  int32_t* hb_ids = (int32_t*)(pb.hblock + sizeof(HostBlockHeader));
-  int32_t* hb_map = hb_ids + Tk;
+  // slot map and GPU list (ascending u).  The host block (ids, slot map,
+  // activations) and the doorbell are written by the fill kernel's hand-off
+  // workgroup that follows on the stream, so this kernel makes no
+  // host-memory writes and no system-scope fences.
   for (int i = tid; i < Tk; i += kPlanThreads) {
     int ee = a.ids[i];
-    int sl = (ee >= 0 && ee < E) ? s_eslot[ee] : -1;
-    pb.slot_map[i] = sl;
-    if (n_cpu > 0) {
-      hb_ids[i] = ee;
-      hb_map[i] = sl;
-    }
-  }
-  if (n_cpu > 0) {
-    const uint4* xs = (const uint4*)a.x;
-    uint4* xd = (uint4*)(pb.hblock + pb.x_offset);
-    for (int64_t i = tid; i < a.x_bytes / 16; i += kPlanThreads) xd[i] = xs[i];
+    pb.slot_map[i] = (ee >= 0 && ee < E) ? s_eslot[ee] : -1;
   }
   const bool on_gpu = present && s_eslot[e] >= 0;
   const uint64_t b_gpu = __ballot(on_gpu);
@@ -388,13 +395,6 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     pb.gpu_u[p] = u;
     pb.gpu_slot[p] = s_eslot[e];
   }
-  // host block writes visible before the doorbell: every thread that wrote
-  // part of the block (ids and slot map: tid < Tk; x: tid < x_bytes / 16)
-  // releases at system scope before the barrier, after which thread 0 rings.
-  // Threads that wrote only device memory skip the fence: later kernels on
-  // this stream read those outputs, and the kernel boundary orders them.
-  if (n_cpu > 0 && (tid < Tk || tid < a.x_bytes / 16)) __threadfence_system();
-  __syncthreads();
   if (tid == 0) {
     moe_plan_counts c;
     c.n_uniq = s_nuniq;
@@ -406,18 +406,13 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     c.K = a.K;
     c.tick_lo = (int32_t)tick;
     *pb.counts = c;
+    // the host branch has work: misses left to the CPU, or ids outside
+    // [0, E) (their rows are zeros from the host branch)
+    *pb.host_work = (mm - q > 0 || s_bad > 0) ? 1 : 0;
     // the call's sequence number is the plan count after it: it lives on the
     // device, so a replayed graph of calls numbers its calls correctly
     DevState* st = a.st;
     const int64_t seq = st->plans + 1;
-    if (n_cpu > 0) {
-      hb->c = c;
-      hb->layer = a.layer;
-      hb->T = a.T;
-      __threadfence_system();
-      *(volatile int64_t*)&hb->seq = seq;  // ring the host branch
-      __threadfence_system();
-    }
     st->tick = tick;
     st->plans = seq;
     st->hits += s_nhit;
@@ -430,9 +425,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
 hipError_t launch_plan(moe_ctx* ctx, int layer, const int32_t* ids, int T, const void* x,
                        hipStream_t s) {
   PlanArgs a;
+  (void)x;
   a.ids = ids;
-  a.x = (const uint8_t*)x;
-  a.x_bytes = (int64_t)T * ctx->cfg.hidden * ctx->plan.act_bytes;
   a.T = T;
   a.k = ctx->cfg.top_k;
   a.layer = layer;

@@ -303,6 +303,80 @@ def test_prefill_then_resize_with_pending_slab():
         g.close()
 
 
+def test_prefill_two_buffers_cache_hits():
+    """Decode first, in a pool of 2E + 16 slots: experts of every layer end up
+    in slots outside the two full-layer buffers [0, 2E).  A two-buffer prefill
+    of every layer then copies those experts device to device into the
+    buffers and brings only the others over PCIe.  Tables follow the oracle's
+    buffer admission, every buffer slot holds its bank's bytes, every token is
+    within tolerance, the copy counts match the residency the chunk found, and
+    decode continues.  A second chunk right after finds no expert outside the
+    buffers (the first chunk's admissions emptied them): it copies from the
+    host, except the layer whose slab is still in its buffer."""
+    import torch
+    wl = dataclasses.replace(W.DSV4_PREFILL, L=3, E=16, k=4, H=512, I=512, T=333, n_slots=48)
+    log("two-buffer prefill after decode: L=3 E=16 k=4 H=512 I=512 T=333 n=48")
+    g = GpuRun(wl, n_slots=wl.n_slots, max_tokens=8, max_prefill_tokens=wl.T)
+    try:
+        o = OracleRun(wl, g.bank, n_slots=wl.n_slots, max_tokens=8)
+        dl = dataclasses.replace(wl, T=1, steps=16, prefill=False)
+        logits = W.decode_logits(dl)
+
+        def decode_steps(steps):
+            for s_ in steps:
+                for l in range(wl.L):
+                    xdec = W.hidden(dl, 300 + s_, l)
+                    ids_g, _ = g.decode_call(l, logits[s_, l], xdec)
+                    ids_o, w_o = o.route(logits[s_, l])
+                    assert np.array_equal(ids_g, ids_o)
+                    compare_plan(g.plan_view(1), o.plan(l, ids_o), 1)
+                    ref = o.output(l, x_f64(dl, xdec), ids_o, w_o)
+                    assert rel_err(g.y[:1].float().cpu().numpy().astype(np.float64), ref)[0] <= TOL
+
+        decode_steps(range(12))
+        i2s = g.tables()[0]
+        outside = {l: [e for e in range(wl.E) if i2s[l * wl.E + e] >= 2 * wl.E] for l in range(wl.L)}
+        n_out = sum(len(v) for v in outside.values())
+        log(f"  after decode: experts outside the buffers per layer {[len(outside[l]) for l in range(wl.L)]}")
+        assert n_out > 0, "the scenario must leave experts outside the full-layer buffers"
+        dev = g.dev
+        ids = torch.empty((wl.T, wl.k), dtype=torch.int32, device=dev)
+        w = torch.empty((wl.T, wl.k), dtype=torch.float32, device=dev)
+        y = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device=dev)
+        st0 = g.B.moe_ctx_stats(g.ctx)
+        for chunk in range(2):
+            for l in range(wl.L):
+                lg = W.prefill_logits(wl, l)
+                x = W.hidden(wl, chunk, l)
+                g.B.moe_route_topk(g.ctx, torch.from_numpy(lg).to(dev), wl.T, ids, w)
+                g.B.moe_prefill_layer(g.ctx, l, g.to_dev_x(x), wl.T, ids, w, y)
+                torch.cuda.synchronize()
+                ids_o, w_o = o.route(lg)
+                b = OP.prefill_admit(o.st, l, wl.E, 2)
+                i2s_g, s2i, ts, tick = g.tables()
+                assert i2s_g == o.st.id2slot and s2i == o.st.slot2id and ts == o.st.slot_ts, (chunk, l)
+                assert tick == o.st.tick
+                for e in range(wl.E):
+                    assert np.array_equal(g.slot_bytes(b * wl.E + e), g.bank(l * wl.E + e)), (chunk, l, e)
+                ref = OY.moe_layer(x_f64(wl, x), ids_o, w_o, l, wl.E, o.weights)
+                err, _ = rel_err(y.float().cpu().numpy().astype(np.float64), ref)
+                assert err <= TOL, (chunk, l, err)
+            st1 = g.B.moe_ctx_stats(g.ctx)
+            d2d = st1.prefill_d2d_experts - st0.prefill_d2d_experts
+            h2d = st1.prefill_h2d_experts - st0.prefill_h2d_experts
+            # chunk 0 copies every layer; chunk 1 finds layer 1 still in buffer 1
+            # (layer 2 went to buffer 0 last) and reuses it, copying layers 0 and 2
+            want_d2d = n_out if chunk == 0 else 0
+            want_total = wl.L * wl.E if chunk == 0 else (wl.L - 1) * wl.E
+            log(f"  chunk {chunk}: {d2d} experts device to device, {h2d} over PCIe")
+            assert d2d == want_d2d and h2d == want_total - want_d2d, (chunk, d2d, h2d)
+            st0 = st1
+        decode_steps(range(12, 16))
+        log("  decode after: plans bit-exact, outputs within tolerance")
+    finally:
+        g.close()
+
+
 def test_prefill_on_demand_cache_hits():
     """Decode first: two layers of 16 experts through 24 slots leave some of
     layer 1's experts in slots 16..23.  An on-demand prefill of layer 1 (one
@@ -347,12 +421,16 @@ def test_prefill_on_demand_cache_hits():
         w = torch.empty((wl.T, wl.k), dtype=torch.float32, device=dev)
         y = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device=dev)
         x = W.hidden(wl, 0, layer)
+        st0 = g.B.moe_ctx_stats(g.ctx)
         g.B.moe_route_topk(g.ctx, torch.from_numpy(lg).to(dev), wl.T, ids, w)
         g.B.moe_prefill_layer(g.ctx, layer, g.to_dev_x(x), wl.T, ids, w, y)
         torch.cuda.synchronize()
         assert np.array_equal(ids.cpu().numpy(), ids_o)
         passes = OP.prefill_on_demand(o.st, layer, ids_o.ravel(), wl.E)
         assert len(passes) == 1
+        st1 = g.B.moe_ctx_stats(g.ctx)
+        assert st1.prefill_d2d_experts - st0.prefill_d2d_experts == len(beyond)
+        assert st1.prefill_h2d_experts - st0.prefill_h2d_experts == P - len(beyond) - len(in_place)
         i2s, s2i, ts, tick = g.tables()
         assert i2s == o.st.id2slot and s2i == o.st.slot2id and ts == o.st.slot_ts and tick == o.st.tick
         for i, e in enumerate(passes[0]):
@@ -366,6 +444,9 @@ def test_prefill_on_demand_cache_hits():
         y.zero_()
         g.B.moe_prefill_layer(g.ctx, layer, g.to_dev_x(x), wl.T, ids, w, y)
         torch.cuda.synchronize()
+        st2 = g.B.moe_ctx_stats(g.ctx)
+        assert (st2.prefill_d2d_experts, st2.prefill_h2d_experts) == (st1.prefill_d2d_experts,
+                                                                     st1.prefill_h2d_experts)
         assert OP.prefill_on_demand(o.st, layer, ids_o.ravel(), wl.E) == passes
         i2s, s2i, ts, tick = g.tables()
         assert i2s == o.st.id2slot and s2i == o.st.slot2id and ts == o.st.slot_ts and tick == o.st.tick

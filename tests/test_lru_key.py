@@ -12,7 +12,7 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "tests", "native", "lru_key_check.cpp")
 NOT_CANDIDATE = 0xFFFFFFFF
-SPAN = 0xFFFFFFFE  # ticks within the last 2^32 - 3 calls keep their order
+SPAN = 0xFFFFFFFD  # occupied candidates' ticks within this span of the oldest keep their order
 
 
 @pytest.fixture(scope="module")
@@ -36,43 +36,56 @@ def key_order(keys_):
     return sorted(range(len(keys_)), key=lambda s: (keys_[s], s))
 
 
-@pytest.mark.parametrize("now", [1, 5, 1000, 2**32 - 3, 2**32 - 1, 2**32, 2**32 + 7, 2**33 + 12345,
-                                 2**62])
-def test_order_matches_ticks_within_the_span(keys, now):
-    rng = random.Random(now)
-    lo = max(0, now - SPAN + 1)  # oldest tick still distinguished
-    ticks = [-1, -1, lo, now - 1, now - 1]
-    ticks += [rng.randint(lo, now - 1) for _ in range(200)]
-    # neighbours of 2^32 and of the span's edge when they are candidates
-    for t in (2**32 - 2, 2**32 - 1, 2**32, 2**32 + 1, lo + 1, lo + 2):
-        if lo <= t < now:
+@pytest.mark.parametrize("tmin", [0, 5, 1000, 2**32 - 3, 2**32 - 1, 2**32, 2**32 + 7, 2**33 + 12345,
+                                  2**62])
+def test_order_matches_ticks_within_the_span(keys, tmin):
+    """Empty slots and occupied ticks in [tmin, tmin + SPAN): the keys order
+    the slots exactly as (tick, slot) does."""
+    rng = random.Random(tmin)
+    hi = tmin + SPAN - 1  # newest tick still distinguished
+    ticks = [-1, -1, tmin, tmin, hi, hi]
+    ticks += [rng.randint(tmin, hi) for _ in range(200)]
+    ticks += [rng.randint(tmin, tmin + 50) for _ in range(50)]  # near-ties
+    for t in (2**32 - 2, 2**32 - 1, 2**32, 2**32 + 1, tmin + 1, hi - 1):
+        if tmin <= t <= hi:
             ticks.append(t)
     rng.shuffle(ticks)
-    k = keys([(t, now) for t in ticks])
+    k = keys([(t, tmin) for t in ticks])
     assert all(0 <= v < NOT_CANDIDATE for v in k)
     assert key_order(k) == lru_order(ticks)
     assert all((v == 0) == (t < 0) for v, t in zip(k, ticks))
+    assert all(v == 1 for v, t in zip(k, ticks) if t == tmin)
 
 
 def test_truncation_case_crossing_2_32(keys):
     """Ticks on both sides of 2^32: a key of the low 32 bits of tick + 1 would
     put 2^32 + 1 before 2^32 - 2 (and collide with the non-candidate value)."""
-    now = 2**32 + 2
+    tmin = 2**32 - 2
     ticks = [2**32 - 2, 2**32 - 1, 2**32, 2**32 + 1, -1]
-    k = keys([(t, now) for t in ticks])
+    k = keys([(t, tmin) for t in ticks])
     assert k[4] == 0 and k[0] < k[1] < k[2] < k[3] < NOT_CANDIDATE
     truncated = [(t + 1) & 0xFFFFFFFF for t in ticks]
     assert key_order(truncated) != lru_order(ticks)
 
 
 def test_saturation_beyond_the_span(keys):
-    """Slots untouched for 2^32 - 2 calls or more share key 1: after every
-    empty slot, before every slot touched later, ordered among themselves by
-    slot index (the one departure from exact LRU, documented)."""
-    now = 2**40
-    old = [now - SPAN, now - SPAN - 1, 5, 0]
-    recent = [now - SPAN + 1, now - 1]
-    k = keys([(t, now) for t in old + recent + [-1]])
-    assert k[:4] == [1, 1, 1, 1]
+    """Occupied candidates touched SPAN calls or more after the oldest share
+    the largest key: after every other candidate, ordered among themselves by
+    slot index (the one departure from exact LRU; the oldest, which the
+    victims are drawn from, stay exact)."""
+    tmin = 2**40
+    inside = [tmin, tmin + 1, tmin + SPAN - 1]
+    beyond = [tmin + SPAN, tmin + SPAN + 5, tmin + 2**33]
+    k = keys([(t, tmin) for t in inside + beyond + [-1]])
     assert k[6] == 0
-    assert 1 < k[4] < k[5] <= SPAN
+    assert k[0] == 1 and k[0] < k[1] < k[2] < k[3]
+    assert k[3:6] == [0xFFFFFFFE] * 3
+
+
+def test_small_spread_means_small_keys(keys):
+    """The keys' range is the candidates' age range (what the select's digit
+    skipping relies on), also with empty slots present and far-off absolute
+    ticks."""
+    tmin = 2**35 + 17
+    ticks = [-1, tmin, tmin + 3, tmin + 1000]
+    assert keys([(t, tmin) for t in ticks]) == [0, 1, 4, 1001]
