@@ -448,8 +448,11 @@ def copy_calibration():
     """Four launches of an elementwise kernel (negate) that reads 1 GiB and
     writes 1 GiB of float32: the HBM traffic counters of these launches are
     what a counter reads for a known number of bytes.  Also times (HIP
-    events) the same kernel at the decode FFN's size, 72 MB of traffic, as a
-    reference for what one short streaming launch reaches."""
+    events) the same kernel at the decode FFN's size, 72 MB of traffic, and
+    a one-element kernel, as references for
+    what one short launch reaches between two events on this GPU (also
+    with the events the library's timing uses, without a system-scope
+    fence)."""
     import torch
     n = 1 << 28
     a = torch.ones(n, dtype=torch.float32, device="cuda")
@@ -475,6 +478,48 @@ def copy_calibration():
     us = sum(ts) / len(ts) * 1e3
     out["stream_72MB_us"] = round(us, 2)
     out["stream_72MB_gbps"] = round(2 * m * 4 / us / 1e3, 1)
+
+    # the same references timed with the events the library's timing uses
+    # (no system-scope fence), on torch's stream: a one-element kernel (the
+    # floor of one launch between two events) and the 72 MB negation
+    import ctypes
+    hip = ctypes.CDLL("libamdhip64.so.7")
+    hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+    hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+    hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+    hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    ev = [ctypes.c_void_p(), ctypes.c_void_p()]
+    for e in ev:
+        assert hip.hipEventCreateWithFlags(ctypes.byref(e), 0x20000000) == 0  # hipEventDisableSystemFence
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def event_us(fn, reps=200, skip=20):
+        t = []
+        ms = ctypes.c_float()
+        for it in range(reps):
+            # a 2 GiB pass first keeps the GPU busy while the host enqueues the
+            # events and the kernel, as the decode stream's fill does for the
+            # expert FFN, so no host submission latency sits between the events
+            torch.neg(a, out=b)
+            assert hip.hipEventRecord(ev[0], stream) == 0
+            fn(it)
+            assert hip.hipEventRecord(ev[1], stream) == 0
+            assert hip.hipEventSynchronize(ev[1]) == 0
+            assert hip.hipEventElapsedTime(ctypes.byref(ms), ev[0], ev[1]) == 0
+            if it >= skip:
+                t.append(ms.value * 1e3)
+        return sum(t) / len(t)
+
+    one = torch.zeros(1, dtype=torch.float32, device="cuda")
+    out["fenceless_events"] = {
+        "queued_behind": "a 2 GiB elementwise pass",
+        "one_element_kernel_us": round(event_us(lambda it: one.add_(1.0)), 2),
+        "stream_72MB_us": round(event_us(lambda it: torch.neg(srcs[it % 8], out=dst)), 2)}
+    out["fenceless_events"]["stream_72MB_frac_of_8TBps"] = round(
+        2 * m * 4 / (out["fenceless_events"]["stream_72MB_us"] * 1e-6) / 8e12, 4)
+    for e in ev:
+        hip.hipEventDestroy(e)
     return out
 
 

@@ -18,9 +18,10 @@
 // Everything is deterministic: no atomics touch outputs.
 //
 // GEMM tiling (gfx950, v_mfma_f32_32x32x16_bf16): a workgroup of 4 waves owns
-// a 128-row M-tile of one expert and a 256-column N-tile, the waves in a 2x2
-// grid of 64 x 128 wave tiles (2 x 4 MFMA tiles); an expert's last tile of at
-// most 64 rows runs as 64 x 256 with the waves side by side.  K steps of 64
+// a 128-row M-tile of one expert and a 256-column N-tile; each wave takes a
+// quarter of the columns and every row, in 32-row MFMA blocks, and computes
+// only the ceil(rows / 32) blocks the tile holds (an expert's last tile is
+// short).  Each wave converts only its own quarter of the B tile.  K steps of 64
 // go through three LDS stages that direct-to-LDS copies fill two steps ahead
 // (A rows XOR-swizzled by 16-byte chunk, B as raw MXFP4 codes, a quarter of
 // its bf16 size, E8M0 scales per two steps).  Each lane dequantises its B
@@ -253,14 +254,13 @@ __global__ __launch_bounds__(kGemmThreads, 2) void grouped_gemm_kernel(GemmArgs 
   if (ml >= per_xcd || mt >= n_mtiles) return;
   const int tile = a.tiles[mt];
   const int e = tile >> 20, m0 = ((tile >> 1) & 0x7FFFF) * 64;
-  const bool half = tile & 1;  // at most 64 rows: computed as 64 x 256
+  const bool half = tile & 1;  // a last tile of at most 64 rows
   const int eslot = a.slot_of ? a.slot_of[e] : a.slot0 + e;
   if (eslot < 0) return;  // not in this on-demand pass
   const int pos0 = a.offsets[e] + m0;
   const int rows = min(half ? kBM / 2 : kBM, a.offsets[e + 1] - pos0);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
 
   // rows past the expert's end (padding of the last M-tile) read the tile's
   // first row: no masked loads, and their results are never written
@@ -319,25 +319,21 @@ __global__ __launch_bounds__(kGemmThreads, 2) void grouped_gemm_kernel(GemmArgs 
 
   const int lr = lane & 31, kg = lane >> 5;
 
-  // The rest runs in one of two shapes.  Full tile: waves in a 2 x 2 grid of
-  // 64 x 128 wave tiles (2 x 4 MFMA tiles); B rows GLU -> gate wn*64 + {0,32}
-  // and up 128 + wn*64 + {0,32}, down -> wn*128 + {0,32,64,96}.  Half tile
-  // (at most 64 rows): the four waves side by side, each 64 x 64 (2 x 2 MFMA
-  // tiles); B rows GLU -> gate 32*w and up 128 + 32*w, down -> 64*w + {0,32}.
-  // The copies are the same in both shapes (the unused A rows repeat row 0).
-  auto run = [&](auto half_c) {
-    constexpr bool HALF = decltype(half_c)::value;
-    constexpr int NJ = HALF ? 2 : 4;
-    const int arow0 = HALF ? 0 : wm * 64;
+  // Compute shape: the four waves side by side, each all NI = ceil(rows / 32)
+  // row blocks of the tile by 64 columns (NI x 2 MFMA tiles); B rows GLU ->
+  // gate 32*w and up 128 + 32*w (a wave's gate and up accumulators share
+  // lanes), down -> 64*w + {0,32}.  The copies are the same for every NI (the
+  // unused A rows repeat row 0).
+  auto run = [&](auto ni_c) {
+    constexpr int NI = decltype(ni_c)::value;  // 32-row blocks computed: ceil(rows / 32)
+    constexpr int NJ = 2;
+    const int arow0 = 0;
     int brow[NJ];
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      if (HALF) brow[j] = GLU ? j * (kBN / 2) + wave * 32 : wave * 64 + j * 32;
-      else brow[j] = GLU ? (j < 2 ? 0 : kBN / 2) + wn * 64 + (j & 1) * 32 : wn * 128 + j * 32;
-    }
-    f32x16 acc[2][NJ];
+    for (int j = 0; j < NJ; ++j) brow[j] = GLU ? j * (kBN / 2) + wave * 32 : wave * 64 + j * 32;
+    f32x16 acc[NI][NJ];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < NI; ++i)
 #pragma unroll
       for (int j = 0; j < NJ; ++j) acc[i][j] = f32x16{};
 
@@ -357,11 +353,11 @@ __global__ __launch_bounds__(kGemmThreads, 2) void grouped_gemm_kernel(GemmArgs 
       }
       // every A fragment of the step is requested up front, so one LDS
       // latency per step is exposed instead of one per 16-wide slice
-      bf16x8 af[kBK / 16][2];
+      bf16x8 af[kBK / 16][NI];
 #pragma unroll
       for (int ks = 0; ks < kBK / 16; ++ks)
 #pragma unroll
-        for (int i = 0; i < 2; ++i) af[ks][i] = *(const bf16x8*)(sa + swz(arow0 + i * 32 + lr, 4 * kg + ks));
+        for (int i = 0; i < NI; ++i) af[ks][i] = *(const bf16x8*)(sa + swz(arow0 + i * 32 + lr, 4 * kg + ks));
       __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the MFMAs
 #pragma unroll
       for (int ks = 0; ks < kBK / 16; ++ks) {
@@ -372,7 +368,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void grouped_gemm_kernel(GemmArgs 
           bfr[j] = fp4x8_to_bf16(w, bsc[j]);
         }
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < NI; ++i)
 #pragma unroll
           for (int j = 0; j < NJ; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks][i], bfr[j], acc[i][j], 0, 0, 0);
@@ -413,7 +409,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void grouped_gemm_kernel(GemmArgs 
       float* cbuf = (float*)s_stage + wave * (32 * CS);
       const int c4 = lane % LPR, rsub = lane / LPR;
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
+      for (int i = 0; i < NI; ++i) {
 #pragma unroll
         for (int j = 0; j < NJ; ++j)
 #pragma unroll
@@ -432,7 +428,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void grouped_gemm_kernel(GemmArgs 
     }
     // gate/up epilogue: h = silu(g) * u rounded to bf16, rows in pos order
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < NI; ++i) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int row = arow0 + i * 32 + 8 * (r >> 2) + 4 * kg + (r & 3);
@@ -444,15 +440,19 @@ __global__ __launch_bounds__(kGemmThreads, 2) void grouped_gemm_kernel(GemmArgs 
             const float hv = g * u * __builtin_amdgcn_rcpf(1.f + __expf(-g));
             uint32_t bits = __float_as_uint(hv);
             bits += 0x7FFFu + ((bits >> 16) & 1u);
-            const int col = n0 + (HALF ? wave * 32 : wn * 64 + j * 32) + lr;
+            const int col = n0 + wave * 32 + lr;
             a.h_out[(size_t)(pos0 + row) * a.N + col] = (uint16_t)(bits >> 16);
           }
         }
       }
     }
   };
-  if (half) run(std::true_type{});
-  else run(std::false_type{});
+  switch ((rows + 31) >> 5) {
+    case 1: run(std::integral_constant<int, 1>{}); break;
+    case 2: run(std::integral_constant<int, 2>{}); break;
+    case 3: run(std::integral_constant<int, 3>{}); break;
+    default: run(std::integral_constant<int, 4>{}); break;
+  }
 }
 
 // y[t] = sum over ascending j of w[t][j] * P[t*k + j]
