@@ -300,6 +300,13 @@ typedef struct {
   const float* p_cpu;        /* [max_tokens*k][H] fp32 (pinned host, mapped)   */
   const void* slot_base;     /* slot s at slot_base + s * moe_expert_bytes()   */
   int32_t n_slots, max_slots, umax, kmax;
+  const uint64_t* h_marked;  /* [max_tokens*k][inter] the expert FFN's
+                                intermediate silu(gate) * up: fp32 bits in the
+                                low word, the low 32 bits of the tick of the
+                                call that wrote it in the high word (an entry
+                                counts only with its call's mark; every 2^30
+                                ticks the control kernel sets all marks to
+                                that call's tick with bit 31 flipped)         */
 } moe_plan_view;
 
 moe_status moe_plan_view_get(moe_ctx* ctx, moe_plan_view* out);

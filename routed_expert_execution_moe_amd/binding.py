@@ -49,7 +49,8 @@ class PlanView(ctypes.Structure):
                 ("slot2id", ctypes.c_void_p), ("slot_ts", ctypes.c_void_p),
                 ("tick", ctypes.c_void_p), ("p_gpu", ctypes.c_void_p), ("p_cpu", ctypes.c_void_p),
                 ("slot_base", ctypes.c_void_p), ("n_slots", ctypes.c_int32),
-                ("max_slots", ctypes.c_int32), ("umax", ctypes.c_int32), ("kmax", ctypes.c_int32)]
+                ("max_slots", ctypes.c_int32), ("umax", ctypes.c_int32), ("kmax", ctypes.c_int32),
+                ("h_marked", ctypes.c_void_p)]
 
 
 class PrefillView(ctypes.Structure):

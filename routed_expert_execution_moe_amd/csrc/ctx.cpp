@@ -311,7 +311,7 @@ extern "C" moe_status moe_create(const moe_config* cfg, void* host_pool, size_t 
   ALLOC(ctx->slot_ts, sizeof(int64_t) * std::max(1, cfg->max_slots));
   ALLOC(ctx->dstate, sizeof(DevState));
   ALLOC(ctx->p_gpu, sizeof(float) * maxTk * H);
-  ALLOC(ctx->h_mid, sizeof(float) * maxTk * I);
+  ALLOC(ctx->h_mid, sizeof(uint64_t) * maxTk * I);
 
   // plan buffers: one allocation, 256-byte aligned sub-arrays
   {
@@ -327,7 +327,6 @@ extern "C" moe_status moe_create(const moe_config* cfg, void* host_pool, size_t 
            o_fo = take(4 * ctx->kmax);
     size_t o_cpu = take(4 * ctx->umax), o_gu = take(4 * ctx->umax), o_gs = take(4 * ctx->umax);
     size_t o_sm = take(4 * maxTk);
-    size_t o_fd = take(4 * (size_t)kFfnDoneStride * kFfnSub * ctx->umax);
     size_t o_hw = take(4);
     ALLOC(ctx->plan_alloc, off);
     uint8_t* b = ctx->plan_alloc;
@@ -344,7 +343,8 @@ extern "C" moe_status moe_create(const moe_config* cfg, void* host_pool, size_t 
     p.gpu_u = (int32_t*)(b + o_gu);
     p.gpu_slot = (int32_t*)(b + o_gs);
     p.slot_map = (int32_t*)(b + o_sm);
-    p.ffn_done = (int32_t*)(b + o_fd);
+    p.h_marked = ctx->h_mid;
+    p.h_words = (int64_t)maxTk * I;
     p.host_work = (int32_t*)(b + o_hw);
     p.hblock_bytes = sizeof(HostBlockHeader) + 2 * 4 * (size_t)maxTk;
     p.x_offset = (p.hblock_bytes + 255) / 256 * 256;
@@ -648,6 +648,7 @@ extern "C" moe_status moe_plan_view_get(moe_ctx* ctx, moe_plan_view* v) {
   v->slot_base = ctx->pool.base;
   v->n_slots = ctx->n_slots; v->max_slots = ctx->cfg.max_slots;
   v->umax = ctx->umax; v->kmax = ctx->kmax;
+  v->h_marked = ctx->h_mid;
   return MOE_OK;
 }
 

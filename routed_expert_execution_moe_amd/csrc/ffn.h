@@ -11,30 +11,31 @@
 //     routed pair and requests that token's inputs, then loads its weight rows
 //     into registers (lane l holds 16-byte chunks l, l+64, ... of each row),
 //     evaluates every routed token of the expert, reduces the rows across the
-//     wave, stores h = silu(g) * u (fp32) per token and bumps the expert's
-//     counter;
+//     wave and stores h = silu(g) * u (fp32) per token;
 //   * down items (the later workgroups, four row blocks of one expert each):
 //     RW_B rows of W_down per wave.  The waves load their rows first (they
-//     stream behind the gate/up weights), one wave waits for the expert's
-//     counters to be complete, the workgroup stages h of each routed pair in
-//     LDS, and every wave writes its fp32 partial rows.
+//     stream behind the gate/up weights), then the workgroup collects h of
+//     each routed pair into LDS as it becomes valid, and every wave writes
+//     its fp32 partial rows.
 // Memory serves requests roughly in issue order, so the gate/up halves
-// finish while the down weights are still streaming and the wait is mostly
-// already over when a down wave gets its data.  Workgroups are dispatched in
-// index order and every gate/up item precedes every down item, so a waiting
-// down item only waits for items that are already running; the wait is still
-// bounded (wall clock) and flags an error instead of hanging.  The control
-// kernel zeroes the counters of each call.
+// finish while the down weights are still streaming and h is mostly valid
+// when a down wave gets its data.  Workgroups are dispatched in index order
+// and every gate/up item precedes every down item, so a waiting down item
+// only waits for items that are already running; the wait is still bounded
+// (wall clock) and flags an error instead of hanging.
 //
 // The intermediate crosses compute dies (each XCD has its own L2), so it
-// moves with device-coherent accesses instead of cache-wide fences: the
-// gate/up wave stores h with device scope, waits for its stores to complete,
-// then bumps one of its expert's counters; the down workgroup polls the
-// counters with device-scope loads and reads h with device-scope vector
-// loads (buffer loads with the device-scope cache policy), rather than an L2
-// write-back and invalidate paid by every wave.  Gate/up items spread their
-// counts over several counters on separate lines: same-address atomics from
-// hundreds of waves queue behind each other.
+// moves with device-coherent accesses instead of cache-wide fences.  Each
+// value travels with its own validity mark: one 64-bit device-scope store of
+// {value, low 32 bits of the call's LRU tick}, which a reader sees whole or
+// not at all.  A gate/up wave therefore stores and exits, with no wait for
+// its stores and no completion counter (a counter has to wait until the
+// stores behind it have reached memory, which under a full read queue takes
+// microseconds and holds the wave's slot from the down workgroups still to be
+// dispatched); a down workgroup polls the entries it needs until their marks
+// equal this call's.  The control kernel rewrites every mark once per 2^30
+// ticks to a value no tick of the new epoch has, so an entry left from an
+// earlier call never matches, also where the low word wraps.
 //
 // Arithmetic: bf16 x bf16 uses the two-term bf16 dot with fp32 accumulation;
 // MXFP4 weights are expanded with the gfx950 scaled FP4 converts (to bf16
@@ -65,10 +66,8 @@ struct FfnArgs {
   size_t og, ou, od;          // byte offsets of W_gate, W_up, W_down (codes for MXFP4)
   size_t sg, su, sd;          // byte offsets of their E8M0 scales (MXFP4)
   const void* x;              // [T][H] activations
-  float* h;                   // [Tk][I] fp32 intermediate
-  uint32_t h_bytes;           // bytes of h (buffer descriptor range)
+  uint64_t* h;                // [Tk][I] {fp32 bits, tick mark} intermediate
   float* p;                   // [Tk][H] fp32 partial rows
-  int32_t* done;              // [umax] finished gate/up items per GPU expert
   HostSync* sync;             // error word (2 = a down item gave up waiting)
   uint64_t wait_ticks;
   int umax;
@@ -82,8 +81,6 @@ template <int WT> struct FfnChunk;
 template <> struct FfnChunk<MOE_F32> { static constexpr int CH = 4; };
 template <> struct FfnChunk<MOE_BF16> { static constexpr int CH = 8; };
 template <> struct FfnChunk<MOE_MXFP4> { static constexpr int CH = 32; };
-
-constexpr int kCpolDevice = 16;  // SC1: device-scope coherent buffer access
 
 // chunk slots per lane: gate/up items hold kRegA per matrix, down items kRegB
 constexpr int kRegA = 8;
@@ -246,6 +243,7 @@ __device__ void ffn_gate_up(const FfnArgs& a, int g, int rb, int lane) {
   constexpr int CH = FfnChunk<WT>::CH;
   constexpr int RW = kRegA / CPL;
   const int K = a.H, nch = K / CH, row0 = rb * RW;
+  const uint64_t mark = (uint64_t)(uint32_t)a.counts->tick_lo << 32;
 
   // the slot and its first routed pair come first, so that pair's inputs
   // are requested ahead of the weights and arrive with them
@@ -310,8 +308,8 @@ __device__ void ffn_gate_up(const FfnArgs& a, int g, int rb, int lane) {
     constexpr int SH = 6 - Log2<2 * RW>::v;
     const int r = lane >> SH;
     if (lane < 32 && (lane & ((1 << SH) - 1)) == 0 && row0 + r < a.I)
-      __hip_atomic_store(a.h + (size_t)p * a.I + row0 + r, ffn_silu(v[0]) * up, __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(a.h + (size_t)p * a.I + row0 + r, mark | __float_as_uint(ffn_silu(v[0]) * up),
+                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     p = ffn_next_pair(a, slot, lane, base, bm);
     if (p >= 0) {
 #pragma unroll
@@ -319,21 +317,38 @@ __device__ void ffn_gate_up(const FfnArgs& a, int g, int rb, int lane) {
         ffn_load_x<WT, XT>(a.x, (size_t)(p / a.k) * K, min(lane + 64 * c, nch - 1), xw[c]);
     }
   }
-  // publish: this wave's device-scope stores complete, then the count
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  if (lane == 0)
-    __hip_atomic_fetch_add(a.done + (g * kFfnSub + rb % kFfnSub) * kFfnDoneStride, 1,
-                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Down items run as whole workgroups of one expert (four row blocks): wave
-// 0 waits for the expert's gate/up counters, then the workgroup stages h of
-// each routed pair in LDS once and every wave reads its chunks from there.
+// h of pair p into LDS: each thread polls its entries until they carry this
+// call's mark.  A workgroup that waits past the bound flags error 2 and
+// goes on with what it has (the call then fails).
+__device__ inline void ffn_collect_h(const FfnArgs& a, int p, int K, uint32_t want, float* lds_h) {
+  const uint64_t* hp = a.h + (size_t)p * K;
+  uint64_t t0 = 0;
+  for (int i = threadIdx.x; i < K; i += blockDim.x) {
+    uint64_t v = __hip_atomic_load(hp + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    while ((uint32_t)(v >> 32) != want) {
+      if (t0 == 0) t0 = wall_clock64();
+      if (wall_clock64() - t0 > a.wait_ticks) {
+        __hip_atomic_store(&a.sync->error, 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+      v = __hip_atomic_load(hp + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    lds_h[i] = __uint_as_float((uint32_t)v);
+  }
+}
+
+// Down items run as whole workgroups of one expert (four row blocks): the
+// workgroup collects h of each routed pair in LDS once and every wave reads
+// its chunks from there.
 template <int WT, int CPL>
 __device__ void ffn_down(const FfnArgs& a, int g, int rb, int lane, float* lds_h) {
   constexpr int CH = FfnChunk<WT>::CH;
   constexpr int RW = FfnRegB<WT>::N / CPL;
   typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+  const uint32_t want = (uint32_t)a.counts->tick_lo;
   const int slot = __builtin_amdgcn_readfirstlane(a.gpu_slot[g]);
   const uint8_t* sp = a.slot_base + (size_t)slot * a.stride;
   const int K = a.I, nch = K / CH, row0 = rb * RW;
@@ -359,36 +374,13 @@ __device__ void ffn_down(const FfnArgs& a, int g, int rb, int lane, float* lds_h
     }
   }
 
-  // wave 0 waits: lanes 0..kFfnSub-1 each watch one sub-counter of the expert
-  if (threadIdx.x < 64) {
-    const uint64_t t0 = wall_clock64();
-    const int sub = lane < kFfnSub ? lane : 0;
-    const int want = (a.itemsA - sub + kFfnSub - 1) / kFfnSub;
-    const int32_t* ctr = a.done + (g * kFfnSub + sub) * kFfnDoneStride;
-    for (;;) {
-      const bool ok = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= want;
-      if (__ballot(ok || lane >= kFfnSub) == ~0ull) break;
-      if (wall_clock64() - t0 > a.wait_ticks) {
-        if (lane == 0) __hip_atomic_store(&a.sync->error, 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-        break;
-      }
-      __builtin_amdgcn_s_sleep(8);
-    }
-  }
-  __syncthreads();  // h is read only after the count is complete
-  const __amdgpu_buffer_rsrc_t hr = __builtin_amdgcn_make_buffer_rsrc(a.h, 0, a.h_bytes, 0x00020000);
-
   int base = 0;
   uint64_t bm = __ballot(lane < a.Tk && a.slot_map[lane] == slot);
   for (;;) {
     const int p = ffn_next_pair(a, slot, lane, base, bm);  // uniform in the workgroup
     if (p < 0) break;
     __syncthreads();  // the previous pair's reads of LDS are done
-    for (int i = threadIdx.x; i < K / 4; i += blockDim.x) {
-      const u32x4v v = __builtin_amdgcn_raw_buffer_load_b128(hr, (int)(((size_t)p * K + 4 * i) * 4), 0,
-                                                             kCpolDevice);
-      ((u32x4v*)lds_h)[i] = v;
-    }
+    ffn_collect_h(a, p, K, want, lds_h);
     __syncthreads();
 #pragma unroll
     for (int r = 0; r < RW; ++r)
@@ -471,9 +463,7 @@ hipError_t launch_ffn_typed(moe_ctx* ctx, const void* x, int T, hipStream_t s) {
   }
   a.x = x;
   a.h = ctx->h_mid;
-  a.h_bytes = (uint32_t)(sizeof(float) * (size_t)ctx->cfg.max_tokens * c.top_k * I);
   a.p = ctx->p_gpu;
-  a.done = ctx->plan.ffn_done;
   a.sync = ctx->sync_dev;
   a.wait_ticks = ctx->ffn_wait_ticks;
   a.umax = ctx->umax;

@@ -18,11 +18,10 @@ constexpr int kMaxTopK = 32;
 constexpr int kMaxSlots = 32768;
 constexpr int kMaxDecodeTokens = 256;
 constexpr int kPlanThreads = 1024;
-// expert FFN completion counters: kFfnSub per GPU expert (gate/up item rb
-// counts into sub-counter rb % kFfnSub), each on its own 256-byte line, so
-// that same-address atomics do not queue behind each other
-constexpr int kFfnSub = 8;
-constexpr int kFfnDoneStride = 64;
+// the expert FFN's intermediate entries carry the low 32 bits of their
+// call's tick; every 2^kHMarkEpochBits ticks the control kernel rewrites all
+// marks to one that no tick of the new epoch has
+constexpr int kHMarkEpochBits = 30;
 
 // Device-resident scalars the control kernel owns: the LRU tick and the
 // running counters of the pool table.
@@ -32,6 +31,7 @@ struct DevState {
   int64_t prefill_layers;
   int32_t n_slots;   // current budget, read by the control kernel
   int32_t pad;
+  int64_t h_epoch;   // tick >> kHMarkEpochBits when the marks were last rewritten
 };
 
 // Everything the host branch needs from one plan, in pinned host memory that
@@ -58,7 +58,8 @@ struct PlanBufs {
   moe_plan_counts* counts;
   int32_t *uniq, *hits, *misses, *victims, *fill_u, *fill_slot, *fill_old;
   int32_t *cpu_u, *gpu_u, *gpu_slot, *slot_map;
-  int32_t* ffn_done;      // [umax * kFfnSub * kFfnDoneStride] gate/up items finished
+  uint64_t* h_marked;     // [h_words] the expert FFN's marked intermediate
+  int64_t h_words;
   int32_t* host_work;     // [1] set by the control kernel: the host branch has work
   // host block in pinned, device-mapped memory, written by the fill kernel's
   // hand-off workgroup:
@@ -160,7 +161,7 @@ struct moe_ctx {
   float* p_gpu = nullptr;      // device [max_tokens*k][H]
   float* p_cpu = nullptr;      // pinned host, mapped [max_tokens*k][H]
   const float* p_cpu_dev = nullptr;
-  float* h_mid = nullptr;      // device [max_tokens*k][I]
+  uint64_t* h_mid = nullptr;   // device [max_tokens*k][I] {fp32 bits, tick mark}
 
   // host block (pinned, mapped): the control kernel writes it, the host branch reads it
   uint8_t* hstage = nullptr;   // host address

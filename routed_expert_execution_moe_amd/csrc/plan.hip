@@ -87,8 +87,6 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   if (tid < kMaxExperts / 32) s_mask[tid] = 0;
   for (int i = tid; i < (n + 31) / 32; i += kPlanThreads) s_hitbits[i] = 0;
   if (tid < E) s_eslot[tid] = -1;
-  for (int i = tid; i < a.umax * kFfnSub; i += kPlanThreads)
-    pb.ffn_done[i * kFfnDoneStride] = 0;  // the expert FFN counts from zero
   if (tid == 0) {
     s_evict = 0;
     s_bad = 0;
@@ -99,6 +97,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   // victim's occupant when it is selected, to spare registers)
   constexpr bool kHold = SPT <= 8;
   const int64_t now = a.st->tick + 1;
+  const int64_t h_epoch = a.st->h_epoch;
   int64_t tsr[SPT];
   int32_t sid_r[kHold ? SPT : 1];
   if constexpr (kHold) {
@@ -395,6 +394,15 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     pb.gpu_u[p] = u;
     pb.gpu_slot[p] = s_eslot[e];
   }
+  // first call of a new tick epoch: every intermediate entry gets a mark no
+  // tick of this epoch has (the mark of this tick with the top bit flipped;
+  // the epoch spans 2^30 ticks), so no entry left from an earlier call
+  // passes for one of a later call of the epoch
+  const bool new_epoch = (tick >> kHMarkEpochBits) != h_epoch;
+  if (new_epoch) {
+    const uint64_t stale = (uint64_t)((uint32_t)tick ^ 0x80000000u) << 32;
+    for (int64_t i = tid; i < pb.h_words; i += kPlanThreads) pb.h_marked[i] = stale;
+  }
   if (tid == 0) {
     moe_plan_counts c;
     c.n_uniq = s_nuniq;
@@ -419,6 +427,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     st->fills += q;
     st->cpu += mm - q;
     st->evictions += s_evict;
+    if (new_epoch) st->h_epoch = tick >> kHMarkEpochBits;
   }
 }
 

@@ -119,6 +119,7 @@ __global__ void table_reset_kernel(int32_t* id2slot, int64_t n_ids, int32_t* slo
     st->plans = st->hits = st->fills = st->cpu = st->evictions = st->prefill_layers = 0;
     st->n_slots = n_slots;
     st->pad = 0;
+    st->h_epoch = -1;  // the first control call writes the intermediate's marks
   }
 }
 

@@ -12,7 +12,7 @@ import numpy as np
 import pytest
 
 import workload as W
-from tests.harness import (GpuRun, OracleRun, bf16_round_err, compare_plan, log, rel_err,
+from tests.harness import (GpuRun, OracleRun, bf16_round_err, compare_plan, d2h, h2d, log, rel_err,
                            x_f64)
 
 pytestmark = pytest.mark.gpu
@@ -183,5 +183,124 @@ def test_cpu_layers_bf16():
         assert i2s == o.st.id2slot and s2i == o.st.slot2id and ts == o.st.slot_ts
         assert any(i2s[1 * wl.E + e] >= 0 for e in range(wl.E))  # filled once released
         log(f"  host layers 1, 3 then none: worst rel err {worst:.3e}")
+    finally:
+        g.close()
+
+
+@pytest.mark.parametrize("T", [1, 3])
+def test_repeated_expert_in_a_token(T):
+    """ids given directly, with an expert listed two or three times by one
+    token (the layer sums w[t][j] * FFN_e(x_t) over every j, repeats
+    included): plans bit-exact, outputs within tolerance, and a repeated
+    pair's partial rows equal to its first occurrence's.  T = 1 runs the
+    single-pair FFN kernel, T = 3 the token loop."""
+    wl = mini(W.QWEN_BF16, L=2, steps=6, n_slots=40, T=T)
+    g = GpuRun(wl)
+    torch = g.torch
+    try:
+        o = OracleRun(wl, g.bank)
+        rng = np.random.default_rng(7)
+        worst = 0.0
+        for s in range(wl.steps):
+            for l in range(wl.L):
+                ids = np.empty((T, wl.k), np.int32)
+                for t in range(T):
+                    pick = rng.choice(wl.E, 5, replace=False)
+                    ids[t] = [pick[0], pick[0], pick[1], pick[2], pick[2], pick[2], pick[3], pick[4]]
+                    if (s + t) % 2:
+                        ids[t] = ids[t][::-1]
+                w = rng.random((T, wl.k)).astype(np.float32)
+                w /= w.sum(axis=1, keepdims=True)
+                x = W.hidden(wl, s, l)
+                xd = g.to_dev_x(x)
+                idd = torch.from_numpy(ids).to(g.dev)
+                wd = torch.from_numpy(w).to(g.dev)
+                g.B.moe_cache_plan(g.ctx, l, idd, T, xd)
+                g.B.moe_expert_ffn(g.ctx, l, xd, T)
+                g.B.moe_merge(g.ctx, wd, T, g.y[:T])
+                torch.cuda.synchronize()
+                op = o.plan(l, ids)
+                gp = g.plan_view(T)
+                compare_plan(gp, op, T)
+                pg = g.p_gpu_rows(T)
+                for t in range(T):
+                    for j in range(wl.k):
+                        first = int(np.flatnonzero(ids[t] == ids[t][j])[0])
+                        if gp["slot_map"][t][j] >= 0 and first != j:
+                            assert np.array_equal(pg[t, j], pg[t, first]), (s, l, t, j)
+                err, _ = rel_err(g.y_f64()[:T], o.output(l, x_f64(wl, x), ids, w.astype(np.float64)))
+                worst = max(worst, err)
+                assert err <= TOL[wl.w_dtype], (s, l, err)
+        log(f"  repeated experts, T={T}: worst rel err {worst:.3e}")
+    finally:
+        g.close()
+
+
+def test_intermediate_marks_across_tick_jumps():
+    """The expert FFN hands silu(gate) * up from its gate/up waves to its down
+    workgroups as 64-bit entries {fp32 value, low 32 bits of the call's tick}.
+    Before every step the clock moves on by 2^32 - 1 (the tick and every
+    occupied slot's tick, on the device and in the oracle, which keeps the
+    LRU order), so the first call of the step has the same low word as the
+    call before it: only the control kernel's rewrite of every mark at a new
+    2^30-tick epoch keeps that call's entries from passing for this one's.
+    After each call: the GPU pairs' entries carry this call's mark and hold
+    silu(W_g x) * (W_u x) of the oracle's weights; every other entry carries
+    another mark (the rewritten one after a jump); plans and outputs match
+    the oracle."""
+    from oracle import expert as OX
+    wl = mini(W.QWEN_BF16, L=2, steps=6, n_slots=189)
+    g = GpuRun(wl)
+    try:
+        o = OracleRun(wl, g.bank)
+        logits = W.router_logits(wl)
+        Tk, I = wl.T * wl.k, wl.I
+        checked = 0
+        for s in range(wl.steps):
+            jumped = s > 0
+            if jumped:
+                v = g.B.moe_plan_view_get(g.ctx)
+                ts = d2h(v.slot_ts, v.n_slots, np.int64)
+                tick = int(d2h(v.tick, 1, np.int64)[0])
+                assert tick == o.st.tick
+                off = 2**32 - 1
+                ts[ts >= 0] += off
+                h2d(v.slot_ts, ts)
+                h2d(v.tick, np.array([tick + off], np.int64))
+                o.st.slot_ts = [t + off if t >= 0 else t for t in o.st.slot_ts]
+                o.st.tick += off
+            for l in range(wl.L):
+                x = W.hidden(wl, s, l)
+                ids_g, w_g = g.decode_call(l, logits[s, l], x)
+                ids_o, w_o = o.route(logits[s, l])
+                assert np.array_equal(ids_g, ids_o), (s, l)
+                op = o.plan(l, ids_o)
+                gp = g.plan_view(wl.T)
+                compare_plan(gp, op, wl.T)
+                v = g.B.moe_plan_view_get(g.ctx)
+                tick = int(d2h(v.tick, 1, np.int64)[0])
+                cur = tick & 0xFFFFFFFF
+                hm = d2h(v.h_marked, Tk * I, np.uint64).reshape(Tk, I)
+                marks = (hm >> np.uint64(32)).astype(np.int64)
+                vals = (hm & np.uint64(0xFFFFFFFF)).astype(np.uint32).view(np.float32)
+                sm = np.asarray(gp["slot_map"]).ravel()
+                xf = x_f64(wl, x)
+                for p in range(Tk):
+                    if sm[p] >= 0:
+                        assert (marks[p] == cur).all(), (s, l, p)
+                        wg, wu, _ = o.weights(l * wl.E + int(ids_o.ravel()[p]))
+                        xt = xf[p // wl.k]
+                        h_ref = OX.silu(wg @ xt) * (wu @ xt)
+                        rms = np.sqrt(np.mean(h_ref ** 2))
+                        assert np.max(np.abs(vals[p] - h_ref)) <= 2e-3 * rms, (s, l, p)
+                        checked += 1
+                    else:
+                        assert (marks[p] != cur).all(), (s, l, p)
+                        if jumped and l == 0:
+                            assert (marks[p] == cur ^ 0x80000000).all(), (s, l, p)
+                err, _ = rel_err(g.y_f64(), o.output(l, xf, ids_o, w_o))
+                assert err <= TOL[wl.w_dtype], (s, l, err)
+        assert o.st.tick > 5 * 2**32
+        log(f"  marks checked on {checked} GPU pairs over {wl.steps - 1} clock jumps")
     finally:
         g.close()
