@@ -319,25 +319,45 @@ __device__ void ffn_gate_up(const FfnArgs& a, int g, int rb, int lane) {
   }
 }
 
-// h of pair p into LDS: each thread polls its entries until they carry this
-// call's mark.  A workgroup that waits past the bound flags error 2 and
-// goes on with what it has (the call then fails).
-__device__ inline void ffn_collect_h(const FfnArgs& a, int p, int K, uint32_t want, float* lds_h) {
+// h entries per thread of the first routed pair that a down workgroup
+// requests together with its weights (all of h for I <= 1,024)
+constexpr int kHEarly = 4;
+
+__device__ inline uint64_t ffn_load_h(const uint64_t* e) {
+  return __hip_atomic_load(e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// One entry of h into LDS once it carries this call's mark (v: its first
+// reading).  A thread that waits past the bound flags error 2 and goes on
+// with what it has (the call then fails).
+__device__ inline void ffn_take_h(const FfnArgs& a, const uint64_t* e, uint64_t v, uint32_t want,
+                                  uint64_t& t0, float* dst) {
+  while ((uint32_t)(v >> 32) != want) {
+    if (t0 == 0) t0 = wall_clock64();
+    if (wall_clock64() - t0 > a.wait_ticks) {
+      __hip_atomic_store(&a.sync->error, 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(2);
+    v = ffn_load_h(e);
+  }
+  *dst = __uint_as_float((uint32_t)v);
+}
+
+// h of pair p into LDS (256 threads); `early` holds the first readings of
+// the thread's first kHEarly entries when EARLY.
+template <bool EARLY>
+__device__ inline void ffn_collect_h(const FfnArgs& a, int p, int K, uint32_t want, float* lds_h,
+                                     const uint64_t (&early)[kHEarly]) {
   const uint64_t* hp = a.h + (size_t)p * K;
   uint64_t t0 = 0;
-  for (int i = threadIdx.x; i < K; i += blockDim.x) {
-    uint64_t v = __hip_atomic_load(hp + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    while ((uint32_t)(v >> 32) != want) {
-      if (t0 == 0) t0 = wall_clock64();
-      if (wall_clock64() - t0 > a.wait_ticks) {
-        __hip_atomic_store(&a.sync->error, 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-        break;
-      }
-      __builtin_amdgcn_s_sleep(2);
-      v = __hip_atomic_load(hp + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    lds_h[i] = __uint_as_float((uint32_t)v);
+#pragma unroll
+  for (int j = 0; j < kHEarly; ++j) {
+    const int i = (int)threadIdx.x + 256 * j;
+    if (i < K) ffn_take_h(a, hp + i, EARLY ? early[j] : ffn_load_h(hp + i), want, t0, lds_h + i);
   }
+  for (int i = (int)threadIdx.x + 256 * kHEarly; i < K; i += 256)
+    ffn_take_h(a, hp + i, ffn_load_h(hp + i), want, t0, lds_h + i);
 }
 
 // Down items run as whole workgroups of one expert (four row blocks): the
@@ -349,6 +369,7 @@ __device__ void ffn_down(const FfnArgs& a, int g, int rb, int lane, float* lds_h
   constexpr int RW = FfnRegB<WT>::N / CPL;
   typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
   const uint32_t want = (uint32_t)a.counts->tick_lo;
+  const int sm0 = lane < a.Tk ? a.slot_map[lane] : -2;
   const int slot = __builtin_amdgcn_readfirstlane(a.gpu_slot[g]);
   const uint8_t* sp = a.slot_base + (size_t)slot * a.stride;
   const int K = a.I, nch = K / CH, row0 = rb * RW;
@@ -374,13 +395,21 @@ __device__ void ffn_down(const FfnArgs& a, int g, int rb, int lane, float* lds_h
     }
   }
 
+  // the first pair's h is requested right behind the weights: it is mostly
+  // complete by the time the weights arrive, and then comes with them
   int base = 0;
-  uint64_t bm = __ballot(lane < a.Tk && a.slot_map[lane] == slot);
-  for (;;) {
-    const int p = ffn_next_pair(a, slot, lane, base, bm);  // uniform in the workgroup
-    if (p < 0) break;
+  uint64_t bm = __ballot(sm0 == slot);
+  int p = ffn_next_pair(a, slot, lane, base, bm);  // uniform in the workgroup
+  uint64_t early[kHEarly];
+#pragma unroll
+  for (int j = 0; j < kHEarly; ++j) {
+    const int i = (int)threadIdx.x + 256 * j;
+    early[j] = p >= 0 && i < K ? ffn_load_h(a.h + (size_t)p * K + i) : 0;
+  }
+  for (bool first = true; p >= 0; p = ffn_next_pair(a, slot, lane, base, bm), first = false) {
     __syncthreads();  // the previous pair's reads of LDS are done
-    ffn_collect_h(a, p, K, want, lds_h);
+    if (first) ffn_collect_h<true>(a, p, K, want, lds_h, early);
+    else ffn_collect_h<false>(a, p, K, want, lds_h, early);
     __syncthreads();
 #pragma unroll
     for (int r = 0; r < RW; ++r)
