@@ -25,6 +25,7 @@
 namespace moert {
 
 constexpr int kWaves = kPlanThreads / 64;
+constexpr int kSmallK = 16;  // victim counts chosen by wave minima instead of the radix select
 constexpr uint32_t kSentinel = kLruNoCandidate;
 
 struct PlanArgs {
@@ -60,6 +61,147 @@ __device__ inline int lane_rank(uint64_t m, int lane) {
   return __builtin_popcountll(m & ((1ull << lane) - 1ull));
 }
 
+// Wave minima through DPP lane moves (VALU operand modifiers, a few cycles
+// each, instead of LDS-routed permutes): swaps within quads, the half-row
+// and row mirrors, then the broadcasts of lane 15 into the next row and of
+// lane 31 into the upper half, which leave the wave's minimum in lane 63.
+// A DPP step that has no source for a lane (the broadcasts' unselected
+// rows) leaves that lane's value unchanged.
+template <int CTRL, int ROWS>
+__device__ inline int64_t dpp_min64_step(int64_t v) {
+  const int lo = (int)(uint32_t)v, hi = (int)(v >> 32);
+  const int tl = __builtin_amdgcn_update_dpp(lo, lo, CTRL, ROWS, 0xF, false);
+  const int th = __builtin_amdgcn_update_dpp(hi, hi, CTRL, ROWS, 0xF, false);
+  const int64_t t = (int64_t)(((uint64_t)(uint32_t)th << 32) | (uint32_t)tl);
+  return min(v, t);
+}
+template <int CTRL, int ROWS>
+__device__ inline int32_t dpp_min32_step(int32_t v) {
+  return min(v, __builtin_amdgcn_update_dpp(v, v, CTRL, ROWS, 0xF, false));
+}
+
+// Wave minimum of a 64-bit value, returned as a wave-uniform value.
+__device__ inline int64_t wave_min64(int64_t v) {
+  v = dpp_min64_step<0xB1, 0xF>(v);   // quad_perm 1,0,3,2
+  v = dpp_min64_step<0x4E, 0xF>(v);   // quad_perm 2,3,0,1
+  v = dpp_min64_step<0x141, 0xF>(v);  // row_half_mirror
+  v = dpp_min64_step<0x140, 0xF>(v);  // row_mirror
+  v = dpp_min64_step<0x142, 0xA>(v);  // row_bcast:15 into rows 1, 3
+  v = dpp_min64_step<0x143, 0xC>(v);  // row_bcast:31 into rows 2, 3
+  const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)v, 63);
+  const uint32_t hi = __builtin_amdgcn_readlane((int)(v >> 32), 63);
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// Wave minimum of a 32-bit value, returned as a wave-uniform value.
+__device__ inline int32_t wave_min32(int32_t v) {
+  v = dpp_min32_step<0xB1, 0xF>(v);
+  v = dpp_min32_step<0x4E, 0xF>(v);
+  v = dpp_min32_step<0x141, 0xF>(v);
+  v = dpp_min32_step<0x140, 0xF>(v);
+  v = dpp_min32_step<0x142, 0xA>(v);
+  v = dpp_min32_step<0x143, 0xC>(v);
+  return __builtin_amdgcn_readlane(v, 63);
+}
+
+// The thread's smallest remaining candidate tick and its index (the lowest
+// index among equal ticks, so the lowest slot).
+template <int SPT>
+__device__ inline int64_t small_k_head(const int64_t (&ct)[SPT], int& hi) {
+  int64_t m = ct[0];
+  hi = 0;
+#pragma unroll
+  for (int i = 1; i < SPT; ++i)
+    if (ct[i] < m) {
+      m = ct[i];
+      hi = i;
+    }
+  return m;
+}
+
+// Victims when K is small (at most kSmallK) and each thread holds its slots'
+// ticks and occupants (sid_r) in registers: the keff least recently used
+// candidate slots by (tick, slot), in that order, straight from the ticks.
+// Each wave takes its keff smallest by repeated wave minima: the lowest lane
+// holding the minimum has the lowest slot, since a thread's slots are
+// contiguous and ascend with the thread index.  Wave 0 then merges the
+// sorted lists of all waves, ties broken by slot.  Empty slots (tick -1)
+// come first; hits and slots beyond the budget are no candidates.
+template <int SPT>
+__device__ __forceinline__ void small_k_victims(const PlanArgs& a, const int64_t (&tsr)[SPT], const int32_t* sid_r,
+                                const uint32_t* s_hitbits, int keff, int64_t (*s_wtick)[kSmallK],
+                                int32_t (*s_wslot)[kSmallK], int32_t (*s_wold)[kSmallK],
+                                int32_t* s_vic, int32_t* s_vicold) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = a.n, s0 = tid * SPT;
+  int64_t ct[SPT];
+#pragma unroll
+  for (int i = 0; i < SPT; ++i) {
+    const int s = s0 + i;
+    ct[i] = s < n && !((s_hitbits[s >> 5] >> (s & 31)) & 1u) ? tsr[i] : INT64_MAX;
+  }
+  int hi;
+  int64_t h = small_k_head<SPT>(ct, hi);
+  for (int r = 0; r < keff; ++r) {
+    const int64_t m = wave_min64(h);
+    const int win = __builtin_ctzll(__ballot(h == m));
+    if (lane == win) {
+      s_wtick[wave][r] = m;  // INT64_MAX: the wave has no candidate left
+      s_wslot[wave][r] = s0 + hi;
+      s_wold[wave][r] = sid_r[hi];
+      ct[hi] = INT64_MAX;
+      h = small_k_head<SPT>(ct, hi);
+    }
+  }
+  __syncthreads();
+  if (wave == 0) {
+    // kWaves * keff sorted entries, up to 4 per lane
+    constexpr int kPer = kWaves * kSmallK / 64;
+    const int tot = kWaves * keff;
+    int64_t et[kPer];
+    int32_t es[kPer], eo[kPer];
+#pragma unroll
+    for (int c = 0; c < kPer; ++c) {
+      const int j = lane + 64 * c;
+      const bool ok = j < tot;
+      const int w = ok ? j / keff : 0, r = ok ? j % keff : 0;
+      et[c] = ok ? s_wtick[w][r] : INT64_MAX;
+      es[c] = ok && et[c] != INT64_MAX ? s_wslot[w][r] : INT32_MAX;
+      eo[c] = ok ? s_wold[w][r] : -1;
+    }
+    for (int r = 0; r < keff; ++r) {
+      // the lane's smallest entry by (tick, slot)
+      int hc = 0;
+      int64_t ht = et[0];
+      int32_t hs = es[0];
+#pragma unroll
+      for (int c = 1; c < kPer; ++c) {
+        if (et[c] < ht || (et[c] == ht && es[c] < hs)) {
+          ht = et[c];
+          hs = es[c];
+          hc = c;
+        }
+      }
+      const int64_t mt = wave_min64(ht);
+      const int32_t ms = wave_min32(ht == mt ? hs : INT32_MAX);
+      const int win = __builtin_ctzll(__ballot(ht == mt && hs == ms));
+      if (lane == win) {
+        int32_t old = -1;
+#pragma unroll
+        for (int c = 0; c < kPer; ++c)
+          if (c == hc) {
+            old = eo[c];
+            et[c] = INT64_MAX;
+            es[c] = INT32_MAX;
+          }
+        s_vic[r] = hs;
+        s_vicold[r] = old;
+      }
+    }
+  }
+  __syncthreads();
+}
+
 template <int SPT>
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   __shared__ uint32_t s_mask[kMaxExperts / 32];
@@ -78,6 +220,9 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   __shared__ uint32_t s_prefix, s_pmask, s_kk;
   __shared__ int64_t s_tmin[kWaves], s_tmax[kWaves];
   __shared__ bool s_wempty[kWaves];
+  __shared__ int64_t s_wtick[kWaves][kSmallK];  // small K: each wave's oldest candidates
+  __shared__ int32_t s_wslot[kWaves][kSmallK];
+  __shared__ int32_t s_wold[kWaves][kSmallK];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int E = a.E, Tk = a.T * a.k, n = a.n;
@@ -186,6 +331,12 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
 #pragma unroll
       for (int i = 0; i < SPT; ++i) tsr[i] = s0 + i < n ? a.slot_ts[s0 + i] : -1;
     }
+    // small K with the slot table held in registers (pools up to 8 slots
+    // per thread): wave minima; otherwise the radix select
+    if (kHold && keff <= kSmallK) {  // uniform
+      if constexpr (kHold)
+        small_k_victims<SPT>(a, tsr, sid_r, s_hitbits, keff, s_wtick, s_wslot, s_wold, s_vic, s_vicold);
+    } else {
     int64_t tmin = INT64_MAX, tmax = -1;
     bool empty = false;
 #pragma unroll
@@ -350,6 +501,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
       s_vicold[rank] = s_selold[tid];
     }
     __syncthreads();
+    }
   }
   if (tid < a.K) pb.victims[tid] = tid < keff ? s_vic[tid] : -1;
 
