@@ -525,7 +525,9 @@ def copy_calibration():
 
 def cpu_baseline(wl, pool_np, stride, logits, xs, steps_range, budget_s):
     """The oracle as it stands (route, integer plan, fp64 expert FFN, merge),
-    on the same calls in order, until the time budget is spent."""
+    on the same calls in order, until the time budget is spent.  Beside it,
+    the oracle's plan alone (Python integers, one thread) on every call of
+    the warmup and timed steps, timed over the timed steps."""
     import numpy as np
 
     from oracle import expert as OX, layer as OY, plan as OP
@@ -537,20 +539,34 @@ def cpu_baseline(wl, pool_np, stride, logits, xs, steps_range, budget_s):
     except Exception:  # noqa: BLE001
         blas_threads = None
     cores = len(os.sched_getaffinity(0))
-    st = OP.Residency(wl.n_ids, wl.n_slots)
     K = OP.victim_bound(wl.T, wl.k, wl.E, wl.n_slots)
 
     def weights(u):
         return OX.expert_weights(pool_np[u * stride:(u + 1) * stride], wl.w_dtype, wl.H, wl.I)
 
-    calls = 0
+    # the plan alone, every call from a cold pool
+    st = OP.Residency(wl.n_ids, wl.n_slots)
+    plan_s, plan_calls = 0.0, 0
+    for s in range(steps_range.stop):
+        for l in range(wl.L):
+            ids, _ = route_topk(logits[s, l], wl.k)
+            t = time.perf_counter()
+            OP.plan(st, l, ids.tolist(), wl.E, K, wl.bw_pcie_mbps, wl.bw_host_mbps)
+            if s >= steps_range.start:
+                plan_s += time.perf_counter() - t
+                plan_calls += 1
+
+    st = OP.Residency(wl.n_ids, wl.n_slots)
+    calls, layer_s = 0, 0.0
     t0 = time.perf_counter()
     for s in steps_range:
         for l in range(wl.L):
             ids, w = route_topk(logits[s, l], wl.k)
             OP.plan(st, l, ids.tolist(), wl.E, K, wl.bw_pcie_mbps, wl.bw_host_mbps)
             x = xs(s, l)
+            t = time.perf_counter()
             OY.moe_layer(x, ids, w, l, wl.E, weights)
+            layer_s += time.perf_counter() - t
             calls += 1
             if time.perf_counter() - t0 > budget_s:
                 break
@@ -560,7 +576,10 @@ def cpu_baseline(wl, pool_np, stride, logits, xs, steps_range, budget_s):
     return dict(value=round(dt / calls * 1e6, 1), unit="us/layer", cores=cores,
                 blas_threads=blas_threads, kind="oracle",
                 sample=f"first {calls} layer calls of the timed steps (route, plan, fp64 expert "
-                       f"FFN and merge from the pinned host banks; plan state starts cold)")
+                       f"FFN and merge from the pinned host banks; plan state starts cold)",
+                plan_us_per_call=round(plan_s / max(plan_calls, 1) * 1e6, 1),
+                plan_calls=plan_calls,
+                ffn_merge_us_per_call=round(layer_s / max(calls, 1) * 1e6, 1))
 
 
 def main():
