@@ -31,7 +31,6 @@ constexpr uint32_t kSentinel = kLruNoCandidate;
 struct PlanArgs {
   const int32_t* ids;
   int32_t T, k, layer, E, K, n, mode, max_fetch;
-  int32_t umax;         // plan list bound; the FFN counters to clear
   int64_t bwp, bwh;
   int32_t* id2slot;
   int32_t* slot2id;
@@ -597,7 +596,6 @@ hipError_t launch_plan(moe_ctx* ctx, int layer, const int32_t* ids, int T, const
   K = std::min<int64_t>(K, a.n);
   if (ctx->cfg.max_fetch > 0) K = std::min<int64_t>(K, ctx->cfg.max_fetch);
   a.K = (int32_t)K;
-  a.umax = ctx->umax;
   a.mode = (!ctx->cpu_layers.empty() && ctx->cpu_layers[layer]) ? MOE_CPU : ctx->cfg.mode;
   a.max_fetch = ctx->cfg.max_fetch;
   a.bwp = ctx->cfg.bw_pcie_mbps;
