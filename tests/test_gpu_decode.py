@@ -304,3 +304,18 @@ def test_intermediate_marks_across_tick_jumps():
         log(f"  marks checked on {checked} GPU pairs over {wl.steps - 1} clock jumps")
     finally:
         g.close()
+
+
+@pytest.mark.parametrize("name,T", [("mxfp4", 4), ("f32", 3)])
+def test_token_loop_other_formats(name, T):
+    """Several tokens per call with MXFP4 (DeepSeek-shaped) and fp32 (tiny)
+    experts: the FFN kernels evaluate every routed pair of an expert from one
+    register-resident copy of its rows; every plan bit-exact, every output
+    within tolerance, filled slots byte-equal to their banks."""
+    if name == "mxfp4":
+        wl = mini(W.DSV4_MXFP4, L=2, steps=6, n_slots=56, T=T)
+    else:
+        wl = mini(W.TINY, steps=12, T=T)
+    log(f"{name} T={T}")
+    worst, n, st = run_decode(wl, check_fill=lambda s, l: True)
+    log(f"{name} T={T}: worst {worst:.3e} over {n} outputs {st}")
