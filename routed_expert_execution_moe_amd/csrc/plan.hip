@@ -127,10 +127,11 @@ __device__ inline int64_t small_k_head(const int64_t (&ct)[SPT], int& hi) {
 // sorted lists of all waves, ties broken by slot.  Empty slots (tick -1)
 // come first; hits and slots beyond the budget are no candidates.
 template <int SPT>
-__device__ __forceinline__ void small_k_victims(const PlanArgs& a, const int64_t (&tsr)[SPT], const int32_t* sid_r,
-                                const uint32_t* s_hitbits, int keff, int64_t (*s_wtick)[kSmallK],
-                                int32_t (*s_wslot)[kSmallK], int32_t (*s_wold)[kSmallK],
-                                int32_t* s_vic, int32_t* s_vicold) {
+__device__ __forceinline__ void small_k_victims(const PlanArgs& a, const int64_t (&tsr)[SPT],
+                                                const int32_t* sid_r, const uint32_t* s_hitbits, int keff,
+                                                int64_t (*s_wtick)[kSmallK], int32_t (*s_wslot)[kSmallK],
+                                                int32_t (*s_wold)[kSmallK], int32_t* s_vic,
+                                                int32_t* s_vicold) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = a.n, s0 = tid * SPT;
   int64_t ct[SPT];
