@@ -83,3 +83,39 @@ def test_large_pools_and_tick_crossing_2_32():
         assert o.st.tick > 2**32 and evictions > 0
     finally:
         g.close()
+
+
+@pytest.mark.timeout(600)
+def test_maximum_shapes():
+    """The largest shapes the configuration accepts, on small fp32 experts
+    (H = I = 64): 1,024 experts per layer, top-32, 64 tokens per call (2,048
+    routed pairs, the most the plan buffers take at this k is 4,096), so K =
+    1,024 victims: the radix select and the rank sort at their largest.  Every
+    plan and table bit-exact, outputs within tolerance."""
+    wl = dataclasses.replace(W.TINY, name="tiny-f32-max-shapes", L=3, E=1024, k=32, H=64, I=64,
+                             n_slots=2500, T=64, steps=4, seed=1779, router="zipf", zipf_s=0.8,
+                             beta=0.0, bw_pcie_mbps=1000, bw_host_mbps=2000)
+    log("maximum shapes: E=1024, k=32, T=64 (2,048 pairs), 2,500 slots")
+    g = GpuRun(wl, mode=OP.HYBRID, n_slots=wl.n_slots, max_tokens=wl.T)
+    try:
+        o = OracleRun(wl, g.bank, mode=OP.HYBRID, n_slots=wl.n_slots, max_tokens=wl.T)
+        assert o.K == 1024
+        logits = W.router_logits(wl)
+        worst = 0.0
+        for s in range(wl.steps):
+            for l in range(wl.L):
+                x = W.hidden(wl, s, l)
+                ids_g, w_g = g.decode_call(l, logits[s, l], x)
+                ids_o, w_o = o.route(logits[s, l])
+                assert np.array_equal(ids_g, ids_o), (s, l)
+                op = o.plan(l, ids_o)
+                compare_plan(g.plan_view(wl.T), op, wl.T)
+                err, _ = rel_err(g.y_f64(), o.output(l, x_f64(wl, x), ids_o, w_o))
+                worst = max(worst, err)
+                assert err <= 1e-4, (s, l, err)
+            i2s, s2i, ts, tick = g.tables()
+            assert i2s == o.st.id2slot and s2i == o.st.slot2id and ts == o.st.slot_ts, s
+            log(f"  step {s}: {len(op.uniq)} unique, {len(op.hits)} hits, q {op.q}, "
+                f"worst rel err {worst:.2e}")
+    finally:
+        g.close()
