@@ -19,10 +19,12 @@
 //     its fp32 partial rows.
 // Memory serves requests roughly in issue order, so the gate/up halves
 // finish while the down weights are still streaming and h is mostly valid
-// when a down wave gets its data.  Workgroups are dispatched in index order
-// and every gate/up item precedes every down item, so a waiting down item
-// only waits for items that are already running; the wait is still bounded
-// (wall clock) and flags an error instead of hanging.
+// when a down wave gets its data.  With one token every gate/up item comes
+// first; with more, an expert's down items follow the gate/up items of a
+// few experts later (ffn_lag).  Workgroups are dispatched in index order
+// and every down item follows all gate/up items of its own expert, so a
+// waiting down item only waits for items that are already running; the
+// wait is still bounded (wall clock) and flags an error instead of hanging.
 //
 // The intermediate crosses compute dies (each XCD has its own L2), so it
 // moves with device-coherent accesses instead of cache-wide fences.  Each
@@ -72,8 +74,12 @@ struct FfnArgs {
   uint64_t wait_ticks;
   int umax;
   int itemsA, itemsB;         // row blocks per expert
-  int blocksA;                // workgroups of gate/up items
+  int blocksA;                // workgroups of gate/up items (lag < 0)
+  int blocksAe;               // gate/up workgroups per expert (lag >= 0)
   int blocksB;                // down workgroups per expert
+  int lag;                    // < 0: all gate/up items first; else per expert, each expert's
+                              // down items after the gate/up items of the expert lag places on
+                              // (every down item still after its own expert's gate/up items)
   int cplA, cplB;             // 16-byte chunks per lane per row
 };
 
@@ -447,16 +453,69 @@ __global__ __launch_bounds__(256) void ffn_kernel(FfnArgs a) {
   // the scalar base of each load, the per-lane part in a 32-bit offset
   const int wave = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
   const int n_gpu = a.counts->n_gpu;
-  if ((int)blockIdx.x < a.blocksA) {
-    const int g = wave / a.itemsA;
-    if (g < n_gpu && g < a.umax) ffn_gate_up<WT, XT, CPLA>(a, g, wave - g * a.itemsA, lane);
-  } else {
-    // whole workgroups of one expert, four row blocks each
-    const int b = (int)blockIdx.x - a.blocksA;
-    const int g = b / a.blocksB;
-    const int rb = (b - g * a.blocksB) * 4 + (int)(threadIdx.x >> 6);
-    if (g < n_gpu && g < a.umax) ffn_down<WT, CPLB>(a, g, rb, lane, lds_h);
+  const int w4 = (int)(threadIdx.x >> 6);
+  if (a.lag < 0) {
+    if ((int)blockIdx.x < a.blocksA) {
+      const int g = wave / a.itemsA;
+      if (g < n_gpu && g < a.umax) ffn_gate_up<WT, XT, CPLA>(a, g, wave - g * a.itemsA, lane);
+    } else {
+      // whole workgroups of one expert, four row blocks each
+      const int b = (int)blockIdx.x - a.blocksA;
+      const int g = b / a.blocksB;
+      const int rb = (b - g * a.blocksB) * 4 + w4;
+      if (g < n_gpu && g < a.umax) ffn_down<WT, CPLB>(a, g, rb, lane, lds_h);
+    }
+    return;
   }
+  // per expert: the gate/up workgroups of expert j, then the down workgroups
+  // of expert j - lag; every down workgroup still follows all gate/up
+  // workgroups of its expert in dispatch order
+  const int A = a.blocksAe, Bw = a.blocksB, L = a.lag;
+  int b = (int)blockIdx.x, g, r;
+  bool up;
+  if (b < L * A) {
+    g = b / A;
+    r = b - g * A;
+    up = true;
+  } else {
+    b -= L * A;
+    const int pairs = a.umax - L;
+    if (b < pairs * (A + Bw)) {
+      const int j = b / (A + Bw);
+      r = b - j * (A + Bw);
+      up = r < A;
+      g = up ? L + j : j;
+      if (!up) r -= A;
+    } else {
+      b -= pairs * (A + Bw);
+      g = pairs + b / Bw;
+      r = b - (g - pairs) * Bw;
+      up = false;
+    }
+  }
+  if (g >= n_gpu || g >= a.umax) return;
+  const int rb = r * 4 + w4;
+  if (up) {
+    if (rb < a.itemsA) ffn_gate_up<WT, XT, CPLA>(a, g, rb, lane);
+  } else {
+    ffn_down<WT, CPLB>(a, g, rb, lane, lds_h);
+  }
+}
+
+// Dispatch order of the FFN grid (see FfnArgs::lag).  With one token the
+// grid is sized for k experts and nearly fits the chip at once: every
+// gate/up item first.  With more tokens it is several times what fits, and
+// a down item dispatched behind all gate/up items starts late; there each
+// expert's down items follow the gate/up items of the expert `lag` places
+// on, about 36 MB of gate/up weights later, so its h is mostly complete
+// when its own weights arrive.  (Measured on 8 tokens of the Qwen-shaped
+// experts, 6.3 MB of gate/up weights each: lag 0 / 2 / 4 / 6 / 8 / 16 and
+// all gate/up first gave 58.1 / 50.4 / 47.1 / 46.7 / 46.9 / 47.6 / 48.4 us.)
+inline int ffn_lag(int T, int umax, size_t gate_up_bytes) {
+  if (T == 1) return -1;
+  const size_t target = (size_t)36 << 20;
+  const int lag = (int)((target + gate_up_bytes - 1) / gate_up_bytes);
+  return std::max(1, std::min(lag, umax));
 }
 
 // chunks per lane for a row of nch 16-byte chunks (nch <= 512)
@@ -502,8 +561,13 @@ hipError_t launch_ffn_typed(moe_ctx* ctx, const void* x, int T, hipStream_t s) {
   a.itemsA = (I + rwA - 1) / rwA;
   a.itemsB = (H + rwB - 1) / rwB;
   a.blocksA = (int)(((int64_t)a.umax * a.itemsA + 3) / 4);
+  a.blocksAe = (a.itemsA + 3) / 4;
   a.blocksB = (a.itemsB + 3) / 4;
-  const dim3 grid((unsigned)(a.blocksA + (int64_t)a.umax * a.blocksB)), block(256);
+  // gate/up bytes of one expert: two matrices (and their scales)
+  a.lag = ffn_lag(T, a.umax, 2 * (a.ou - a.og) + (WT == MOE_MXFP4 ? 2 * (a.su - a.sg) : 0));
+  const int64_t nblocks = a.lag < 0 ? a.blocksA + (int64_t)a.umax * a.blocksB
+                                    : (int64_t)a.umax * (a.blocksAe + a.blocksB);
+  const dim3 grid((unsigned)nblocks), block(256);
   const size_t lds = sizeof(float) * (size_t)I;
   auto go = [&](auto xt, auto ca, auto cb) {
     hipLaunchKernelGGL((ffn_kernel<WT, decltype(xt)::value, decltype(ca)::value, decltype(cb)::value>),
