@@ -502,20 +502,40 @@ __global__ __launch_bounds__(256) void ffn_kernel(FfnArgs a) {
   }
 }
 
-// Dispatch order of the FFN grid (see FfnArgs::lag).  With one token the
-// grid is sized for k experts and nearly fits the chip at once: every
-// gate/up item first.  With more tokens it is several times what fits, and
-// a down item dispatched behind all gate/up items starts late; there each
-// expert's down items follow the gate/up items of the expert `lag` places
-// on, about 36 MB of gate/up weights later, so its h is mostly complete
-// when its own weights arrive.  (Measured on 8 tokens of the Qwen-shaped
-// experts, 6.3 MB of gate/up weights each: lag 0 / 2 / 4 / 6 / 8 / 16 and
-// all gate/up first gave 58.1 / 50.4 / 47.1 / 46.7 / 46.9 / 47.6 / 48.4 us.)
-inline int ffn_lag(int T, int umax, size_t gate_up_bytes) {
-  if (T == 1) return -1;
+// Dispatch order of the FFN grid (see FfnArgs::lag).  A grid that nearly
+// fits the chip at once (at most 1.5 times the workgroups it holds) puts
+// every gate/up item first.  A larger one would start its down items late,
+// queued behind all gate/up items; there each expert's down items follow
+// the gate/up items of the expert `lag` places on, about 36 MB of gate/up
+// weights later, so its h is mostly complete when its own weights arrive.
+// Measured: 8 tokens of the Qwen-shaped experts (6.3 MB of gate/up weights
+// each, a grid ten times what fits): lag 0 / 2 / 4 / 6 / 8 / 16 and all
+// gate/up first gave 58.1 / 50.4 / 47.1 / 46.7 / 46.9 / 47.6 / 48.4 us;
+// one token of the DeepSeek-shaped MXFP4 experts (twice what fits): lag 5
+// 20.2 us against 20.7; one token of the Qwen-shaped experts (1.25 times):
+// all gate/up first 16.5 us against 17.0 at lag 6.
+inline int ffn_lag(int64_t blocks, int64_t resident, int umax, size_t gate_up_bytes) {
+  if (2 * blocks <= 3 * resident) return -1;
   const size_t target = (size_t)36 << 20;
   const int lag = (int)((target + gate_up_bytes - 1) / gate_up_bytes);
   return std::max(1, std::min(lag, umax));
+}
+
+// Workgroups of one FFN kernel instance the device holds at once (counted
+// once per process; every device a context runs on is the same model).
+template <int WT, int XT, int CPLA, int CPLB>
+int64_t ffn_resident_blocks(size_t lds) {
+  static int64_t resident = 0;
+  if (resident == 0) {
+    int per_cu = 0, dev = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)ffn_kernel<WT, XT, CPLA, CPLB>,
+                                                     256, lds) != hipSuccess ||
+        hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return 1;  // unknown: treated as a large grid
+    resident = std::max<int64_t>(1, (int64_t)per_cu * cus);
+  }
+  return resident;
 }
 
 // chunks per lane for a row of nch 16-byte chunks (nch <= 512)
@@ -564,14 +584,15 @@ hipError_t launch_ffn_typed(moe_ctx* ctx, const void* x, int T, hipStream_t s) {
   a.blocksAe = (a.itemsA + 3) / 4;
   a.blocksB = (a.itemsB + 3) / 4;
   // gate/up bytes of one expert: two matrices (and their scales)
-  a.lag = ffn_lag(T, a.umax, 2 * (a.ou - a.og) + (WT == MOE_MXFP4 ? 2 * (a.su - a.sg) : 0));
-  const int64_t nblocks = a.lag < 0 ? a.blocksA + (int64_t)a.umax * a.blocksB
-                                    : (int64_t)a.umax * (a.blocksAe + a.blocksB);
-  const dim3 grid((unsigned)nblocks), block(256);
+  const size_t gate_up_bytes = 2 * (a.ou - a.og) + (WT == MOE_MXFP4 ? 2 * (a.su - a.sg) : 0);
+  const int64_t blocks_first = a.blocksA + (int64_t)a.umax * a.blocksB;
   const size_t lds = sizeof(float) * (size_t)I;
+  const dim3 block(256);
   auto go = [&](auto xt, auto ca, auto cb) {
-    hipLaunchKernelGGL((ffn_kernel<WT, decltype(xt)::value, decltype(ca)::value, decltype(cb)::value>),
-                       grid, block, lds, s, a);
+    constexpr int XT = decltype(xt)::value, CA = decltype(ca)::value, CB = decltype(cb)::value;
+    a.lag = ffn_lag(blocks_first, ffn_resident_blocks<WT, XT, CA, CB>(lds), a.umax, gate_up_bytes);
+    const int64_t nblocks = a.lag < 0 ? blocks_first : (int64_t)a.umax * (a.blocksAe + a.blocksB);
+    hipLaunchKernelGGL((ffn_kernel<WT, XT, CA, CB>), dim3((unsigned)nblocks), block, lds, s, a);
   };
   auto by_b = [&](auto xt, auto ca) {
     switch (a.cplB) {
