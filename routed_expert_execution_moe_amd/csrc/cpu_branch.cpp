@@ -236,8 +236,9 @@ struct HostBranch {
 
 static void poller(moe_ctx* ctx) {
   HostBranch* hb = ctx->hb;
-  // HostBlockHeader::seq, written last by the control kernel after a
-  // system-scope release; an acquire load here orders the block's reads
+  // HostBlockHeader::seq, written last by the fill launch's hand-off
+  // workgroup after a system-scope release; an acquire load here orders the
+  // block's reads
   const int64_t* bell = (const int64_t*)ctx->hstage;
   int64_t last = 0;
   int idle = 0;

@@ -352,8 +352,9 @@ extern "C" moe_status moe_create(const moe_config* cfg, void* host_pool, size_t 
   }
 #undef ALLOC
 
-  // pinned, device-mapped memory: the host block (control kernel -> host
-  // branch) and the host branch's output rows (host branch -> merge)
+  // pinned, device-mapped memory: the host block (the fill launch's hand-off
+  // workgroup -> host branch) and the host branch's output rows (host branch
+  // -> merge)
   {
     void* p = nullptr;
     size_t hb = ctx->plan.x_offset + (size_t)cfg->max_tokens * H * ctx->plan.act_bytes;

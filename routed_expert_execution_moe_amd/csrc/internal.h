@@ -163,7 +163,8 @@ struct moe_ctx {
   const float* p_cpu_dev = nullptr;
   uint64_t* h_mid = nullptr;   // device [max_tokens*k][I] {fp32 bits, tick mark}
 
-  // host block (pinned, mapped): the control kernel writes it, the host branch reads it
+  // host block (pinned, mapped): the fill launch's hand-off workgroup writes it, the
+  // host branch reads it
   uint8_t* hstage = nullptr;   // host address
   uint8_t* xstage = nullptr;   // host address of its activations copy
 
