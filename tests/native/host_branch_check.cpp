@@ -1,6 +1,7 @@
 // Drives the host branch (cpu_branch.cpp: doorbell poller + worker pool) on
 // the CPU alone, for a ThreadSanitizer build.  This program plays the part of
-// the control kernel: it writes each call's host block (header, ids, slot map,
+// the device (the fill launch's hand-off workgroup): it writes each call's host
+// block (header, ids, slot map,
 // activations) and rings the doorbell with a release store, then waits for the
 // completion word with acquire loads, as the merge kernel does, and copies out
 // the rows of the pairs assigned to the host.  Meanwhile it polls
@@ -52,7 +53,7 @@ int main(int argc, char** argv) {
   ctx->stride = (size_t)stride;
   ctx->host_pool = pool.data();
   ctx->cpu_threads = threads;
-  // host block laid out as the control kernel writes it
+  // host block laid out as the device's hand-off writes it
   const size_t hbytes = sizeof(HostBlockHeader) + 2 * 4 * (size_t)Tk;
   const size_t x_off = (hbytes + 255) / 256 * 256;
   std::vector<uint8_t> block(x_off + (size_t)T * H * ab + 256, 0);
