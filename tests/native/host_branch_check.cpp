@@ -1,11 +1,10 @@
 // Drives the host branch (cpu_branch.cpp: doorbell poller + worker pool) on
 // the CPU alone, for a ThreadSanitizer build.  This program plays the part of
 // the device (the fill launch's hand-off workgroup): it writes each call's host
-// block (header, ids, slot map,
-// activations) and rings the doorbell with a release store, then waits for the
-// completion word with acquire loads, as the merge kernel does, and copies out
-// the rows of the pairs assigned to the host.  Meanwhile it polls
-// host_branch_idle() as a resize would.
+// block (header, ids, slot map, activations) and rings the doorbell with a
+// release store, then waits for the completion word with acquire loads, as the
+// merge kernel does, and copies out the rows of the pairs assigned to the host.
+// Meanwhile it polls host_branch_idle() as a resize would.
 //
 // usage: host_branch_check IN OUT
 // IN  (little-endian): int32 L E k H I w_dtype act_dtype T n_calls threads,
