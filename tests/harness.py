@@ -47,7 +47,7 @@ def log(msg):
     sys.stdout.flush()
 
 
-class GpuRun:
+class DeviceRun:
     """One context on cuda:0 with the workload's host pool."""
 
     def __init__(self, wl: W.Workload, mode=0, n_slots=None, max_slots=None, cpu_threads=0,

@@ -9,14 +9,14 @@ import numpy as np
 import pytest
 
 import workload as W
-from tests.harness import GpuRun, OracleRun, compare_plan, log, rel_err, x_f64
+from tests.harness import DeviceRun, OracleRun, compare_plan, log, rel_err, x_f64
 
 pytestmark = pytest.mark.gpu
 
 
 def test_measure_then_decode_with_measured_split():
     wl = dataclasses.replace(W.QWEN_BF16, L=4, steps=8, n_slots=189)
-    g = GpuRun(wl)
+    g = DeviceRun(wl)
     try:
         B = g.B
         logits = W.router_logits(wl)

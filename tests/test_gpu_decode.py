@@ -12,7 +12,7 @@ import numpy as np
 import pytest
 
 import workload as W
-from tests.harness import (GpuRun, OracleRun, bf16_round_err, compare_plan, d2h, h2d, log, rel_err,
+from tests.harness import (DeviceRun, OracleRun, bf16_round_err, compare_plan, d2h, h2d, log, rel_err,
                            x_f64)
 
 pytestmark = pytest.mark.gpu
@@ -23,7 +23,7 @@ TOL = {"f32": 1e-4, "bf16": 2e-2, "mxfp4": 2e-2}
 def run_decode(wl, mode=0, check_output=lambda s, l: True, check_fill=lambda s, l: False,
                resize=None, n_slots=None, max_fetch=0):
     resize = wl.resize if resize is None else resize
-    g = GpuRun(wl, mode=mode, n_slots=n_slots, max_fetch=max_fetch)
+    g = DeviceRun(wl, mode=mode, n_slots=n_slots, max_fetch=max_fetch)
     try:
         o = OracleRun(wl, g.bank, mode=mode, n_slots=n_slots, max_fetch=max_fetch)
         logits = W.router_logits(wl)
@@ -151,7 +151,7 @@ def test_cpu_layers_bf16():
     per-layer modes, outputs within tolerance, and no expert of a host layer
     ever admitted.  Switching the flags off mid-run lets those layers fill."""
     wl = mini(W.QWEN_BF16, L=4, steps=12, n_slots=189)
-    g = GpuRun(wl)
+    g = DeviceRun(wl)
     try:
         o = OracleRun(wl, g.bank)
         logits = W.router_logits(wl)
@@ -195,7 +195,7 @@ def test_repeated_expert_in_a_token(T):
     pair's partial rows equal to its first occurrence's.  T = 1 runs the
     single-pair FFN kernel, T = 3 the token loop."""
     wl = mini(W.QWEN_BF16, L=2, steps=6, n_slots=40, T=T)
-    g = GpuRun(wl)
+    g = DeviceRun(wl)
     torch = g.torch
     try:
         o = OracleRun(wl, g.bank)
@@ -250,7 +250,7 @@ def test_intermediate_marks_across_tick_jumps():
     the oracle."""
     from oracle import expert as OX
     wl = mini(W.QWEN_BF16, L=2, steps=6, n_slots=189)
-    g = GpuRun(wl)
+    g = DeviceRun(wl)
     try:
         o = OracleRun(wl, g.bank)
         logits = W.router_logits(wl)

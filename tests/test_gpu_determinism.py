@@ -14,7 +14,7 @@ import numpy as np
 import pytest
 
 import workload as W
-from tests.harness import GpuRun, log
+from tests.harness import DeviceRun, log
 
 pytestmark = pytest.mark.gpu
 
@@ -22,7 +22,7 @@ pytestmark = pytest.mark.gpu
 def record_decode(wl, resize=None):
     """Every call's output bits, plan view and tables, in call order."""
     resize = resize or {}
-    g = GpuRun(wl)
+    g = DeviceRun(wl)
     out = []
     try:
         logits = W.router_logits(wl)
@@ -69,7 +69,7 @@ def test_decode_runs_bit_identical(case):
 def test_prefill_chunk_bit_identical():
     import torch
     wl = dataclasses.replace(W.DSV4_PREFILL, L=3, E=16, k=4, H=512, I=512, T=777, n_slots=40)
-    g = GpuRun(wl, n_slots=wl.n_slots, max_tokens=8, max_prefill_tokens=wl.T)
+    g = DeviceRun(wl, n_slots=wl.n_slots, max_tokens=8, max_prefill_tokens=wl.T)
     try:
         dev = g.dev
         ids = torch.empty((wl.T, wl.k), dtype=torch.int32, device=dev)

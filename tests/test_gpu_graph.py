@@ -16,7 +16,7 @@ import numpy as np
 import pytest
 
 import workload as W
-from tests.harness import GpuRun, OracleRun, compare_plan, log, rel_err, x_f64
+from tests.harness import DeviceRun, OracleRun, compare_plan, log, rel_err, x_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -25,7 +25,7 @@ TOL = {"f32": 1e-4, "bf16": 2e-2, "mxfp4": 2e-2}
 
 def _graph_steps(wl, eager_steps):
     import torch
-    g = GpuRun(wl)
+    g = DeviceRun(wl)
     try:
         B = g.B
         o = OracleRun(wl, g.bank)

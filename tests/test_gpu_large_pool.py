@@ -21,7 +21,7 @@ import pytest
 
 import workload as W
 from oracle import plan as OP
-from tests.harness import GpuRun, OracleRun, compare_plan, d2h, h2d, log, rel_err, x_f64
+from tests.harness import DeviceRun, OracleRun, compare_plan, d2h, h2d, log, rel_err, x_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -33,7 +33,7 @@ def test_large_pools_and_tick_crossing_2_32():
                              beta=0.0, bw_pcie_mbps=1000, bw_host_mbps=2000)
     schedule = {1: 12_000, 2: 20_000}
     log("large pools: 160 layers x 128 experts (f32, H=I=64), T=32, slots 5000 -> 12000 -> 20000")
-    g = GpuRun(wl, mode=OP.OFFLOAD, n_slots=wl.n_slots, max_slots=20_000, max_tokens=wl.T)
+    g = DeviceRun(wl, mode=OP.OFFLOAD, n_slots=wl.n_slots, max_slots=20_000, max_tokens=wl.T)
     try:
         o = OracleRun(wl, g.bank, mode=OP.OFFLOAD, n_slots=wl.n_slots, max_tokens=wl.T)
         logits = W.router_logits(wl)
@@ -96,7 +96,7 @@ def test_maximum_shapes():
                              n_slots=2500, T=64, steps=4, seed=1779, router="zipf", zipf_s=0.8,
                              beta=0.0, bw_pcie_mbps=1000, bw_host_mbps=2000)
     log("maximum shapes: E=1024, k=32, T=64 (2,048 pairs), 2,500 slots")
-    g = GpuRun(wl, mode=OP.HYBRID, n_slots=wl.n_slots, max_tokens=wl.T)
+    g = DeviceRun(wl, mode=OP.HYBRID, n_slots=wl.n_slots, max_tokens=wl.T)
     try:
         o = OracleRun(wl, g.bank, mode=OP.HYBRID, n_slots=wl.n_slots, max_tokens=wl.T)
         assert o.K == 1024

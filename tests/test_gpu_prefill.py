@@ -19,7 +19,7 @@ import pytest
 
 import workload as W
 from oracle import layer as OY, plan as OP
-from tests.harness import (GpuRun, OracleRun, bf16_round_err, check_grouping, compare_plan, log,
+from tests.harness import (DeviceRun, OracleRun, bf16_round_err, check_grouping, compare_plan, log,
                            rel_err, x_f64)
 
 pytestmark = pytest.mark.gpu
@@ -30,7 +30,7 @@ def run_prefill(wl, sample_tokens=None, check_bytes=True, decode_after=False, bu
     """buffers x E > n_slots runs the on-demand fallback (checked against the
     oracle's on-demand admission, pass by pass through the final tables)."""
     import torch
-    g = GpuRun(wl, n_slots=wl.n_slots, max_tokens=8, max_prefill_tokens=wl.T)
+    g = DeviceRun(wl, n_slots=wl.n_slots, max_tokens=8, max_prefill_tokens=wl.T)
     try:
         if buffers != 2:
             g.B.moe_prefill_set_buffers(g.ctx, buffers)
@@ -153,7 +153,7 @@ def test_prefill_full():
     wl = W.DSV4_PREFILL
     n_od = W.DSV4_MXFP4.n_slots
     log("prefill full: 8 layers x 8192 tokens, E=256, H=4096, I=2048, n=512, then n=225 on demand")
-    g = GpuRun(wl, n_slots=wl.n_slots, max_tokens=8, max_prefill_tokens=wl.T)
+    g = DeviceRun(wl, n_slots=wl.n_slots, max_tokens=8, max_prefill_tokens=wl.T)
     try:
         o = OracleRun(wl, g.bank, n_slots=wl.n_slots, max_tokens=8)
         dev = g.dev
@@ -251,7 +251,7 @@ def test_prefill_then_resize_with_pending_slab():
     import torch
     wl = dataclasses.replace(W.DSV4_PREFILL, L=4, E=16, k=4, H=512, I=512, T=200, n_slots=40)
     log("prefill then resize with a pending slab: L=4 E=16 k=4 H=512 I=512 T=200 n=40")
-    g = GpuRun(wl, n_slots=wl.n_slots, max_slots=64, max_tokens=8, max_prefill_tokens=wl.T)
+    g = DeviceRun(wl, n_slots=wl.n_slots, max_slots=64, max_tokens=8, max_prefill_tokens=wl.T)
     try:
         o = OracleRun(wl, g.bank, n_slots=wl.n_slots, max_tokens=8)
         dev = g.dev
@@ -316,7 +316,7 @@ def test_prefill_two_buffers_cache_hits():
     import torch
     wl = dataclasses.replace(W.DSV4_PREFILL, L=3, E=16, k=4, H=512, I=512, T=333, n_slots=48)
     log("two-buffer prefill after decode: L=3 E=16 k=4 H=512 I=512 T=333 n=48")
-    g = GpuRun(wl, n_slots=wl.n_slots, max_tokens=8, max_prefill_tokens=wl.T)
+    g = DeviceRun(wl, n_slots=wl.n_slots, max_tokens=8, max_prefill_tokens=wl.T)
     try:
         o = OracleRun(wl, g.bank, n_slots=wl.n_slots, max_tokens=8)
         dl = dataclasses.replace(wl, T=1, steps=16, prefill=False)
@@ -388,7 +388,7 @@ def test_prefill_on_demand_cache_hits():
     import torch
     wl = dataclasses.replace(W.DSV4_PREFILL, L=2, E=16, k=4, H=512, I=512, T=333, n_slots=24)
     log("prefill on demand after decode: L=2 E=16 k=4 H=512 I=512 T=333 n=24")
-    g = GpuRun(wl, n_slots=wl.n_slots, max_tokens=8, max_prefill_tokens=wl.T)
+    g = DeviceRun(wl, n_slots=wl.n_slots, max_tokens=8, max_prefill_tokens=wl.T)
     try:
         o = OracleRun(wl, g.bank, n_slots=wl.n_slots, max_tokens=8)
         dl = dataclasses.replace(wl, T=1, steps=12, prefill=False)

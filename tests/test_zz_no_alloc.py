@@ -17,7 +17,7 @@ import pytest
 
 import workload as W
 from oracle import layer as OY
-from tests.harness import GpuRun, OracleRun, d2h, log, rel_err, x_f64
+from tests.harness import DeviceRun, OracleRun, d2h, log, rel_err, x_f64
 
 pytestmark = pytest.mark.gpu
 TOL = 2e-2
@@ -34,7 +34,7 @@ def grouping(B, ctx, E, Tk):
 
 def run_case(wl, n_slots, Ts, max_T, with_oracle):
     import torch
-    g = GpuRun(wl, n_slots=n_slots, max_tokens=8, max_prefill_tokens=max_T)
+    g = DeviceRun(wl, n_slots=n_slots, max_tokens=8, max_prefill_tokens=max_T)
     B = g.B
     ctx_b = None
     try:
