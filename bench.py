@@ -131,6 +131,8 @@ def parse():
     ap.add_argument("--mode", default="hybrid", choices=["hybrid", "offload", "cpu"])
     ap.add_argument("--cpu-baseline-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-mxfp4", action="store_true",
+                    help="leave out the DeepSeek-shaped MXFP4 decode leg")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-elastic", action="store_true", help="skip the resize-schedule leg")
     ap.add_argument("--max-fetch", type=int, default=0,
@@ -437,6 +439,85 @@ def bench_streams(steps=64, warmup=8):
             "fills_per_layer": round((st_b.fills - st_a.fills) / max(timed_layers, 1), 3),
             "cpu_experts_per_layer": round((st_b.cpu - st_a.cpu) / max(timed_layers, 1), 3),
             "resizes": resizes, "host_pool_unchanged": checksum() == ck0,
+        }
+    finally:
+        if ctx:
+            B.moe_destroy(ctx)
+        B.moe_host_pool_free(pool)
+
+
+def bench_mxfp4_decode(steps=60, warmup=8):
+    """The DeepSeek-V4-Flash-shaped MXFP4 decode workload (8 of its layers,
+    256 experts, 225 slots, one token per call) on its own context and host
+    pool: `warmup` untimed steps, then `steps` timed ones with per-phase HIP
+    events (control kernel, fill, FFN, merge) and the FFN's HBM rate over the
+    same algorithmic bytes as the headline line (unique GPU experts' weights,
+    activations, partial rows and the fp32 intermediate)."""
+    import numpy as np
+    import torch
+
+    import routed_expert_execution_moe_amd as B
+    import workload as W
+
+    wl = W.DSV4_MXFP4
+    dev = torch.device("cuda:0")
+    n_run = warmup + steps
+    cfg = B.config(wl.L, wl.E, wl.k, wl.H, wl.I, wl.w_dtype, wl.act_dtype, wl.n_slots,
+                   max_tokens=wl.T, bw_pcie_mbps=wl.bw_pcie_mbps, bw_host_mbps=wl.bw_host_mbps,
+                   timing=1)
+    stride = B.moe_expert_bytes(cfg)
+    pool_bytes = wl.n_ids * stride
+    pool = B.moe_host_pool_alloc(pool_bytes)
+    ctx = None
+    try:
+        W.fill_banks(wl, pool, 0, wl.n_ids)
+        logits = W.decode_logits(wl, steps=n_run)
+        lg_d = torch.from_numpy(np.ascontiguousarray(logits)).to(dev)
+        xs = np.stack([np.stack([W.hidden(wl, s, l) for l in range(wl.L)]) for s in range(n_run)])
+        x_d = torch.from_numpy(xs.view(np.int16)).to(dev).view(torch.bfloat16)
+        ids = torch.empty((wl.L, wl.T, wl.k), dtype=torch.int32, device=dev)
+        w = torch.empty((wl.L, wl.T, wl.k), dtype=torch.float32, device=dev)
+        y = torch.empty((wl.L, wl.T, wl.H), dtype=torch.bfloat16, device=dev)
+        ctx = B.moe_create(cfg, pool, pool_bytes)
+
+        def step(s):
+            for l in range(wl.L):
+                B.moe_route_topk(ctx, lg_d[s, l], wl.T, ids[l], w[l])
+                B.moe_cache_plan(ctx, l, ids[l], wl.T, x_d[s, l])
+                B.moe_expert_ffn(ctx, l, x_d[s, l], wl.T)
+                B.moe_merge(ctx, w[l], wl.T, y[l])
+
+        for s in range(warmup):
+            step(s)
+        torch.cuda.synchronize()
+        B.moe_ctx_timing(ctx, reset=True)
+        st_a = B.moe_ctx_stats(ctx)
+        t0 = time.perf_counter()
+        for s in range(warmup, n_run):
+            step(s)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        tm = B.moe_ctx_timing(ctx)
+        st_b = B.moe_ctx_stats(ctx)
+        calls = steps * wl.L
+        gpu_experts = (st_b.hits - st_a.hits) + (st_b.fills - st_a.fills)
+        # one token a call: each GPU expert serves one (token, expert) pair
+        ffn_bytes = (gpu_experts * W.expert_bytes(wl) + calls * wl.T * wl.H * 2
+                     + gpu_experts * (wl.H * 4 + 2 * wl.I * 4))
+        per = {k: (round(v["ms"] * 1e3 / v["calls"], 2) if v["calls"] else None) for k, v in tm.items()}
+        ffn_gbps = ffn_bytes / (tm["ffn"]["ms"] * 1e-3) / 1e9 if tm["ffn"]["ms"] else None
+        acc = gpu_experts + (st_b.cpu - st_a.cpu)
+        return {
+            "workload": wl.name, "tokens_per_call": wl.T, "steps": steps, "warmup": warmup,
+            "us_per_layer": round(wall / calls * 1e6, 2),
+            "control_kernel_us": per.get("plan"), "ffn_us": per.get("ffn"), "fill_us": per.get("fill"),
+            "merge_us": per.get("merge"), "route_us": per.get("route"),
+            "ffn_algorithmic_bytes_per_launch": round(ffn_bytes / calls),
+            "ffn_gbps": round(ffn_gbps, 1) if ffn_gbps else None,
+            "ffn_frac_of_hbm": round(ffn_gbps / HBM_PEAK_GBPS, 4) if ffn_gbps else None,
+            "miss_rate": round(1 - (st_b.hits - st_a.hits) / max(acc, 1), 4),
+            "fills_per_layer": round((st_b.fills - st_a.fills) / calls, 3),
+            "cpu_experts_per_layer": round((st_b.cpu - st_a.cpu) / calls, 3),
         }
     finally:
         if ctx:
@@ -872,6 +953,8 @@ def main():
     B.moe_host_pool_free(pool)
     if not a.no_streams:
         out["streams_8"] = bench_streams()
+    if not a.no_mxfp4:
+        out["mxfp4_decode"] = bench_mxfp4_decode()
     if not a.no_prefill:
         out.update(bench_prefill())
     print(json.dumps(out), flush=True)
