@@ -43,9 +43,10 @@
 // MXFP4 weights are expanded with the gfx950 scaled FP4 converts (to bf16
 // pairs against bf16 activations, to fp32 pairs against fp32 inputs), the
 // E8M0 scale applied in the convert; everything accumulates in fp32.  Row
-// totals use a transpose reduction: at each xor step a lane keeps half of its
-// values and sends the other half, so R rows cost R - 1 + 6 - log2(R)
-// shuffles instead of 6 R.
+// totals use a transpose reduction: at each cross-lane step a lane keeps half
+// of its values and takes the partner's copy of that half, so R rows cost
+// R - 1 + 6 - log2(R) lane moves instead of 6 R; the moves are DPP and the
+// gfx950 lane swaps, not LDS permutes.
 #pragma once
 
 #include <algorithm>
@@ -216,23 +217,58 @@ __device__ inline float ffn_dot(const WChunk16& c, const XWords<WT, XT>& x, floa
   return acc;
 }
 
+// Cross-lane steps of the row reduction, all in the vector ALU (an LDS
+// permute per step would put a round trip through the LDS unit on every
+// step of the tail of the launch).
+//
+// x of the lane paired with this one at step O = 1, 2, 4, 8 (DPP within a
+// row of 16): xor 1 and xor 2 by quad permutes, 4 and 8 by the half-row and
+// row mirrors, which pair each lane with one whose bit O differs.
+template <int O>
+__device__ inline float ffn_dpp_pair(float x) {
+  constexpr int ctrl = O == 1 ? 0xB1 : O == 2 ? 0x4E : O == 4 ? 0x141 : 0x140;
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), ctrl, 0xF, 0xF, false));
+}
+
+// Step O = 16 or 32 by the gfx950 row / half-wave swaps: lanes whose bit O is
+// clear get the pair's sum of a, lanes whose bit O is set the pair's sum of b.
+template <int O>
+__device__ inline float ffn_swap_sum(float a, float b) {
+  const uint32_t ua = __float_as_uint(a), ub = __float_as_uint(b);
+  if constexpr (O == 32) {
+    const auto r = __builtin_amdgcn_permlane32_swap(ua, ub, false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  } else {
+    const auto r = __builtin_amdgcn_permlane16_swap(ua, ub, false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+}
+
 // Transpose reduction of N values across the wave (N a power of two <= 64),
-// starting at xor offset O.  Afterwards lane l holds the wave total of value
-// l >> (6 - log2 N) in v[0].
-template <int N>
-__device__ inline void ffn_xreduce(float* v, int lane, int o) {
+// steps O = 32, 16, ..., 1: at each a lane keeps the half of its values that
+// its bit O selects and adds the partner's copy of that half.  Afterwards
+// lane l holds the wave total of value l >> (6 - log2 N) in v[0].
+template <int N, int O = 32>
+__device__ inline void ffn_xreduce(float* v, int lane) {
   if constexpr (N > 1) {
     constexpr int HN = N / 2;
-    const bool up = (lane & o) != 0;
+    if constexpr (O >= 16) {
 #pragma unroll
-    for (int i = 0; i < HN; ++i) {
-      const float send = up ? v[i] : v[i + HN];
-      const float keep = up ? v[i + HN] : v[i];
-      v[i] = keep + __shfl_xor(send, o);
+      for (int i = 0; i < HN; ++i) v[i] = ffn_swap_sum<O>(v[i], v[i + HN]);
+    } else {
+      const bool up = (lane & O) != 0;
+#pragma unroll
+      for (int i = 0; i < HN; ++i) {
+        const float send = up ? v[i] : v[i + HN];
+        const float keep = up ? v[i + HN] : v[i];
+        v[i] = keep + ffn_dpp_pair<O>(send);
+      }
     }
-    ffn_xreduce<HN>(v, lane, o >> 1);
-  } else {
-    for (; o >= 1; o >>= 1) v[0] += __shfl_xor(v[0], o);
+    ffn_xreduce<HN, O / 2>(v, lane);
+  } else if constexpr (O >= 1) {
+    if constexpr (O >= 16) v[0] = ffn_swap_sum<O>(v[0], v[0]);
+    else v[0] += ffn_dpp_pair<O>(v[0]);
+    ffn_xreduce<1, O / 2>(v, lane);
   }
 }
 
@@ -319,8 +355,10 @@ __device__ void ffn_gate_up(const FfnArgs& a, int g, int rb, int lane) {
         v[RW + r] = ffn_dot<WT, XT>(wu[r][c], xw[c], v[RW + r]);
       }
     // gate totals land in lanes 0..31, up totals in lanes 32..63
-    ffn_xreduce<2 * RW>(v, lane, 32);
-    const float up = __shfl_xor(v[0], 32);
+    ffn_xreduce<2 * RW>(v, lane);
+    // lane l < 32 takes lane l + 32's value
+    const float up = __uint_as_float(
+        __builtin_amdgcn_permlane32_swap(__float_as_uint(v[0]), __float_as_uint(v[0]), false, false)[1]);
     constexpr int SH = 6 - Log2<2 * RW>::v;
     const int r = lane >> SH;
     if (lane < 32 && (lane & ((1 << SH) - 1)) == 0 && row0 + r < a.I)
@@ -446,7 +484,7 @@ __device__ void ffn_down(const FfnArgs& a, int g, int rb, int lane, float* lds_h
 #pragma unroll
       for (int r = 0; r < RW; ++r) v[r] = ffn_dot<WT, MOE_F32>(wd[r][c], hw, v[r]);
     }
-    ffn_xreduce<RW>(v, lane, 32);
+    ffn_xreduce<RW>(v, lane);
     constexpr int SH = 6 - Log2<RW>::v;
     const int r = lane >> SH;
     if ((lane & ((1 << SH) - 1)) == 0 && row0 + r < a.H) a.p[(size_t)p * a.H + row0 + r] = v[0];
