@@ -89,9 +89,15 @@ template <> struct FfnChunk<MOE_F32> { static constexpr int CH = 4; };
 template <> struct FfnChunk<MOE_BF16> { static constexpr int CH = 8; };
 template <> struct FfnChunk<MOE_MXFP4> { static constexpr int CH = 32; };
 
-// chunk slots per lane: gate/up items hold kRegA per matrix, down items kRegB
-constexpr int kRegA = 8;
-template <int WT> struct FfnRegB { static constexpr int N = WT == MOE_MXFP4 ? 8 : 16; };
+// chunk slots per lane: gate/up items hold FfnRegA per matrix, down items
+// FfnRegB; rows per wave = slots / chunks per lane of a row, at least one.
+// bf16 / fp32: eight loads of 16 B in flight per lane per item, whose
+// smaller items leave less arithmetic on the tail of the launch than
+// sixteen.  MXFP4 keeps sixteen for gate/up: its kernel's registers are set
+// by the FP4 converts, so smaller items bring no more waves per SIMD.
+template <int WT> struct FfnRegA { static constexpr int N = WT == MOE_MXFP4 ? 8 : 4; };
+template <int WT> struct FfnRegB { static constexpr int N = 8; };
+__host__ __device__ constexpr int ffn_rows(int slots, int cpl) { return slots / cpl > 0 ? slots / cpl : 1; }
 
 __device__ inline float ffn_bf_lo(uint32_t v) { return __uint_as_float(v << 16); }
 __device__ inline float ffn_bf_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
@@ -293,7 +299,7 @@ __device__ inline float ffn_silu(float g) { return g / (1.f + expf(-g)); }
 template <int WT, int XT, int CPL>
 __device__ void ffn_gate_up(const FfnArgs& a, int g, int rb, int lane) {
   constexpr int CH = FfnChunk<WT>::CH;
-  constexpr int RW = kRegA / CPL;
+  constexpr int RW = ffn_rows(FfnRegA<WT>::N, CPL);
   const int K = a.H, nch = K / CH, row0 = rb * RW;
   const uint64_t mark = (uint64_t)(uint32_t)a.counts->tick_lo << 32;
 
@@ -420,7 +426,7 @@ __device__ inline void ffn_collect_h(const FfnArgs& a, int p, int K, uint32_t wa
 template <int WT, int CPL>
 __device__ void ffn_down(const FfnArgs& a, int g, int rb, int lane, float* lds_h) {
   constexpr int CH = FfnChunk<WT>::CH;
-  constexpr int RW = FfnRegB<WT>::N / CPL;
+  constexpr int RW = ffn_rows(FfnRegB<WT>::N, CPL);
   typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
   const uint32_t want = (uint32_t)a.counts->tick_lo;
   const int sm0 = lane < a.Tk ? a.slot_map[lane] : -2;
@@ -550,20 +556,21 @@ __global__ __launch_bounds__(256) void ffn_kernel(FfnArgs a) {
   }
 }
 
-// Dispatch order of the FFN grid (see FfnArgs::lag).  A grid that nearly
-// fits the chip at once (at most 1.5 times the workgroups it holds) puts
-// every gate/up item first.  A larger one would start its down items late,
-// queued behind all gate/up items; there each expert's down items follow
-// the gate/up items of the expert `lag` places on, about 36 MB of gate/up
-// weights later, so its h is mostly complete when its own weights arrive.
-// Measured: 8 tokens of the Qwen-shaped experts (6.3 MB of gate/up weights
-// each, a grid ten times what fits): lag 0 / 2 / 4 / 6 / 8 / 16 and all
-// gate/up first gave 58.1 / 50.4 / 47.1 / 46.7 / 46.9 / 47.6 / 48.4 us;
-// one token of the DeepSeek-shaped MXFP4 experts (twice what fits): lag 5
-// 20.2 us against 20.7; one token of the Qwen-shaped experts (1.25 times):
-// all gate/up first 16.5 us against 17.0 at lag 6.
+// Dispatch order of the FFN grid (see FfnArgs::lag).  A grid smaller than
+// twice the workgroups the chip holds at once puts every gate/up item
+// first.  A larger one would start its down items late, queued behind all
+// gate/up items; there each expert's down items follow the gate/up items of
+// the expert `lag` places on, about 36 MB of gate/up weights later, so its h
+// is mostly complete when its own weights arrive.  Measured: 8 tokens of the
+// Qwen-shaped experts (6.3 MB of gate/up weights each, a grid about ten
+// times what fits): lag 0 / 2 / 4 / 6 / 8 / 16 and all gate/up first gave
+// 58.1 / 50.4 / 47.1 / 46.7 / 46.9 / 47.6 / 48.4 us; one token of the
+// DeepSeek-shaped MXFP4 experts (2,048 workgroups, twice what fits): lag 5
+// 20.2 us against 20.7; one token of the Qwen-shaped experts (2,560
+// workgroups, 1,792 resident): all gate/up first 15.8 us against 16.3 at
+// lag 6.
 inline int ffn_lag(int64_t blocks, int64_t resident, int umax, size_t gate_up_bytes) {
-  if (2 * blocks <= 3 * resident) return -1;
+  if (blocks < 2 * resident) return -1;
   const size_t target = (size_t)36 << 20;
   const int lag = (int)((target + gate_up_bytes - 1) / gate_up_bytes);
   return std::max(1, std::min(lag, umax));
@@ -625,7 +632,7 @@ hipError_t launch_ffn_typed(moe_ctx* ctx, const void* x, int T, hipStream_t s) {
   a.umax = ctx->umax;
   a.cplA = ffn_cpl(H / CH);
   a.cplB = ffn_cpl(I / CH);
-  const int rwA = kRegA / a.cplA, rwB = FfnRegB<WT>::N / a.cplB;
+  const int rwA = ffn_rows(FfnRegA<WT>::N, a.cplA), rwB = ffn_rows(FfnRegB<WT>::N, a.cplB);
   a.itemsA = (I + rwA - 1) / rwA;
   a.itemsB = (H + rwB - 1) / rwB;
   a.blocksA = (int)(((int64_t)a.umax * a.itemsA + 3) / 4);
