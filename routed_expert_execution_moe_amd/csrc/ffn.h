@@ -19,9 +19,9 @@
 //     its fp32 partial rows.
 // Memory serves requests roughly in issue order, so the gate/up halves
 // finish while the down weights are still streaming and h is mostly valid
-// when a down wave gets its data.  With one token every gate/up item comes
-// first; with more, an expert's down items follow the gate/up items of a
-// few experts later (ffn_lag).  Workgroups are dispatched in index order
+// when a down wave gets its data.  A grid the chip nearly holds at once
+// puts every gate/up item first; in a larger one an expert's down items
+// follow the gate/up items of a few experts later (ffn_lag).  Workgroups are dispatched in index order
 // and every down item follows all gate/up items of its own expert, so a
 // waiting down item only waits for items that are already running; the
 // wait is still bounded (wall clock) and flags an error instead of hanging.
