@@ -95,6 +95,20 @@ def test_mxfp4_mini_every_call(mode):
     log(f"mxfp4 mini mode={mode}: worst {worst:.3e} over {n} outputs {st}")
 
 
+@pytest.mark.parametrize("T", [1, 3])
+def test_bf16_partial_chunk_columns(T):
+    """bf16 experts whose rows leave the last 64-lane column of 16-byte
+    chunks partly empty in both halves of the FFN: H = 576 (72 chunks of a
+    W_gate / W_up row, two per lane, gate/up items of two rows) and I = 320
+    (40 chunks of a W_down row, one per lane, lanes 40-63 idle, down items of
+    eight rows), at one and three tokens per call.  Every plan bit-exact,
+    every output within tolerance, filled slots byte-equal to their banks."""
+    wl = mini(W.QWEN_BF16, L=2, steps=8, n_slots=60, H=576, I=320, T=T)
+    log(f"bf16 H=576 I=320 T={T}")
+    worst, n, st = run_decode(wl, check_fill=lambda s, l: True)
+    log(f"bf16 H=576 I=320 T={T}: worst {worst:.3e} over {n} outputs {st}")
+
+
 def test_bf16_streams_mini_with_resizes():
     wl = mini(W.QWEN_ELASTIC, L=3, steps=24, n_slots=141, resize={6: 57, 12: 115, 18: 115})
     log("bf16 8-stream mini")
