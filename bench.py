@@ -13,7 +13,8 @@ router logits and hidden states are resident in HBM before timing starts.
 Prints one JSON line: value = MoE-layer decode time in microseconds per layer
 (wall clock over the timed steps, bracketed by device synchronisation), plus
 the roofline of the expert FFN (HBM bytes of the unique GPU-resident experts
-per launch over its HIP-event duration), a per-phase breakdown and the CPU
+per launch over its duration, from HIP events the launch binds to its own
+dispatch), a per-phase breakdown and the CPU
 oracle timed on a bounded sample of the same calls.
 """
 from __future__ import annotations
@@ -932,6 +933,8 @@ def main():
             "traffic": recorded_traffic("decode_ffn", wl.name),
             "traffic_source": traffic_source("decode_ffn", wl.name),
             "algorithmic_bytes_per_launch": round(ffn_bytes / calls),
+            "timing": "HIP events bound to each FFN launch's dispatch (hipExtLaunchKernelGGL start and stop "
+                      "events): the kernel's own start to end on its stream, averaged over the timed steps",
         },
         "cpu_baseline": cpu,
         "breakdown_us_per_call": per,

@@ -521,6 +521,27 @@ hipError_t moert::timing_begin(moe_ctx* ctx, int phase, hipStream_t s) {
   return hipEventRecord(T.a[T.head], s);
 }
 
+hipError_t moert::timing_pair(moe_ctx* ctx, int phase, hipEvent_t* ev0, hipEvent_t* ev1) {
+  *ev0 = *ev1 = nullptr;
+  if (!ctx->timing) return hipSuccess;
+  Timing& T = *ctx->timing;
+  if (T.used == Timing::kRing) {
+    hipError_t e = timing_harvest_one(T);
+    if (e != hipSuccess) return e;
+  }
+  T.phase[T.head] = phase;
+  *ev0 = T.a[T.head];
+  *ev1 = T.b[T.head];
+  return hipSuccess;
+}
+
+void moert::timing_commit(moe_ctx* ctx) {
+  if (!ctx->timing) return;
+  Timing& T = *ctx->timing;
+  T.head = (T.head + 1) % Timing::kRing;
+  T.used += 1;
+}
+
 hipError_t moert::timing_end(moe_ctx* ctx, hipStream_t s) {
   if (!ctx->timing) return hipSuccess;
   Timing& T = *ctx->timing;
@@ -616,9 +637,13 @@ extern "C" moe_status moe_expert_ffn(moe_ctx* ctx, int32_t layer, const void* x,
   if (!x || ctx->state != kPlanned || layer != ctx->cur_layer || T != ctx->cur_T)
     return fail(ctx, MOE_EINVAL, "moe_expert_ffn: must follow moe_cache_plan of the same layer and T");
   if ((uintptr_t)x & 15) return fail(ctx, MOE_EINVAL, "moe_expert_ffn: x must be 16-byte aligned");
-  MOE_HIP(ctx, timing_begin(ctx, MOE_T_FFN, (hipStream_t)stream));
-  MOE_HIP(ctx, launch_ffn(ctx, x, T, (hipStream_t)stream));
-  MOE_HIP(ctx, timing_end(ctx, (hipStream_t)stream));
+  // timed by events bound to the kernel's own dispatch (its start and end),
+  // not recorded around it on the stream
+  MOE_HIP(ctx, timing_pair(ctx, MOE_T_FFN, &ctx->ffn_ev[0], &ctx->ffn_ev[1]));
+  const hipError_t le = launch_ffn(ctx, x, T, (hipStream_t)stream);
+  ctx->ffn_ev[0] = ctx->ffn_ev[1] = nullptr;
+  MOE_HIP(ctx, le);
+  timing_commit(ctx);
   ctx->state = kEvaluated;
   return MOE_OK;
 }

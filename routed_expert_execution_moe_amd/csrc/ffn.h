@@ -49,6 +49,8 @@
 // gfx950 lane swaps, not LDS permutes.
 #pragma once
 
+#include <hip/hip_ext.h>
+
 #include <algorithm>
 #include <type_traits>
 
@@ -647,7 +649,11 @@ hipError_t launch_ffn_typed(moe_ctx* ctx, const void* x, int T, hipStream_t s) {
     constexpr int XT = decltype(xt)::value, CA = decltype(ca)::value, CB = decltype(cb)::value;
     a.lag = ffn_lag(blocks_first, ffn_resident_blocks<WT, XT, CA, CB>(lds), a.umax, gate_up_bytes);
     const int64_t nblocks = a.lag < 0 ? blocks_first : (int64_t)a.umax * (a.blocksAe + a.blocksB);
-    hipLaunchKernelGGL((ffn_kernel<WT, XT, CA, CB>), dim3((unsigned)nblocks), block, lds, s, a);
+    if (ctx->ffn_ev[0])
+      hipExtLaunchKernelGGL((ffn_kernel<WT, XT, CA, CB>), dim3((unsigned)nblocks), block, lds, s,
+                            ctx->ffn_ev[0], ctx->ffn_ev[1], 0, a);
+    else
+      hipLaunchKernelGGL((ffn_kernel<WT, XT, CA, CB>), dim3((unsigned)nblocks), block, lds, s, a);
   };
   auto by_b = [&](auto xt, auto ca) {
     switch (a.cplB) {

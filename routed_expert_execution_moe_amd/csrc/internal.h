@@ -208,6 +208,9 @@ struct moe_ctx {
   int64_t n_resizes = 0;
 
   moert::Timing* timing = nullptr;
+  // a timing context's FFN launch: the ring slot's two events, bound to the
+  // kernel's own dispatch (its start and end), set only around that launch
+  hipEvent_t ffn_ev[2] = {nullptr, nullptr};
 
   moe_status err = MOE_OK;     // latched HIP error
   std::string err_msg;
@@ -272,6 +275,10 @@ moe_status prefill_settle(moe_ctx* ctx, hipStream_t s);
 // timing mode: bracket a launch; no-ops when timing is off
 hipError_t timing_begin(moe_ctx* ctx, int phase, hipStream_t s);
 hipError_t timing_end(moe_ctx* ctx, hipStream_t s);
+// A ring slot's two events for a launch to bind (not recorded here; both
+// null without timing), and the slot's release once the launch is queued.
+hipError_t timing_pair(moe_ctx* ctx, int phase, hipEvent_t* ev0, hipEvent_t* ev1);
+void timing_commit(moe_ctx* ctx);
 
 // host branch -----------------------------------------------------------------
 CpuPool* cpu_pool_create(int threads);
